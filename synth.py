@@ -1,0 +1,159 @@
+"""Seeded synthetic inputs for the fine-grained MoE layer.
+
+This module only draws random numbers and stores them in the element types the
+layer reads (fp32, bf16, or e4m3 codes with fp32 block scales).  It holds none
+of the layer's arithmetic: no routing, no matmul, no activation function.  Both
+the float64 oracle (via the tests) and the GPU path (via the tests, the smoke
+check and the benchmark) consume the same tensors from here, so neither side
+ever produces the other's inputs.
+
+Shapes and value distributions follow the five workloads of the layer:
+
+  tiny      T=16,   H=256,  I=128, E=16  (4 groups of 4, keep 2), k=4, fp32
+  decode    T=4,    H=1536, I=512, E=128 (8 groups of 16, keep 4), k=8, bf16
+  prefill   T=8192, same layer as decode, router bias ~N(0, 0.5) (skewed load)
+  fp8       T=2048, same layer, experts e4m3 with one fp32 scale per 128x128
+  inkling   T=4096, H=2048, I=512, E=256 ungrouped, k=6, 2 shared experts
+
+The Ling-3.0-tiny layer shape (128 routed experts split into 8 groups of 16,
+of which 4 groups survive per token; hidden size 1536; SwiGLU experts) comes
+from the config paragraph of the TensorFold issue "Ling-3.0-tiny on a Qualcomm
+board"; the count of 8 routed experts per token comes from the routing table
+("模型與路由") of the HelloSun/ling30tiny model card; the 256-expert, top-6,
+two-shared-expert layer comes from the summary of llama.cpp PR "Add TML
+Inkling architecture".  The intermediate size 512 and the hidden size
+2048 of the Inkling-shaped layer are synthetic choices.
+
+Draw order (numpy PCG64, ``default_rng(seed)``), every tensor drawn in float32:
+  x; router weight; router bias (prefill only); then for each expert
+  e = 0..E+S-1: gate, up, down (for fp8 each tensor is followed by its
+  per-block scale factors u ~ U(0.5, 2)).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+import torch
+
+F32, BF16, E4M3 = "f32", "bf16", "e4m3"
+
+
+@dataclasses.dataclass(frozen=True)
+class LayerShape:
+    """One MoE layer workload: sizes, element types and input recipe."""
+    name: str
+    T: int                 # tokens
+    H: int                 # hidden size
+    I: int                 # expert intermediate size
+    E: int                 # routed experts
+    G: int                 # expert groups (1 = ungrouped)
+    Gk: int                # groups kept per token
+    k: int                 # experts per token
+    S: int                 # always-on shared experts
+    act: str               # element type of x, router weight and y: f32 | bf16
+    wt: str                # element type of the experts: f32 | bf16 | e4m3
+    x_dist: str            # "normal" or "rms" (RMS-normalised N(0,1))
+    bias_std: float        # std of the per-expert router bias, 0 = no bias
+    seed: int
+    router_std: float = 0.05
+    expert_std: float = 0.02
+
+    def with_tokens(self, T: int, seed: Optional[int] = None) -> "LayerShape":
+        return dataclasses.replace(self, T=T, seed=self.seed if seed is None else seed)
+
+
+WORKLOADS = {
+    "tiny": LayerShape("tiny", T=16, H=256, I=128, E=16, G=4, Gk=2, k=4, S=0,
+                       act=F32, wt=F32, x_dist="normal", bias_std=0.0, seed=0),
+    "decode": LayerShape("decode", T=4, H=1536, I=512, E=128, G=8, Gk=4, k=8, S=0,
+                         act=BF16, wt=BF16, x_dist="rms", bias_std=0.0, seed=1),
+    "prefill": LayerShape("prefill", T=8192, H=1536, I=512, E=128, G=8, Gk=4, k=8, S=0,
+                          act=BF16, wt=BF16, x_dist="rms", bias_std=0.5, seed=2),
+    "fp8": LayerShape("fp8", T=2048, H=1536, I=512, E=128, G=8, Gk=4, k=8, S=0,
+                      act=BF16, wt=E4M3, x_dist="rms", bias_std=0.0, seed=3),
+    "inkling": LayerShape("inkling", T=4096, H=2048, I=512, E=256, G=1, Gk=1, k=6, S=2,
+                          act=BF16, wt=BF16, x_dist="normal", bias_std=0.0, seed=4),
+}
+
+FP8_BLOCK = 128
+E4M3_MAX = 448.0
+
+
+def _store(a32: np.ndarray, dtype: str) -> torch.Tensor:
+    """float32 array -> tensor in the stored element type (bf16 by torch's RNE cast)."""
+    t = torch.from_numpy(np.ascontiguousarray(a32, dtype=np.float32))
+    if dtype == F32:
+        return t
+    if dtype == BF16:
+        return t.to(torch.bfloat16)
+    raise ValueError(dtype)
+
+
+def _encode_blocks(rng: np.random.Generator, w: np.ndarray):
+    """Store one [rows, cols] expert matrix as e4m3 codes + one fp32 scale per 128x128.
+
+    Per block: s = u * amax / 448 with u ~ U(0.5, 2), codes = e4m3(W / s) after
+    clamping to +-448 (torch's cast rounds to nearest even but does not
+    saturate).  The (code, scale) pair is the weight for every consumer.
+    """
+    rows, cols = w.shape
+    rb, cb = rows // FP8_BLOCK, cols // FP8_BLOCK
+    blocks = w.reshape(rb, FP8_BLOCK, cb, FP8_BLOCK)
+    amax = np.abs(blocks).max(axis=(1, 3)).astype(np.float32)
+    u = rng.uniform(0.5, 2.0, size=(rb, cb)).astype(np.float32)
+    s = (u * amax / np.float32(E4M3_MAX)).astype(np.float32)
+    s[s == 0] = 1.0
+    q = (blocks / s[:, None, :, None]).astype(np.float32)
+    q = np.clip(q, -E4M3_MAX, E4M3_MAX).reshape(rows, cols)
+    codes = torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, torch.from_numpy(s)
+
+
+def make_layer(shape: LayerShape) -> dict:
+    """Draw one layer's inputs.  Returns CPU tensors keyed by argument name.
+
+    Keys: x [T,H]; w_router [E,H]; bias [E] fp32 or None; w_gate, w_up [E,I,H];
+    w_down [E,H,I]; s_gate, s_up [E,I/128,H/128] and s_down [E,H/128,I/128]
+    (fp8 only, else None); sh_gate, sh_up, sh_down (+ sh_s_*) for the S shared
+    experts, or None when S == 0.
+    """
+    rng = np.random.default_rng(shape.seed)
+    T, H, I, E, S = shape.T, shape.H, shape.I, shape.E, shape.S
+    z = rng.standard_normal((T, H), dtype=np.float32)
+    if shape.x_dist == "rms":
+        z64 = z.astype(np.float64)
+        z64 = z64 / np.sqrt(np.mean(z64 * z64, axis=1, keepdims=True))
+        z = z64.astype(np.float32)
+    x = _store(z, shape.act)
+    w_router = _store(rng.standard_normal((E, H), dtype=np.float32) * np.float32(shape.router_std),
+                      shape.act)
+    bias = None
+    if shape.bias_std > 0:
+        bias = torch.from_numpy(rng.standard_normal(E, dtype=np.float32) * np.float32(shape.bias_std))
+
+    fp8 = shape.wt == E4M3
+    mats = {n: [] for n in ("gate", "up", "down")}
+    scales = {n: [] for n in ("gate", "up", "down")}
+    for _e in range(E + S):
+        for name, dims in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I))):
+            w = rng.standard_normal(dims, dtype=np.float32) * np.float32(shape.expert_std)
+            if fp8:
+                c, s = _encode_blocks(rng, w)
+                mats[name].append(c)
+                scales[name].append(s)
+            else:
+                mats[name].append(_store(w, shape.wt))
+
+    out = {"x": x, "w_router": w_router, "bias": bias}
+    for name in ("gate", "up", "down"):
+        out["w_" + name] = torch.stack(mats[name][:E])
+        out["sh_" + name] = torch.stack(mats[name][E:]) if S else None
+        if fp8:
+            out["s_" + name] = torch.stack(scales[name][:E])
+            out["sh_s_" + name] = torch.stack(scales[name][E:]) if S else None
+        else:
+            out["s_" + name] = None
+            out["sh_s_" + name] = None
+    return out
