@@ -1,0 +1,194 @@
+"""Benchmark of the MoE layer on one MI355X.
+
+A step is one moe_forward over one batch of synthetic tokens: router, group-limited
+top-k, permutation, grouped SwiGLU experts, weighted combine.  The default workload
+is the Ling-3.0-tiny-shaped decode layer (T=4, H=1536, I=512, E=128 in 8 groups of
+16 keeping 4, top-8, bf16).  Expert weights rotate over several copies placed at
+different addresses so that every step streams them from HBM rather than from the
+256 MiB Infinity Cache (a model runs a different layer's weights each time).
+
+Prints ONE JSON line (stdout) with the throughput, a roofline entry for the
+dominant kernel (timed with HIP events on the library's stream) and the float64
+oracle timed on the host cores as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s at 1 MI355X; decode HBM GB/s and prefill MFMA % of peak"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2516.6        # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5033.2         # MI355X dense fp8 MFMA
+WEIGHT_KEYS = ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down", "sh_gate", "sh_up",
+               "sh_down", "sh_s_gate", "sh_s_up", "sh_s_down")
+DEFAULT_SETS = {"tiny": 1, "decode": 8, "prefill": 2, "fp8": 4, "inkling": 1}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode",
+                    choices=["tiny", "decode", "prefill", "fp8", "inkling"])
+    ap.add_argument("--sets", type=int, default=0, help="weight copies rotated per step")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="host time budget for the oracle baseline (0 = skip)")
+    return ap.parse_args()
+
+
+def dominant(shape, stage_ms, U):
+    """Roofline of the gate/up projection (the largest stage on every workload)."""
+    T, H, I, E, k, S = shape.T, shape.H, shape.I, shape.E, shape.k, shape.S
+    Rk = T * k
+    ms = stage_ms["gateup"]
+    wbytes = 1 if shape.wt == "e4m3" else (4 if shape.wt == "f32" else 2)
+    if shape.name in ("prefill",):
+        flops = 2.0 * (Rk + T * S) * H * 2 * I
+        achieved = flops / (ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "gate/up grouped GEMM + SwiGLU",
+                "per_launch": f"{flops / 1e9:.2f} GFLOP = 2*R*H*2I, R={Rk + T * S}"}
+    # weight-stream bound: each touched expert's gate and up matrices once
+    per_expert = 2 * I * H * wbytes + (2 * (I // 128) * (H // 128) * 4 if shape.wt == "e4m3" else 0)
+    abytes = U * per_expert
+    achieved = abytes / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "gate/up expert projection + SwiGLU",
+            "per_launch": f"{abytes} B = {U} touched experts x {per_expert} B (gate+up weights)"}
+
+
+def cpu_baseline(shape, cpu, budget_s):
+    """The float64 oracle, as it stands, on a bounded sample of the same workload."""
+    from oracle import moe_oracle as mo
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    f = lambda t: None if t is None else (t.numpy() if t.dtype.itemsize == 1 else t.float().numpy())
+    ex = mo.Experts(*(f(cpu[n]) for n in WEIGHT_KEYS))
+    x, wr, b = f(cpu["x"]), f(cpu["w_router"]), f(cpu["router_bias"])
+    n_tok = min(shape.T, 64)
+    xs = x[:n_tok]
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        mo.forward(xs, wr, b, ex, shape.G, shape.Gk, shape.k)
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(reps * n_tok / el, 3), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{reps} x oracle forward of the first {n_tok} of {shape.T} tokens "
+                      f"(full routing + experts + combine, float64 numpy), {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer is built "
+              "and measured on a single MI355X", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import mixture_experts_layer_route_amd as moe
+    import synth
+    from oracle import moe_oracle as mo
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    moe.load_library()
+    shape = synth.WORKLOADS[args.workload]
+    nsets = args.sets or DEFAULT_SETS[args.workload]
+    log(f"workload {shape}; weight sets {nsets}")
+    cpu = synth.make_layer(shape)
+    dev = {k: (None if v is None else v.cuda()) for k, v in cpu.items()}
+    sets = [dev]
+    for _ in range(nsets - 1):
+        sets.append({k: (v.clone() if (k in WEIGHT_KEYS and v is not None) else v)
+                     for k, v in dev.items()})
+    wsts = [moe.weights_struct(s) for s in sets]
+    cfg = moe.make_config(shape.T, shape.H, shape.I, shape.E, shape.G, shape.Gk, shape.k,
+                          shape.S, shape.act, shape.wt)
+    ws = moe.alloc_workspace(cfg)
+    x = dev["x"]
+    y = torch.empty((shape.T, shape.H), dtype=x.dtype, device="cuda")
+    ids = torch.empty((shape.T, shape.k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((shape.T, shape.k), dtype=torch.float32, device="cuda")
+
+    # parity of what is timed: set 0, sampled tokens against the oracle on the GPU's routing
+    moe.forward(cfg, x, dev, ws, y=y, ids=ids, wts=wts, wst=wsts[0])
+    torch.cuda.synchronize()
+    g_ids = ids.cpu().numpy()
+    U = int(np.unique(g_ids).size) + shape.S
+    rng = np.random.default_rng(0)
+    sample = np.arange(shape.T) if shape.T <= 16 else np.unique(
+        np.concatenate([[0, shape.T - 1], rng.choice(shape.T, 14, replace=False)]))
+    f = lambda t: None if t is None else (t.numpy() if t.dtype.itemsize == 1 else t.float().numpy())
+    ex = mo.Experts(*(f(cpu[n]) for n in WEIGHT_KEYS))
+    l64 = mo.router_logits(f(cpu["x"]), f(cpu["w_router"]), f(cpu["router_bias"]))
+    w64 = mo.renormalise(mo.gate_scores(l64[sample]), g_ids[sample])
+    ref = mo.forward_tokenmajor(f(cpu["x"])[sample], ex, g_ids[sample], w64)
+    err = mo.rel_l2(y.float().cpu().numpy()[sample], ref)
+    log(f"parity on {len(sample)} tokens: rel_l2 {err:.3e}; unique experts {U}")
+
+    K, W = args.steps, args.warmup
+    for i in range(W):
+        moe.forward(cfg, x, None, ws, y=y, wst=wsts[i % nsets])
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.TIMED_STAGES)] for _ in range(K)]
+    for row in ev:
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    arrays = [(ctypes.c_void_p * moe.TIMED_STAGES)(*[e.cuda_event for e in row]) for row in ev]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(K):
+        moe.forward_timed(cfg, x, wsts[i % nsets], ws, y, arrays[i])
+    end.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / K
+    names = ("route", "gateup", "down", "combine")
+    stage_ms = {n: float(np.mean([ev[i][s].elapsed_time(ev[i][s + 1]) for i in range(K)]))
+                for s, n in enumerate(names)}
+    log("stage ms: " + ", ".join(f"{n} {v * 1e3:.1f} us" for n, v in stage_ms.items()))
+    tokens_per_s = shape.T / (ms_per_step * 1e-3)
+
+    roof = dominant(shape, stage_ms, U)
+    res = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": K, "warmup": W, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "e4m3": "e4m3+bf16"}[shape.wt],
+        "data": "synthetic",
+        "config": {"workload": shape.name, "T": shape.T, "H": shape.H, "I": shape.I,
+                   "E": shape.E, "G": shape.G, "Gk": shape.Gk, "k": shape.k, "S": shape.S,
+                   "weight_sets": nsets, "touched_experts": U},
+        "stage_us": {n: round(v * 1e3, 2) for n, v in stage_ms.items()},
+        "parity_rel_l2": float(f"{err:.3e}"),
+        "roofline": roof,
+    }
+    if args.cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(shape, cpu, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,197 @@
+/*
+ * moe.h - C ABI of the fine-grained MoE layer on MI355X (gfx950).
+ *
+ * The layer (route -> permute -> grouped SwiGLU experts -> weighted combine) is
+ * the one the pages describe for Ling-3.0-tiny and Inkling:
+ *   - TensorFold issue #1247 "Ling-3.0-tiny on a Qualcomm board", jschmied's
+ *     comment, config paragraph: 128 experts in 8 groups of 16 with 4 groups
+ *     kept, hidden 1536, SwiGLU experts whose limit lists are null (no clamp);
+ *     list "What it does not cover": the router is group-limited, and the bf16
+ *     experts run each expert on just the rows that picked it, which today
+ *     costs a host synchronisation per layer.
+ *   - HelloSun/ling30tiny model card, routing table (模型與路由): 8 experts per
+ *     token; numeric-check summary (數值檢查摘要): routing plus a weighted layer.
+ *   - llama.cpp PR "Add TML Inkling architecture", PR summary: 256 experts,
+ *     top-6, plus 2 shared experts; large MoEs need 64-bit index arithmetic.
+ *
+ * Conventions shared by every call
+ *   - Every pointer argument except `cfg`/`w` structs is a DEVICE pointer
+ *     (memory from hipMalloc or a torch CUDA tensor); the structs themselves
+ *     live in host memory and are read during the call only.
+ *   - Layouts are row-major.  Expert matrices are [out, in] per expert, experts
+ *     stacked: gate/up [E, I, H], down [E, H, I].  Shared experts have their
+ *     own arrays of the same form with S in place of E.
+ *   - Work is enqueued asynchronously on `stream`.  No call synchronises, copies
+ *     device memory to the host, or allocates: every call can be captured into
+ *     a HIP graph.  The caller owns every buffer and must keep it alive until
+ *     the stream has finished the work.  The library keeps no pointer after a
+ *     call returns and holds no device state, so calls on different streams
+ *     with distinct workspaces may run concurrently.
+ *   - The workspace `ws` is scratch memory of at least moe_workspace_size()
+ *     bytes for the same config, 256-byte aligned; its contents on entry are
+ *     ignored and on exit are unspecified.
+ *   - Errors: every call returns MOE_OK (0) or a negative MOE_ERR_* code.
+ *     Arguments are validated before anything is enqueued, so a failing call
+ *     enqueues nothing (except MOE_ERR_HIP, reported after a launch failed).
+ *     No C++ exception crosses this interface.  Preconditions that are NOT
+ *     checked (checking would need a device-to-host sync): caller-supplied
+ *     expert ids lie in [0, E) and are distinct per token; offsets/rows passed
+ *     to moe_expert_ffn / moe_combine are the ones moe_permute produced for
+ *     the same config; inputs are finite.
+ *   - Determinism: for a fixed config, inputs and device, outputs are bitwise
+ *     identical from run to run (no floating-point atomics anywhere).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define MOE_OK               0
+#define MOE_ERR_ARG         -1   /* null required pointer, non-positive size */
+#define MOE_ERR_UNSUPPORTED -2   /* shape/dtype combination outside the supported set */
+#define MOE_ERR_WORKSPACE   -3   /* workspace smaller than moe_workspace_size() */
+#define MOE_ERR_HIP         -4   /* a HIP launch failed; moe_strerror() has the HIP text */
+
+/* Element types. */
+typedef enum {
+  MOE_F32 = 0,        /* IEEE fp32 */
+  MOE_BF16 = 1,       /* bfloat16 */
+  MOE_E4M3_B128 = 2   /* expert weights only: OCP e4m3 codes (uint8) with one fp32
+                         scale per 128x128 block, value = decode(code) * scale */
+} moe_dtype;
+
+/*
+ * Layer configuration.  Supported element-type pairs (act_dtype, weight_dtype):
+ *   (MOE_F32, MOE_F32), (MOE_BF16, MOE_BF16), (MOE_BF16, MOE_E4M3_B128).
+ * Constraints: T >= 1; H, I >= 1 and multiples of 8 (of 128 for e4m3 experts);
+ * E >= 1; G >= 1 with E % G == 0; 1 <= Gk <= G; 1 <= k <= Gk * E / G;
+ * k <= 16; E + S <= 1024; T * (k + S) < 2^31.
+ */
+typedef struct {
+  int64_t num_tokens;     /* T: tokens in this call */
+  int32_t hidden;         /* H */
+  int32_t intermediate;   /* I: SwiGLU intermediate size of every expert */
+  int32_t num_experts;    /* E: routed experts */
+  int32_t num_groups;     /* G: expert groups (1 = ungrouped); group g = experts [g*E/G, (g+1)*E/G) */
+  int32_t topk_groups;    /* Gk: groups kept per token */
+  int32_t topk;           /* k: routed experts per token */
+  int32_t num_shared;     /* S: always-on shared experts, weight 1 */
+  int32_t act_dtype;      /* x, router weight, y: MOE_F32 | MOE_BF16 */
+  int32_t weight_dtype;   /* experts: MOE_F32 | MOE_BF16 | MOE_E4M3_B128 */
+} moe_config;
+
+/* Weights of one layer (device pointers).  Scales are used only for MOE_E4M3_B128. */
+typedef struct {
+  const void*  w_router;      /* [E, H] act_dtype */
+  const float* router_bias;   /* [E] fp32, added to the logits before the softmax; NULL = none */
+  const void*  w_gate;        /* [E, I, H] weight_dtype */
+  const void*  w_up;          /* [E, I, H] */
+  const void*  w_down;        /* [E, H, I] */
+  const float* s_gate;        /* [E, I/128, H/128] fp32 block scales (e4m3 only) */
+  const float* s_up;          /* [E, I/128, H/128] */
+  const float* s_down;        /* [E, H/128, I/128] */
+  const void*  sh_gate;       /* [S, I, H]; NULL when S == 0 */
+  const void*  sh_up;         /* [S, I, H] */
+  const void*  sh_down;       /* [S, H, I] */
+  const float* sh_s_gate;     /* [S, I/128, H/128] (e4m3 only) */
+  const float* sh_s_up;       /* [S, I/128, H/128] */
+  const float* sh_s_down;     /* [S, H/128, I/128] */
+} moe_weights;
+
+/*
+ * Bytes of workspace any call below needs for `cfg` (host only, no device work).
+ * Returns MOE_OK and writes *bytes, or a validation error.
+ */
+int moe_workspace_size(const moe_config* cfg, size_t* bytes);
+
+/*
+ * Router (group-limited routing of TensorFold #1247, "What it does not cover"):
+ *   l[t,e] = sum_h x[t,h] W_r[e,h] (+ bias[e]), fp32 accumulation;
+ *   s = softmax over all E logits;  group score = max s in the group;
+ *   keep the Gk best groups, then the k best experts inside them
+ *   (ties: lower group / expert index wins);  w = s[ids] / sum s[ids].
+ * x [T,H] act_dtype.  Outputs: topk_ids [T,k] int32 ordered by score
+ * descending (ties by lower id); topk_w [T,k] fp32; logits [T,E] fp32 with the
+ * bias included, or NULL to skip writing them.
+ */
+int moe_route(const moe_config* cfg, const void* x, const void* w_router, const float* router_bias,
+              int32_t* topk_ids, float* topk_w, float* logits,
+              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Permutation ("each expert on just the rows that picked it", TensorFold #1247,
+ * "What it does not cover"), computed on the device without a host sync.
+ * R = T*k + T*S rows.  Rows of routed expert e are the slots (t,j) with
+ * topk_ids[t,j] == e, in ascending (t, j) order; shared expert s owns rows
+ * [T*k + s*T, T*k + (s+1)*T), one per token in order.
+ * Outputs: expert_offsets [E+S+1] int32 (exclusive prefix sum of the row
+ * counts, expert_offsets[E+S] == R); row_token [R] int32 (token of each row);
+ * inv_rows [T,k] int32 (row of each routed slot).
+ */
+int moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t* expert_offsets,
+                int32_t* row_token, int32_t* inv_rows, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Grouped SwiGLU experts on the permuted rows (config paragraph of TensorFold
+ * #1247: SwiGLU, no clamp).  For each row r of expert e (shared experts are
+ * e = E..E+S-1):  h = silu(x[row_token[r]] Wg[e]^T) * (x[row_token[r]] Wu[e]^T),
+ * y_perm[r] = h Wd[e]^T, fp32 accumulation, UNWEIGHTED.  With e4m3 experts the
+ * activations (x and h) are first quantised per row per 128 along K to e4m3
+ * with an fp32 scale amax/448.  x [T,H] act_dtype; y_perm [R,H] fp32.
+ * Uses w->w_gate/up/down (+ scales, + shared arrays); the router fields are ignored.
+ */
+int moe_expert_ffn(const moe_config* cfg, const void* x, const int32_t* expert_offsets,
+                   const int32_t* row_token, const moe_weights* w, float* y_perm,
+                   void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Weighted combine (the weighted layer of the HelloSun/ling30tiny numeric-check
+ * summary; shared sum of the Inkling PR summary):
+ *   y[t] = sum_{j=0..k-1} topk_w[t,j] * y_perm[inv_rows[t,j]]
+ *        + sum_{s<S} y_perm[expert_offsets[E+s] + t],
+ * summed in that fixed order in fp32, then stored as act_dtype.  y [T,H].
+ */
+int moe_combine(const moe_config* cfg, const float* y_perm, const int32_t* expert_offsets,
+                const int32_t* inv_rows, const float* topk_w, void* y, hipStream_t stream);
+
+/*
+ * The whole layer: route, permute, experts, combine, all on the device, no host
+ * sync.  Same semantics as the four calls above in sequence, within rounding:
+ * it may fuse steps (routing weight applied in the down projection, expert
+ * outputs kept in bf16 for bf16 layers).  y [T,H] act_dtype.  topk_ids_out
+ * [T,k] int32 / topk_w_out [T,k] fp32 receive the routing if non-NULL.
+ */
+int moe_forward(const moe_config* cfg, const void* x, const moe_weights* w, void* y,
+                int32_t* topk_ids_out, float* topk_w_out,
+                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_forward with stage timing, for benchmarks and profilers: identical work
+ * and results, plus hipEventRecord(stage_events[i], stream) at the stage
+ * boundaries: [0] before the router; [1] after routing and permutation; [2]
+ * after the gate/up projection with SwiGLU (and the e4m3 quantisation of x);
+ * [3] after the down projection (and the e4m3 quantisation of h); [4] after
+ * the combine ([3] and [4] coincide when the down projection is fused with
+ * the combine).  `stage_events` holds MOE_TIMED_STAGES caller-created events.
+ */
+#define MOE_TIMED_STAGES 5
+int moe_forward_timed(const moe_config* cfg, const void* x, const moe_weights* w, void* y,
+                      int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                      hipStream_t stream, hipEvent_t* stage_events);
+
+/* Static description of a status code (for MOE_ERR_HIP: the last HIP error text
+   seen by this thread).  Never NULL. */
+const char* moe_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

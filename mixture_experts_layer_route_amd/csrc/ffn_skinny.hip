@@ -1,0 +1,334 @@
+// Skinny-M expert kernels: few rows per expert (decode), and every fp32 layer.
+//
+// The SwiGLU expert (config paragraph of TensorFold issue #1247 "Ling-3.0-tiny on
+// a Qualcomm board": SwiGLU experts, null limit lists, so no clamp):
+//   h = silu(x Wg^T) * (x Wu^T),  y = h Wd^T.
+// With a handful of rows per expert the work is a stream over each chosen
+// expert's weights, so these kernels are organised around the weight stream:
+// every wave owns a few weight rows, each lane reads 8 consecutive elements
+// (16 bytes of bf16) per step, all of a wave's weight loads are issued before
+// any is consumed, and the few activation rows come from L2.  fp32 accumulation;
+// one wave reduction per (output, row).
+#include "moe_internal.h"
+
+namespace moe {
+
+// Eight weights as they sit in memory (16 bytes of bf16 or 32 bytes of fp32).
+template <typename TW> struct Chunk8;
+template <> struct Chunk8<bf16_t> {
+  uint4 v;
+  __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void get(float (&o)[8]) const {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = __uint_as_float(w[i] << 16);
+      o[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+};
+template <> struct Chunk8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ void get(float (&o)[8]) const {
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+    o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+  }
+};
+
+__device__ __forceinline__ float dot8(const float (&a)[8], const float (&b)[8], float acc) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc = fmaf(a[i], b[i], acc);
+  return acc;
+}
+
+template <typename TW>
+__device__ __forceinline__ const TW* expert_base(const TW* routed, const TW* shared, int e, int E,
+                                                 int64_t stride) {
+  return e < E ? routed + int64_t(e) * stride : shared + int64_t(e - E) * stride;
+}
+
+constexpr int kSteps = 4;            // 4 steps x 64 lanes x 8 elements = 2048 per pass
+constexpr int kPass = kSteps * 512;
+
+// ---------------------------------------------------------------------------
+// Gate/up + SwiGLU.  grid = (max active experts, ceil(I / (4*NI))), block = 256.
+// Wave w of block (u, y) computes h[:, i0..i0+NI) for i0 = (4y + w) * NI over
+// the rows of the u-th active expert, RC rows per pass.  h is fp32 [R, I].
+template <typename TA, typename TW, int NI, int RC>
+__global__ __launch_bounds__(256) void k_gateup_skinny(
+    const TA* __restrict__ x, const int32_t* __restrict__ row_token,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ active,
+    const int32_t* __restrict__ meta, const TW* __restrict__ wg, const TW* __restrict__ wu,
+    const TW* __restrict__ shg, const TW* __restrict__ shu, float* __restrict__ hout, int H, int I,
+    int E) {
+  const int u = blockIdx.x;
+  if (u >= meta[0]) return;
+  const int lane = threadIdx.x & 63;
+  const int i0 = (blockIdx.y * 4 + (threadIdx.x >> 6)) * NI;
+  if (i0 >= I) return;
+  const int e = active[u];
+  const int r0 = offsets[e], r1 = offsets[e + 1];
+  const int64_t mstride = int64_t(I) * H;
+  const TW* gp = expert_base(wg, shg, e, E, mstride) + int64_t(i0) * H;
+  const TW* up = expert_base(wu, shu, e, E, mstride) + int64_t(i0) * H;
+
+  for (int rc = r0; rc < r1; rc += RC) {
+    const int nr = min(RC, r1 - rc);
+    const TA* xr[RC];
+#pragma unroll
+    for (int q = 0; q < RC; ++q) xr[q] = x + int64_t(row_token[rc + min(q, nr - 1)]) * H;
+    float ag[NI][RC], au[NI][RC];
+#pragma unroll
+    for (int ii = 0; ii < NI; ++ii)
+#pragma unroll
+      for (int q = 0; q < RC; ++q) ag[ii][q] = au[ii][q] = 0.f;
+
+    for (int hb = 0; hb < H; hb += kPass) {
+      Chunk8<TW> cg[kSteps][NI], cu[kSteps][NI];
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) {
+        const int h = hb + s * 512 + lane * 8;
+        if (h < H) {
+#pragma unroll
+          for (int ii = 0; ii < NI; ++ii) {
+            cg[s][ii].load(gp + int64_t(ii) * H + h);
+            cu[s][ii].load(up + int64_t(ii) * H + h);
+          }
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) {
+        const int h = hb + s * 512 + lane * 8;
+        if (h < H) {
+#pragma unroll
+          for (int q = 0; q < RC; ++q) {
+            if (q < nr) {
+              float xv[8];
+              load8(xr[q] + h, xv);
+#pragma unroll
+              for (int ii = 0; ii < NI; ++ii) {
+                float wv[8];
+                cg[s][ii].get(wv);
+                ag[ii][q] = dot8(wv, xv, ag[ii][q]);
+                cu[s][ii].get(wv);
+                au[ii][q] = dot8(wv, xv, au[ii][q]);
+              }
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < RC; ++q) {
+      if (q < nr) {
+#pragma unroll
+        for (int ii = 0; ii < NI; ++ii) {
+          const float g = wave_sum(ag[ii][q]);
+          const float v = wave_sum(au[ii][q]);
+          if (lane == ii) hout[int64_t(rc + q) * I + i0 + ii] = silu(g) * v;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Down projection, unweighted, per expert.  grid = (max active, ceil(H/(4*NR))).
+// y_perm[r, n] = sum_i h[r, i] Wd[e][n, i]  (fp32 out).
+template <typename TW, int NR, int RC>
+__global__ __launch_bounds__(256) void k_down_skinny(
+    const float* __restrict__ hin, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ active, const int32_t* __restrict__ meta,
+    const TW* __restrict__ wd, const TW* __restrict__ shd, float* __restrict__ y_perm, int H, int I,
+    int E) {
+  const int u = blockIdx.x;
+  if (u >= meta[0]) return;
+  const int lane = threadIdx.x & 63;
+  const int n0 = (blockIdx.y * 4 + (threadIdx.x >> 6)) * NR;
+  if (n0 >= H) return;
+  const int e = active[u];
+  const int r0 = offsets[e], r1 = offsets[e + 1];
+  const TW* dp = expert_base(wd, shd, e, E, int64_t(H) * I) + int64_t(n0) * I;
+
+  for (int rc = r0; rc < r1; rc += RC) {
+    const int nr = min(RC, r1 - rc);
+    float acc[NR][RC];
+#pragma unroll
+    for (int nn = 0; nn < NR; ++nn)
+#pragma unroll
+      for (int q = 0; q < RC; ++q) acc[nn][q] = 0.f;
+    for (int kb = 0; kb < I; kb += kPass) {
+      Chunk8<TW> cw[kSteps][NR];
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) {
+        const int kk = kb + s * 512 + lane * 8;
+        if (kk < I) {
+#pragma unroll
+          for (int nn = 0; nn < NR; ++nn) cw[s][nn].load(dp + int64_t(nn) * I + kk);
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) {
+        const int kk = kb + s * 512 + lane * 8;
+        if (kk < I) {
+#pragma unroll
+          for (int q = 0; q < RC; ++q) {
+            if (q < nr) {
+              float hv[8];
+              load8(hin + int64_t(rc + q) * I + kk, hv);
+#pragma unroll
+              for (int nn = 0; nn < NR; ++nn) {
+                float wv[8];
+                cw[s][nn].get(wv);
+                acc[nn][q] = dot8(wv, hv, acc[nn][q]);
+              }
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < RC; ++q) {
+      if (q < nr) {
+#pragma unroll
+        for (int nn = 0; nn < NR; ++nn) {
+          const float v = wave_sum(acc[nn][q]);
+          if (lane == nn) y_perm[int64_t(rc + q) * H + n0 + nn] = v;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Down projection fused with the weighted combine, for few tokens.
+// grid = ceil(H/(4*NR)), block = 256.  Wave w owns output columns n0..n0+NR.
+// y[t, n] = sum_j w[t,j] * (h[inv[t,j]] . Wd[ids[t,j]][n]) + sum_s (h[T*k+s*T+t] . Wd_s[n]).
+template <typename TW, typename TY, int NR>
+__global__ __launch_bounds__(256) void k_down_combine_skinny(
+    const float* __restrict__ hin, const int32_t* __restrict__ ids, const float* __restrict__ w,
+    const int32_t* __restrict__ inv, const TW* __restrict__ wd, const TW* __restrict__ shd,
+    TY* __restrict__ y, int T, int H, int I, int E, int k, int S) {
+  constexpr int JB = 8;
+  const int lane = threadIdx.x & 63;
+  const int n0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * NR;
+  if (n0 >= H) return;
+  const int64_t estride = int64_t(H) * I;
+  const int nslots = k + S;
+  for (int t = 0; t < T; ++t) {
+    float acc[NR];
+#pragma unroll
+    for (int nn = 0; nn < NR; ++nn) acc[nn] = 0.f;
+    for (int jb = 0; jb < nslots; jb += JB) {
+      for (int kb = 0; kb < I; kb += 512) {
+        const int kk = kb + lane * 8;
+        const bool kin = kk < I;
+        Chunk8<TW> cw[JB][NR];
+        const float* hp[JB];
+        float wt[JB];
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj) {
+          const int j = jb + jj;
+          int e, r;
+          float wj;
+          if (j < k) {
+            e = ids[t * k + j];
+            r = inv[t * k + j];
+            wj = w[t * k + j];
+          } else {
+            const int s = min(j - k, S - 1);
+            e = E + max(s, 0);
+            r = T * k + max(s, 0) * T + t;
+            wj = 1.f;
+          }
+          wt[jj] = (j < nslots) ? wj : 0.f;
+          hp[jj] = hin + int64_t(r) * I + kk;
+          if (j < nslots && kin) {
+            const TW* dp = expert_base(wd, shd, e, E, estride) + int64_t(n0) * I + kk;
+#pragma unroll
+            for (int nn = 0; nn < NR; ++nn) cw[jj][nn].load(dp + int64_t(nn) * I);
+          }
+        }
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj) {
+          if (jb + jj < nslots && kin) {
+            float hv[8];
+            load8(hp[jj], hv);
+#pragma unroll
+            for (int nn = 0; nn < NR; ++nn) {
+              float wv[8];
+              cw[jj][nn].get(wv);
+              acc[nn] = fmaf(wt[jj], dot8(wv, hv, 0.f), acc[nn]);
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int nn = 0; nn < NR; ++nn) {
+      const float v = wave_sum(acc[nn]);
+      if (lane == nn) y[int64_t(t) * H + n0 + nn] = from_f32<TY>(v);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <typename TA, typename TW>
+static void gateup(const Plan& p, const void* x, const int32_t* rt, const int32_t* off,
+                   const int32_t* act, const int32_t* meta, const moe_weights* w, float* h,
+                   hipStream_t st) {
+  constexpr int NI = 2, RC = 4;
+  dim3 grid(unsigned(p.max_active), unsigned((p.I + 4 * NI - 1) / (4 * NI)));
+  hipLaunchKernelGGL((k_gateup_skinny<TA, TW, NI, RC>), grid, dim3(256), 0, st, (const TA*)x, rt,
+                     off, act, meta, (const TW*)w->w_gate, (const TW*)w->w_up,
+                     (const TW*)w->sh_gate, (const TW*)w->sh_up, h, p.H, p.I, p.E);
+}
+
+int launch_gateup_skinny(const Plan& p, const void* x, const int32_t* row_token,
+                         const int32_t* offsets, const int32_t* active, const int32_t* meta,
+                         const moe_weights* w, float* h, hipStream_t st) {
+  if (p.wt == MOE_F32)
+    gateup<float, float>(p, x, row_token, offsets, active, meta, w, h, st);
+  else
+    gateup<bf16_t, bf16_t>(p, x, row_token, offsets, active, meta, w, h, st);
+  return check_launch();
+}
+
+int launch_down_skinny(const Plan& p, const float* h, const int32_t* offsets,
+                       const int32_t* active, const int32_t* meta, const moe_weights* w,
+                       float* y_perm, hipStream_t st) {
+  constexpr int NR = 2, RC = 4;
+  dim3 grid(unsigned(p.max_active), unsigned((p.H + 4 * NR - 1) / (4 * NR)));
+  if (p.wt == MOE_F32)
+    hipLaunchKernelGGL((k_down_skinny<float, NR, RC>), grid, dim3(256), 0, st, h, offsets, active,
+                       meta, (const float*)w->w_down, (const float*)w->sh_down, y_perm, p.H, p.I,
+                       p.E);
+  else
+    hipLaunchKernelGGL((k_down_skinny<bf16_t, NR, RC>), grid, dim3(256), 0, st, h, offsets, active,
+                       meta, (const bf16_t*)w->w_down, (const bf16_t*)w->sh_down, y_perm, p.H,
+                       p.I, p.E);
+  return check_launch();
+}
+
+int launch_down_combine_skinny(const Plan& p, const float* h, const int32_t* ids, const float* wts,
+                               const int32_t* inv, const moe_weights* w, void* y,
+                               hipStream_t st) {
+  constexpr int NR = 1;
+  dim3 grid(unsigned((p.H + 4 * NR - 1) / (4 * NR)));
+  const int T = int(p.T);
+  if (p.wt == MOE_F32)
+    hipLaunchKernelGGL((k_down_combine_skinny<float, float, NR>), grid, dim3(256), 0, st, h, ids,
+                       wts, inv, (const float*)w->w_down, (const float*)w->sh_down, (float*)y, T,
+                       p.H, p.I, p.E, p.k, p.S);
+  else
+    hipLaunchKernelGGL((k_down_combine_skinny<bf16_t, bf16_t, NR>), grid, dim3(256), 0, st, h,
+                       ids, wts, inv, (const bf16_t*)w->w_down, (const bf16_t*)w->sh_down,
+                       (bf16_t*)y, T, p.H, p.I, p.E, p.k, p.S);
+  return check_launch();
+}
+
+}  // namespace moe

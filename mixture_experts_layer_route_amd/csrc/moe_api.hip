@@ -1,0 +1,302 @@
+// C ABI of the MoE layer: validation, workspace carve and launch sequences.
+// Every call validates its arguments before enqueuing anything, never
+// synchronises, never copies device memory to the host and never allocates.
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+static thread_local char g_hip_error[256] = "no HIP error recorded";
+
+static int record_hip_error(hipError_t err) {
+  snprintf(g_hip_error, sizeof(g_hip_error), "HIP error %d: %s", int(err), hipGetErrorString(err));
+  return MOE_ERR_HIP;
+}
+
+int check_launch() {
+  const hipError_t err = hipGetLastError();
+  return err == hipSuccess ? MOE_OK : record_hip_error(err);
+}
+
+static size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+int make_plan(const moe_config* c, Plan* p) {
+  if (!c || !p) return MOE_ERR_ARG;
+  if (c->num_tokens < 1 || c->hidden < 1 || c->intermediate < 1 || c->num_experts < 1 ||
+      c->num_groups < 1 || c->topk_groups < 1 || c->topk < 1 || c->num_shared < 0)
+    return MOE_ERR_ARG;
+  const int64_t T = c->num_tokens;
+  const int H = c->hidden, I = c->intermediate, E = c->num_experts, G = c->num_groups;
+  const int Gk = c->topk_groups, k = c->topk, S = c->num_shared;
+  const int act = c->act_dtype, wt = c->weight_dtype;
+  const bool dense32 = act == MOE_F32 && wt == MOE_F32;
+  const bool dense16 = act == MOE_BF16 && wt == MOE_BF16;
+  const bool fp8 = act == MOE_BF16 && wt == MOE_E4M3_B128;
+  if (!(dense32 || dense16 || fp8)) return MOE_ERR_UNSUPPORTED;
+  if (H % 8 || I % 8) return MOE_ERR_UNSUPPORTED;
+  if (fp8 && (H % 128 || I % 128)) return MOE_ERR_UNSUPPORTED;
+  if (E % G || G > 64 || Gk > G) return MOE_ERR_UNSUPPORTED;
+  if (int64_t(k) > int64_t(Gk) * (E / G) || k > 16) return MOE_ERR_UNSUPPORTED;
+  if (E + S > 1024) return MOE_ERR_UNSUPPORTED;
+  if (T * int64_t(k + S) >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+
+  Plan q{};
+  q.T = T; q.H = H; q.I = I; q.E = E; q.G = G; q.Gk = Gk; q.k = k; q.S = S;
+  q.act = act; q.wt = wt;
+  q.Rk = T * k;
+  q.R = T * int64_t(k + S);
+  q.nblk = int((T + 255) / 256);
+  const bool mfma_shape = H % 128 == 0 && I % 64 == 0;
+  // Few rows per expert on average: the weight stream dominates, skinny kernels.
+  q.skinny = dense32 || (dense16 && (q.Rk <= 8 * int64_t(E) || !mfma_shape));
+  q.small_route = T <= 64 && T * k <= 256;
+  q.fused_down = q.skinny && T <= 16;
+  q.max_active = std::min<int64_t>(E, q.Rk) + S;
+  q.max_tiles = q.Rk / kTileRows + std::min<int64_t>(E, q.Rk) +
+                int64_t(S) * ((T + kTileRows - 1) / kTileRows);
+
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o = align256(o + bytes); return at; };
+  q.o_logits = take(size_t(T) * E * 4);
+  q.o_ids = take(size_t(q.Rk) * 4);
+  q.o_w = take(size_t(q.Rk) * 4);
+  q.o_blk = take(size_t(q.nblk) * E * 4);
+  q.o_off = take(size_t(E + S + 1) * 4);
+  q.o_meta = take(16);
+  q.o_active = take(size_t(E + S) * 4);
+  q.o_tiles = take(size_t(q.max_tiles) * 8);
+  q.o_rowtok = take(size_t(q.R) * 4);
+  q.o_inv = take(size_t(q.Rk) * 4);
+  q.o_roww = take(size_t(q.R) * 4);
+  q.o_h = take(size_t(q.R) * I * 4);
+  q.o_ypw = take(q.skinny ? 0 : size_t(q.R) * H * 2);
+  q.o_yp32 = take(q.skinny && !q.fused_down ? size_t(q.R) * H * 4 : 0);
+  q.o_xq = take(fp8 ? size_t(T) * H : 0);
+  q.o_sx = take(fp8 ? size_t(T) * (H / 128) * 4 : 0);
+  q.o_hq = take(fp8 ? size_t(q.R) * I : 0);
+  q.o_shq = take(fp8 ? size_t(q.R) * (I / 128) * 4 : 0);
+  q.total = o;
+  *p = q;
+  return MOE_OK;
+}
+
+template <typename T>
+static T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+static int check_ws(const Plan& p, const void* ws, size_t ws_bytes) {
+  if (!ws) return MOE_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return MOE_ERR_ARG;
+  if (ws_bytes < p.total) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+static int check_experts(const Plan& p, const moe_weights* w) {
+  if (!w || !w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_ARG;
+  if (p.S > 0 && (!w->sh_gate || !w->sh_up || !w->sh_down)) return MOE_ERR_ARG;
+  if (p.wt == MOE_E4M3_B128) {
+    if (!w->s_gate || !w->s_up || !w->s_down) return MOE_ERR_ARG;
+    if (p.S > 0 && (!w->sh_s_gate || !w->sh_s_up || !w->sh_s_down)) return MOE_ERR_ARG;
+  }
+  return MOE_OK;
+}
+
+#define MOE_TRY(expr)              \
+  do {                             \
+    const int rc_ = (expr);        \
+    if (rc_ != MOE_OK) return rc_; \
+  } while (0)
+
+// Expert FFN on permuted rows (schedule already in the workspace).
+static int run_experts(const Plan& p, const void* x, const int32_t* off, const int32_t* rowtok,
+                       const moe_weights* w, void* ws, float* y_perm32, bf16_t* y_perm16,
+                       const float* row_w, hipStream_t st) {
+  int32_t* active = at<int32_t>(ws, p.o_active);
+  int32_t* meta = at<int32_t>(ws, p.o_meta);
+  int2* tiles = at<int2>(ws, p.o_tiles);
+  if (p.skinny) {
+    float* h = at<float>(ws, p.o_h);
+    MOE_TRY(launch_gateup_skinny(p, x, rowtok, off, active, meta, w, h, st));
+    return launch_down_skinny(p, h, off, active, meta, w, y_perm32, st);
+  }
+  if (p.wt == MOE_BF16) {
+    bf16_t* h = at<bf16_t>(ws, p.o_h);
+    MOE_TRY(launch_gateup_mfma(p, x, rowtok, off, tiles, meta, w, h, nullptr, nullptr, st));
+    return launch_down_mfma(p, h, off, tiles, meta, w, row_w, y_perm32, y_perm16, nullptr, st);
+  }
+  uint8_t* xq = at<uint8_t>(ws, p.o_xq);
+  float* sx = at<float>(ws, p.o_sx);
+  uint8_t* hq = at<uint8_t>(ws, p.o_hq);
+  float* shq = at<float>(ws, p.o_shq);
+  float* h = at<float>(ws, p.o_h);
+  MOE_TRY(launch_quant(p, x, true, p.T, p.H, xq, sx, st));
+  MOE_TRY(launch_gateup_mfma(p, x, rowtok, off, tiles, meta, w, h, xq, sx, st));
+  MOE_TRY(launch_quant(p, h, false, p.R, p.I, hq, shq, st));
+  return launch_down_mfma(p, hq, off, tiles, meta, w, row_w, y_perm32, y_perm16, shq, st);
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int moe_workspace_size(const moe_config* cfg, size_t* bytes) {
+  if (!bytes) return MOE_ERR_ARG;
+  Plan p;
+  MOE_TRY(make_plan(cfg, &p));
+  *bytes = p.total;
+  return MOE_OK;
+}
+
+int moe_route(const moe_config* cfg, const void* x, const void* w_router, const float* router_bias,
+              int32_t* topk_ids, float* topk_w, float* logits, void* ws, size_t ws_bytes,
+              hipStream_t stream) {
+  Plan p;
+  MOE_TRY(make_plan(cfg, &p));
+  if (!x || !w_router || !topk_ids || !topk_w) return MOE_ERR_ARG;
+  MOE_TRY(check_ws(p, ws, ws_bytes));
+  float* lg = logits ? logits : at<float>(ws, p.o_logits);
+  MOE_TRY(launch_logits(p, x, w_router, router_bias, lg, stream));
+  return launch_select(p, lg, topk_ids, topk_w, stream);
+}
+
+int moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t* expert_offsets,
+                int32_t* row_token, int32_t* inv_rows, void* ws, size_t ws_bytes,
+                hipStream_t stream) {
+  Plan p;
+  MOE_TRY(make_plan(cfg, &p));
+  if (!topk_ids || !expert_offsets || !row_token || !inv_rows) return MOE_ERR_ARG;
+  MOE_TRY(check_ws(p, ws, ws_bytes));
+  return launch_permute(p, topk_ids, nullptr, at<int32_t>(ws, p.o_blk), expert_offsets,
+                        at<int32_t>(ws, p.o_active), at<int32_t>(ws, p.o_meta),
+                        at<int2>(ws, p.o_tiles), row_token, inv_rows, nullptr, kTileRows, stream);
+}
+
+int moe_expert_ffn(const moe_config* cfg, const void* x, const int32_t* expert_offsets,
+                   const int32_t* row_token, const moe_weights* w, float* y_perm, void* ws,
+                   size_t ws_bytes, hipStream_t stream) {
+  Plan p;
+  MOE_TRY(make_plan(cfg, &p));
+  if (!x || !expert_offsets || !row_token || !y_perm) return MOE_ERR_ARG;
+  MOE_TRY(check_experts(p, w));
+  MOE_TRY(check_ws(p, ws, ws_bytes));
+  MOE_TRY(launch_schedule(p, expert_offsets, at<int32_t>(ws, p.o_active),
+                          at<int32_t>(ws, p.o_meta), at<int2>(ws, p.o_tiles), kTileRows, stream));
+  return run_experts(p, x, expert_offsets, row_token, w, ws, y_perm, nullptr, nullptr, stream);
+}
+
+int moe_combine(const moe_config* cfg, const float* y_perm, const int32_t* expert_offsets,
+                const int32_t* inv_rows, const float* topk_w, void* y, hipStream_t stream) {
+  Plan p;
+  MOE_TRY(make_plan(cfg, &p));
+  if (!y_perm || !expert_offsets || !inv_rows || !topk_w || !y) return MOE_ERR_ARG;
+  return launch_combine(p, y_perm, expert_offsets, inv_rows, topk_w, y, stream);
+}
+
+static int forward_impl(const moe_config* cfg, const void* x, const moe_weights* w, void* y,
+                        int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                        hipStream_t stream, hipEvent_t* ev) {
+  Plan p;
+  MOE_TRY(make_plan(cfg, &p));
+  if (!x || !y || !w || !w->w_router) return MOE_ERR_ARG;
+  MOE_TRY(check_experts(p, w));
+  MOE_TRY(check_ws(p, ws, ws_bytes));
+  auto mark = [&](int i) -> int {
+    if (!ev) return MOE_OK;
+    const hipError_t err = hipEventRecord(ev[i], stream);
+    if (err != hipSuccess) return record_hip_error(err);
+    return MOE_OK;
+  };
+  int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, p.o_ids);
+  float* wts = topk_w_out ? topk_w_out : at<float>(ws, p.o_w);
+  float* logits = at<float>(ws, p.o_logits);
+  int32_t* off = at<int32_t>(ws, p.o_off);
+  int32_t* active = at<int32_t>(ws, p.o_active);
+  int32_t* meta = at<int32_t>(ws, p.o_meta);
+  int2* tiles = at<int2>(ws, p.o_tiles);
+  int32_t* rowtok = at<int32_t>(ws, p.o_rowtok);
+  int32_t* inv = at<int32_t>(ws, p.o_inv);
+  float* row_w = at<float>(ws, p.o_roww);
+
+  MOE_TRY(mark(0));
+  MOE_TRY(launch_logits(p, x, w->w_router, w->router_bias, logits, stream));
+  if (p.small_route) {
+    MOE_TRY(launch_route_permute_small(p, logits, ids, wts, off, active, meta, tiles, rowtok, inv,
+                                       row_w, kTileRows, stream));
+  } else {
+    MOE_TRY(launch_select(p, logits, ids, wts, stream));
+    MOE_TRY(launch_permute(p, ids, wts, at<int32_t>(ws, p.o_blk), off, active, meta, tiles, rowtok,
+                           inv, row_w, kTileRows, stream));
+  }
+  MOE_TRY(mark(1));
+  if (p.skinny) {
+    float* h = at<float>(ws, p.o_h);
+    MOE_TRY(launch_gateup_skinny(p, x, rowtok, off, active, meta, w, h, stream));
+    MOE_TRY(mark(2));
+    if (p.fused_down) {
+      MOE_TRY(launch_down_combine_skinny(p, h, ids, wts, inv, w, y, stream));
+      MOE_TRY(mark(3));
+      return mark(4);
+    }
+    float* yp = at<float>(ws, p.o_yp32);
+    MOE_TRY(launch_down_skinny(p, h, off, active, meta, w, yp, stream));
+    MOE_TRY(mark(3));
+    MOE_TRY(launch_combine(p, yp, off, inv, wts, y, stream));
+    return mark(4);
+  }
+  bf16_t* ypw = at<bf16_t>(ws, p.o_ypw);
+  if (p.wt == MOE_BF16) {
+    bf16_t* h = at<bf16_t>(ws, p.o_h);
+    MOE_TRY(launch_gateup_mfma(p, x, rowtok, off, tiles, meta, w, h, nullptr, nullptr, stream));
+    MOE_TRY(mark(2));
+    MOE_TRY(launch_down_mfma(p, h, off, tiles, meta, w, row_w, nullptr, ypw, nullptr, stream));
+  } else {
+    uint8_t* xq = at<uint8_t>(ws, p.o_xq);
+    float* sx = at<float>(ws, p.o_sx);
+    uint8_t* hq = at<uint8_t>(ws, p.o_hq);
+    float* shq = at<float>(ws, p.o_shq);
+    float* h = at<float>(ws, p.o_h);
+    MOE_TRY(launch_quant(p, x, true, p.T, p.H, xq, sx, stream));
+    MOE_TRY(launch_gateup_mfma(p, x, rowtok, off, tiles, meta, w, h, xq, sx, stream));
+    MOE_TRY(mark(2));
+    MOE_TRY(launch_quant(p, h, false, p.R, p.I, hq, shq, stream));
+    MOE_TRY(launch_down_mfma(p, hq, off, tiles, meta, w, row_w, nullptr, ypw, shq, stream));
+  }
+  MOE_TRY(mark(3));
+  MOE_TRY(launch_combine_preweighted(p, ypw, off, inv, y, stream));
+  return mark(4);
+}
+
+int moe_forward(const moe_config* cfg, const void* x, const moe_weights* w, void* y,
+                int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                hipStream_t stream) {
+  return forward_impl(cfg, x, w, y, topk_ids_out, topk_w_out, ws, ws_bytes, stream, nullptr);
+}
+
+int moe_forward_timed(const moe_config* cfg, const void* x, const moe_weights* w, void* y,
+                      int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                      hipStream_t stream, hipEvent_t* stage_events) {
+  if (!stage_events) return MOE_ERR_ARG;
+  for (int i = 0; i < MOE_TIMED_STAGES; ++i)
+    if (!stage_events[i]) return MOE_ERR_ARG;
+  return forward_impl(cfg, x, w, y, topk_ids_out, topk_w_out, ws, ws_bytes, stream, stage_events);
+}
+
+const char* moe_strerror(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_ARG: return "invalid argument (null pointer, non-positive size or misaligned workspace)";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration (shape or dtype combination)";
+    case MOE_ERR_WORKSPACE: return "workspace smaller than moe_workspace_size()";
+    case MOE_ERR_HIP: return g_hip_error;
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

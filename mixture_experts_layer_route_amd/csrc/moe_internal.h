@@ -1,0 +1,70 @@
+// Host-side plan and kernel launchers of the MoE library (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+#include "moe_device.h"
+
+namespace moe {
+
+constexpr int kTileRows = 128;   // M rows per tile of the matrix-core expert kernels
+
+// Everything a call needs to know about a config, computed on the host from
+// host-known sizes only (never from routing results).
+struct Plan {
+  int64_t T;
+  int H, I, E, G, Gk, k, S, act, wt;
+  int64_t Rk;           // routed rows T*k
+  int64_t R;            // all rows T*(k+S)
+  int nblk;             // permutation blocks of 256 tokens
+  bool skinny;          // skinny expert kernels (else matrix-core tiles)
+  bool small_route;     // selection + permutation in one block
+  bool fused_down;      // forward: down projection fused with the combine
+  int64_t max_active;   // upper bound on experts with rows
+  int64_t max_tiles;    // upper bound on M tiles
+  // workspace carve (byte offsets)
+  size_t o_logits, o_ids, o_w, o_blk, o_off, o_meta, o_active, o_tiles, o_rowtok, o_inv, o_roww,
+      o_h, o_ypw, o_yp32, o_xq, o_sx, o_hq, o_shq, total;
+};
+
+int make_plan(const moe_config* cfg, Plan* p);
+int check_launch();
+
+int launch_logits(const Plan& p, const void* x, const void* wr, const float* bias, float* logits,
+                  hipStream_t st);
+int launch_select(const Plan& p, const float* logits, int32_t* ids, float* w, hipStream_t st);
+int launch_permute(const Plan& p, const int32_t* ids, const float* w, int32_t* blk,
+                   int32_t* offsets, int32_t* active, int32_t* meta, int2* tiles,
+                   int32_t* row_token, int32_t* inv, float* row_w, int BM, hipStream_t st);
+int launch_schedule(const Plan& p, const int32_t* offsets, int32_t* active, int32_t* meta,
+                    int2* tiles, int BM, hipStream_t st);
+int launch_route_permute_small(const Plan& p, const float* logits, int32_t* ids, float* w,
+                               int32_t* offsets, int32_t* active, int32_t* meta, int2* tiles,
+                               int32_t* row_token, int32_t* inv, float* row_w, int BM,
+                               hipStream_t st);
+int launch_gateup_skinny(const Plan& p, const void* x, const int32_t* row_token,
+                         const int32_t* offsets, const int32_t* active, const int32_t* meta,
+                         const moe_weights* w, float* h, hipStream_t st);
+int launch_down_skinny(const Plan& p, const float* h, const int32_t* offsets,
+                       const int32_t* active, const int32_t* meta, const moe_weights* w,
+                       float* y_perm, hipStream_t st);
+int launch_down_combine_skinny(const Plan& p, const float* h, const int32_t* ids, const float* wts,
+                               const int32_t* inv, const moe_weights* w, void* y, hipStream_t st);
+int launch_gateup_mfma(const Plan& p, const void* x, const int32_t* row_token,
+                       const int32_t* offsets, const int2* tiles, const int32_t* meta,
+                       const moe_weights* w, void* h, const uint8_t* xq, const float* sx,
+                       hipStream_t st);
+int launch_down_mfma(const Plan& p, const void* h, const int32_t* offsets, const int2* tiles,
+                     const int32_t* meta, const moe_weights* w, const float* row_w, float* out32,
+                     bf16_t* out16, const float* sh_scale, hipStream_t st);
+int launch_quant(const Plan& p, const void* in, bool in_bf16, int64_t rows, int K, uint8_t* codes,
+                 float* scales, hipStream_t st);
+int launch_combine(const Plan& p, const float* y_perm, const int32_t* offsets, const int32_t* inv,
+                   const float* w, void* y, hipStream_t st);
+int launch_combine_preweighted(const Plan& p, const bf16_t* y_perm, const int32_t* offsets,
+                               const int32_t* inv, void* y, hipStream_t st);
+
+}  // namespace moe

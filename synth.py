@@ -114,7 +114,7 @@ def _encode_blocks(rng: np.random.Generator, w: np.ndarray):
 def make_layer(shape: LayerShape) -> dict:
     """Draw one layer's inputs.  Returns CPU tensors keyed by argument name.
 
-    Keys: x [T,H]; w_router [E,H]; bias [E] fp32 or None; w_gate, w_up [E,I,H];
+    Keys: x [T,H]; w_router [E,H]; router_bias [E] fp32 or None; w_gate, w_up [E,I,H];
     w_down [E,H,I]; s_gate, s_up [E,I/128,H/128] and s_down [E,H/128,I/128]
     (fp8 only, else None); sh_gate, sh_up, sh_down (+ sh_s_*) for the S shared
     experts, or None when S == 0.
@@ -146,7 +146,7 @@ def make_layer(shape: LayerShape) -> dict:
             else:
                 mats[name].append(_store(w, shape.wt))
 
-    out = {"x": x, "w_router": w_router, "bias": bias}
+    out = {"x": x, "w_router": w_router, "router_bias": bias}
     for name in ("gate", "up", "down"):
         out["w_" + name] = torch.stack(mats[name][:E])
         out["sh_" + name] = torch.stack(mats[name][E:]) if S else None

@@ -1,0 +1,212 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Routing: expert ids bit-exact wherever the float64 top-k margin exceeds 1e-4
+logits (near-tie tokens are counted and only checked for validity), weights
+within 2e-6.  Permutation: bit-exact.  Layer outputs: relative L2 within 5e-3
+(bf16, fp32) or 2e-2 (block FP8); fp32 layers also within 1e-5.  Near-tie
+tokens are compared against the oracle forced onto the GPU's routing.
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as mo
+import synth
+from tests.helpers import (TOL, TOL_F32_INTERNAL, check_routing, config_for, np_exact,
+                           oracle_experts, to_device)
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+
+
+def _shape(name, T=None, seed=None):
+    s = W[name]
+    return s if T is None else s.with_tokens(T, seed)
+
+
+@functools.lru_cache(maxsize=4)
+def _layer(name, T=None, seed=None):
+    shape = _shape(name, T, seed)
+    cpu = synth.make_layer(shape)
+    return shape, cpu, to_device(cpu)
+
+
+@pytest.fixture(scope="module")
+def moe():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mixture_experts_layer_route_amd as m
+    m.load_library()
+    return m
+
+
+def _print_case(*a):
+    print("case:", *a, flush=True)
+
+
+# ----------------------------------------------------------------------------- routing
+@pytest.mark.parametrize("name,T", [("tiny", None), ("decode", None), ("prefill", 300),
+                                    ("fp8", 130), ("inkling", 257), ("decode", 1)])
+def test_route(moe, name, T):
+    _print_case("route", name, T)
+    shape, cpu, dev = _layer(name, T)
+    cfg = config_for(shape)
+    ws = moe.alloc_workspace(cfg)
+    logits = torch.empty((shape.T, shape.E), dtype=torch.float32, device="cuda")
+    ids, w = moe.route(cfg, dev["x"], dev["w_router"], dev["router_bias"], ws, logits)
+    torch.cuda.synchronize()
+    l64 = mo.router_logits(np_exact(cpu["x"]), np_exact(cpu["w_router"]), np_exact(cpu["router_bias"]))
+    np.testing.assert_allclose(logits.cpu().numpy(), l64, rtol=0, atol=2e-5)
+    near, _ = check_routing(ids.cpu().numpy(), w.cpu().numpy(), l64, shape)
+    print(f"near-ties {int(near.sum())}/{shape.T}")
+
+
+def test_route_forced_ties(moe):
+    """Duplicated router rows give bit-identical fp32 logits: the lower index must win."""
+    _print_case("route ties")
+    shape = synth.LayerShape("ties", T=64, H=256, I=128, E=16, G=4, Gk=2, k=4, S=0, act="f32",
+                             wt="f32", x_dist="normal", bias_std=0.0, seed=11)
+    cpu = synth.make_layer(shape)
+    wr = cpu["w_router"].clone()
+    wr[5] = wr[3]       # same group (1): expert 3 beats 5
+    wr[9] = wr[1]       # group 2 vs group 0: equal group maxima when they lead
+    wr[14] = wr[2]
+    cpu["w_router"] = wr
+    dev = to_device(cpu)
+    cfg = config_for(shape)
+    ws = moe.alloc_workspace(cfg)
+    logits = torch.empty((shape.T, shape.E), dtype=torch.float32, device="cuda")
+    ids, w = moe.route(cfg, dev["x"], dev["w_router"], None, ws, logits)
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy().astype(np.float64)
+    assert np.all(lg[:, 3] == lg[:, 5]) and np.all(lg[:, 1] == lg[:, 9])
+    # the oracle run on the GPU's own fp32 logits must pick exactly the same ids
+    o_ids, _ = mo.select_experts(mo.gate_scores(lg), shape.G, shape.Gk, shape.k)
+    assert np.array_equal(ids.cpu().numpy(), o_ids)
+
+
+# ----------------------------------------------------------------------------- permutation
+@pytest.mark.parametrize("T,E,k,S", [(1, 16, 4, 0), (4, 128, 8, 0), (257, 128, 8, 0),
+                                     (1000, 128, 8, 0), (333, 256, 6, 2), (64, 16, 4, 1)])
+def test_permute_bit_exact(moe, T, E, k, S):
+    _print_case("permute", T, E, k, S)
+    rng = np.random.default_rng(T * 7 + E)
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    if T > 8:
+        ids[: T // 3] = np.sort(ids[: T // 3], axis=1)   # hot experts: many rows, multi-block
+        ids[: T // 3, 0] = 0
+    cfg = moe.make_config(T, 256, 128, E, 1, 1, k, S, "bf16", "bf16")
+    ws = moe.alloc_workspace(cfg)
+    off, rt, inv = moe.permute(cfg, torch.from_numpy(ids).cuda(), ws)
+    torch.cuda.synchronize()
+    o_off, o_rt, o_inv = mo.permute(ids, E, S)
+    assert np.array_equal(off.cpu().numpy(), o_off)
+    assert np.array_equal(rt.cpu().numpy(), o_rt)
+    assert np.array_equal(inv.cpu().numpy(), o_inv)
+
+
+# ----------------------------------------------------------------------------- experts
+@pytest.mark.parametrize("name,T", [("tiny", None), ("decode", None), ("prefill", 300),
+                                    ("fp8", 130), ("inkling", 100), ("inkling", 420)])
+def test_expert_ffn(moe, name, T):
+    """Unweighted expert outputs on the oracle's own permutation."""
+    _print_case("expert_ffn", name, T)
+    shape, cpu, dev = _layer(name, T)
+    ex = oracle_experts(cpu)
+    x64 = np_exact(cpu["x"])
+    ids, _, _ = mo.route(x64, np_exact(cpu["w_router"]), np_exact(cpu["router_bias"]), shape.G, shape.Gk,
+                         shape.k)
+    off, rt, _ = mo.permute(ids, shape.E, shape.S)
+    cfg = config_for(shape)
+    ws = moe.alloc_workspace(cfg)
+    yp = moe.expert_ffn(cfg, dev["x"], torch.from_numpy(off.astype(np.int32)).cuda(),
+                        torch.from_numpy(rt.astype(np.int32)).cuda(), dev, ws)
+    torch.cuda.synchronize()
+    ref = mo.expert_ffn(x64, off, rt, ex)
+    err = mo.rel_l2(yp.cpu().numpy(), ref)
+    print(f"rel_l2 {err:.3e}")
+    assert err <= TOL[shape.wt]
+    if shape.wt == "f32":
+        assert err <= TOL_F32_INTERNAL
+
+
+def test_combine_identity_round_trip(moe):
+    """Permute then combine with identity experts returns x (weights sum to 1)."""
+    _print_case("combine identity")
+    shape, cpu, dev = _layer("tiny")
+    cfg = config_for(shape)
+    ws = moe.alloc_workspace(cfg)
+    ids, w = moe.route(cfg, dev["x"], dev["w_router"], None, ws)
+    off, rt, inv = moe.permute(cfg, ids, ws)
+    y_perm = dev["x"][rt.long()].contiguous()
+    y = moe.combine(cfg, y_perm, off, inv, w, torch.float32)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(y.cpu().numpy(), cpu["x"].numpy(), rtol=0, atol=2e-6)
+
+
+# ----------------------------------------------------------------------------- whole layer
+def _forward_check(moe, shape, cpu, dev, sample=None):
+    cfg = config_for(shape)
+    ws = moe.alloc_workspace(cfg)
+    ids = torch.empty((shape.T, shape.k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((shape.T, shape.k), dtype=torch.float32, device="cuda")
+    y = moe.forward(cfg, dev["x"], dev, ws, ids=ids, wts=wts)
+    torch.cuda.synchronize()
+    x64 = np_exact(cpu["x"])
+    l64 = mo.router_logits(x64, np_exact(cpu["w_router"]), np_exact(cpu["router_bias"]))
+    g_ids = ids.cpu().numpy()
+    near, o_ids = check_routing(g_ids, wts.cpu().numpy(), l64, shape)
+    rows = np.arange(shape.T) if sample is None else sample
+    # oracle on the sampled tokens, forced onto the GPU's routing for near-tie tokens
+    use_ids = np.where(near[:, None], g_ids, o_ids)[rows]
+    w64 = mo.renormalise(mo.gate_scores(l64[rows]), use_ids)
+    ex = oracle_experts(cpu)
+    if sample is None:
+        off, rt, inv = mo.permute(use_ids, shape.E, shape.S)
+        ref = mo.combine(mo.expert_ffn(x64, off, rt, ex), off, inv, w64, shape.S)
+    else:
+        ref = mo.forward_tokenmajor(x64[rows], ex, use_ids, w64)
+    got = y.float().cpu().numpy()[rows]
+    err = mo.rel_l2(got, ref)
+    print(f"{shape.name} T={shape.T} rel_l2 {err:.3e} near-ties {int(near.sum())}")
+    assert err <= TOL[shape.wt]
+    if shape.wt == "f32":
+        assert err <= TOL_F32_INTERNAL
+    return y
+
+
+@pytest.mark.parametrize("name,T", [("tiny", None), ("decode", None), ("decode", 1),
+                                    ("decode", 16), ("decode", 40), ("prefill", 300),
+                                    ("prefill", 1500), ("fp8", 130), ("fp8", 16),
+                                    ("inkling", 100), ("inkling", 420)])
+def test_forward(moe, name, T):
+    _print_case("forward", name, T)
+    shape, cpu, dev = _layer(name, T)
+    _forward_check(moe, shape, cpu, dev)
+
+
+@pytest.mark.parametrize("name", ["prefill", "fp8", "inkling"])
+def test_forward_full_size_sampled(moe, name):
+    """Full-size workloads in the benchmark's launch configuration; outputs checked on a
+    sample of tokens the oracle computes one by one (first, last, and random)."""
+    _print_case("forward full", name)
+    shape, cpu, dev = _layer(name)
+    rng = np.random.default_rng(99)
+    sample = np.unique(np.concatenate([[0, shape.T - 1], rng.choice(shape.T, 30, replace=False)]))
+    _forward_check(moe, shape, cpu, dev, sample)
+
+
+@pytest.mark.parametrize("name,T", [("decode", None), ("prefill", 600), ("fp8", 200)])
+def test_forward_deterministic(moe, name, T):
+    _print_case("determinism", name, T)
+    shape, cpu, dev = _layer(name, T)
+    cfg = config_for(shape)
+    ws = moe.alloc_workspace(cfg)
+    y1 = moe.forward(cfg, dev["x"], dev, ws).clone()
+    ws.fill_(0x5A)
+    y2 = moe.forward(cfg, dev["x"], dev, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)

@@ -125,7 +125,7 @@ def test_token_major_equals_expert_major(name, T):
         shape = synth.LayerShape("fp8_s", T=T, H=256, I=128, E=8, G=2, Gk=1, k=2, S=1, act="bf16",
                                  wt="e4m3", x_dist="rms", bias_std=0.0, seed=6)
     lay, ex, f = _small_layer(shape)
-    out = mo.forward(f(lay["x"]), f(lay["w_router"]), f(lay["bias"]), ex, shape.G, shape.Gk, shape.k)
+    out = mo.forward(f(lay["x"]), f(lay["w_router"]), f(lay["router_bias"]), ex, shape.G, shape.Gk, shape.k)
     y2 = mo.forward_tokenmajor(f(lay["x"]), ex, out["ids"], out["w"])
     assert mo.rel_l2(out["y"], y2) < 1e-12
 
