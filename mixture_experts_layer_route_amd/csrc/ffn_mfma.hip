@@ -182,6 +182,179 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmBf16Args p) {
 }
 
 // ===========================================================================
+// bf16, pipelined: 128 x 256 tiles, 4 waves (2 x 2) of 64 x 128, K slabs of 64
+// moved global -> LDS by direct-to-LDS loads (global_load_lds_dwordx4) in a
+// 3-stage ring, so two slabs are in flight while one is multiplied.  Each wave
+// load instruction fills 8 tile rows (1 KB); lane L lands in row L/8, 16-byte
+// slot L%8 and fetches the logical chunk (L%8) ^ (L/8), which is the XOR swizzle
+// the fragment reads undo.  Waits are explicit (vmcnt for the slab about to be
+// read, lgkmcnt(0) so no fragment read is in flight when a slot is refilled)
+// followed by a bare s_barrier.
+typedef __attribute__((address_space(1))) void gvoid_t;
+typedef __attribute__((address_space(3))) void lvoid_t;
+
+// The load is written in asm so that the compiler does not add its own
+// conservative vmcnt(0) before every later LDS read; completion is tracked by
+// the explicit waits below (VMEM loads complete in issue order).  The address
+// and M0 are consumed when the load issues; M0 is saved and restored around it
+// and the only register output is that saved scalar copy.
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>((lvoid_t*)lds)));
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0), "v"(g)
+      : "memory");
+}
+// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4]<<14)
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | ((N >> 4) << 14));
+}
+
+namespace v2 {
+constexpr int BM = 128, BN = 256, W = 4, MI = 2, NI = 4;
+constexpr int AJ = BM / (8 * W), BJ = BN / (8 * W), L = AJ + BJ;   // loads per lane per slab
+constexpr int A_U4 = BM * 8, B_U4 = BN * 8;                         // uint4 per slab
+}  // namespace v2
+
+template <bool GATEUP>
+__global__ __launch_bounds__(256) void k_gemm_bf16_v2(GemmBf16Args p) {
+  using namespace v2;
+  __shared__ uint4 sA0[A_U4], sA1[A_U4], sA2[A_U4];
+  __shared__ uint4 sB0[B_U4], sB1[B_U4], sB2[B_U4];
+  const int ncol = GATEUP ? p.N / (BN / 2) : p.N / BN;
+  const int tile = blockIdx.x / ncol;
+  const int ct = blockIdx.x - tile * ncol;
+  if (tile >= p.meta[1]) return;
+  const int2 te = p.tiles[tile];
+  const int e = te.x, m0 = te.y;
+  const int base = p.offsets[e];
+  const int cnt = p.offsets[e + 1] - base;
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wm = wv >> 1, wn = wv & 1;
+  const int64_t K = p.K;
+  const int kcl = ((lane & 7) ^ (lane >> 3)) * 8;   // logical chunk this lane fetches (elements)
+
+  const bf16_t* ag[AJ];
+#pragma unroll
+  for (int i = 0; i < AJ; ++i) {
+    const int r = 8 * (wv + W * i) + (lane >> 3);
+    const int m = min(m0 + r, cnt - 1);
+    ag[i] = (GATEUP ? p.a + int64_t(p.row_token[base + m]) * K : p.a + int64_t(base + m) * K) + kcl;
+  }
+  const bf16_t* bg[BJ];
+  {
+    const int64_t st = int64_t(p.N) * K;
+#pragma unroll
+    for (int i = 0; i < BJ; ++i) {
+      const int r = 8 * (wv + W * i) + (lane >> 3);
+      if (GATEUP) {
+        const int c0 = ct * (BN / 2);
+        bg[i] = (r < BN / 2 ? expert_mat(p.w0, p.sh0, e, p.E, st) + int64_t(c0 + r) * K
+                            : expert_mat(p.w1, p.sh1, e, p.E, st) + int64_t(c0 + r - BN / 2) * K) + kcl;
+      } else {
+        bg[i] = expert_mat(p.w0, p.sh0, e, p.E, st) + int64_t(ct * BN + r) * K + kcl;
+      }
+    }
+  }
+
+  auto issue = [&](int kt, uint4* sa, uint4* sb) {
+    const int64_t ko = int64_t(kt) * 64;
+#pragma unroll
+    for (int i = 0; i < AJ; ++i) dma16(ag[i] + ko, sa + (wv + W * i) * 64);
+#pragma unroll
+    for (int i = 0; i < BJ; ++i) dma16(bg[i] + ko, sb + (wv + W * i) * 64);
+  };
+
+  f32x16 acc[MI][NI];
+#pragma unroll
+  for (int a = 0; a < MI; ++a)
+#pragma unroll
+    for (int b = 0; b < NI; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+  // fragments of k-step ks+1 are read while the MFMAs of k-step ks run
+  auto load_frags = [&](const uint4* sa, const uint4* sb, int ks, bf16x8 (&af)[MI], bf16x8 (&bfr)[NI]) {
+    const int chunk = ks * 2 + (lane >> 5);
+#pragma unroll
+    for (int a = 0; a < MI; ++a)
+      af[a] = __builtin_bit_cast(bf16x8, sa[swz16(wm * 64 + a * 32 + (lane & 31), chunk)]);
+#pragma unroll
+    for (int b = 0; b < NI; ++b) {
+      // gate/up: blocks 0..NI/2-1 are gate columns, NI/2.. the matching up columns
+      const int row = GATEUP ? ((b < NI / 2 ? 0 : BN / 2) + wn * 64 + (b % (NI / 2)) * 32 + (lane & 31))
+                             : (wn * 128 + b * 32 + (lane & 31));
+      bfr[b] = __builtin_bit_cast(bf16x8, sb[swz16(row, chunk)]);
+    }
+  };
+  auto compute = [&](const uint4* sa, const uint4* sb) {
+    bf16x8 af[2][MI], bfr[2][NI];
+    load_frags(sa, sb, 0, af[0], bfr[0]);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks + 1 < 4) load_frags(sa, sb, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
+#pragma unroll
+      for (int a = 0; a < MI; ++a)
+#pragma unroll
+        for (int b = 0; b < NI; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][a], bfr[ks & 1][b], acc[a][b], 0, 0, 0);
+    }
+  };
+
+  const int nk = int(K / 64);
+  issue(0, sA0, sB0);
+  if (nk > 1) issue(1, sA1, sB1);
+  // one step: wait for slab kt, barrier, refill the slot freed by slab kt-1 with kt+2, multiply kt
+#define MOE_V2_STEP(KT, SA, SB, NA, NB)                    \
+  {                                                        \
+    if ((KT) + 1 < nk) wait_vm_lgkm0<L>(); else wait_vm_lgkm0<0>(); \
+    __builtin_amdgcn_s_barrier();                          \
+    if ((KT) + 2 < nk) issue((KT) + 2, NA, NB);            \
+    compute(SA, SB);                                       \
+  }
+  for (int kt = 0; kt < nk; kt += 3) {
+    MOE_V2_STEP(kt, sA0, sB0, sA2, sB2)
+    if (kt + 1 < nk) MOE_V2_STEP(kt + 1, sA1, sB1, sA0, sB0)
+    if (kt + 2 < nk) MOE_V2_STEP(kt + 2, sA2, sB2, sA1, sB1)
+  }
+#undef MOE_V2_STEP
+
+  // epilogue (registers only)
+#pragma unroll
+  for (int a = 0; a < MI; ++a) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = wm * 64 + a * 32 + acc_row(r, lane);
+      if (m0 + row >= cnt) continue;
+      const int64_t grow = int64_t(base + m0 + row);
+      if (GATEUP) {
+#pragma unroll
+        for (int b = 0; b < NI / 2; ++b) {
+          const int col = ct * (BN / 2) + wn * 64 + b * 32 + (lane & 31);
+          const float g = acc[a][b][r], u = acc[a][b + NI / 2][r];
+          p.out16[grow * p.N + col] = f32_to_bf16(silu(g) * u);
+        }
+      } else {
+        const float wr = p.out32 ? 1.f : p.row_w[grow];
+#pragma unroll
+        for (int b = 0; b < NI; ++b) {
+          const int col = ct * BN + wn * 128 + b * 32 + (lane & 31);
+          if (p.out32)
+            p.out32[grow * p.N + col] = acc[a][b][r];
+          else
+            p.out16[grow * p.N + col] = f32_to_bf16(acc[a][b][r] * wr);
+        }
+      }
+    }
+  }
+}
+
+// ===========================================================================
 // Block FP8.  Weights e4m3 with one fp32 scale per 128x128 block; activations
 // e4m3 with one fp32 scale per row per 128 along K.  One K slab = 128 = one
 // scale block.  Here the weight rows are the MFMA's M operand and activation
@@ -433,7 +606,11 @@ int launch_gateup_mfma(const Plan& p, const void* x, const int32_t* row_token,
     a.meta = meta; a.w0 = (const bf16_t*)w->w_gate; a.w1 = (const bf16_t*)w->w_up;
     a.sh0 = (const bf16_t*)w->sh_gate; a.sh1 = (const bf16_t*)w->sh_up;
     a.out16 = (bf16_t*)h; a.K = p.H; a.N = p.I; a.E = p.E;
-    hipLaunchKernelGGL(k_gemm_bf16<true>, dim3(grid), dim3(256), 0, st, a);
+    if (p.I % (v2::BN / 2) == 0 && p.H % 64 == 0)
+      hipLaunchKernelGGL(k_gemm_bf16_v2<true>, dim3(unsigned(p.max_tiles * (p.I / (v2::BN / 2)))),
+                         dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(k_gemm_bf16<true>, dim3(grid), dim3(256), 0, st, a);
   } else {
     GemmFp8Args a{};
     a.a = xq; a.a_scale = sx; a.row_token = row_token; a.offsets = offsets; a.tiles = tiles;
@@ -455,7 +632,11 @@ int launch_down_mfma(const Plan& p, const void* h, const int32_t* offsets, const
     a.a = (const bf16_t*)h; a.offsets = offsets; a.tiles = tiles; a.meta = meta;
     a.w0 = (const bf16_t*)w->w_down; a.sh0 = (const bf16_t*)w->sh_down;
     a.row_w = row_w; a.out16 = out16; a.out32 = out32; a.K = p.I; a.N = p.H; a.E = p.E;
-    hipLaunchKernelGGL(k_gemm_bf16<false>, dim3(grid), dim3(256), 0, st, a);
+    if (p.H % v2::BN == 0 && p.I % 64 == 0)
+      hipLaunchKernelGGL(k_gemm_bf16_v2<false>, dim3(unsigned(p.max_tiles * (p.H / v2::BN))),
+                         dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(k_gemm_bf16<false>, dim3(grid), dim3(256), 0, st, a);
   } else {
     GemmFp8Args a{};
     a.a = (const uint8_t*)h; a.a_scale = sh_scale; a.offsets = offsets; a.tiles = tiles;

@@ -49,7 +49,7 @@ int make_plan(const moe_config* c, Plan* p) {
   q.act = act; q.wt = wt;
   q.Rk = T * k;
   q.R = T * int64_t(k + S);
-  q.nblk = int((T + 255) / 256);
+  q.nblk = int((T + 63) / 64);
   const bool mfma_shape = H % 128 == 0 && I % 64 == 0;
   // Few rows per expert on average: the weight stream dominates, skinny kernels.
   q.skinny = dense32 || (dense16 && (q.Rk <= 8 * int64_t(E) || !mfma_shape));
@@ -161,9 +161,12 @@ int moe_route(const moe_config* cfg, const void* x, const void* w_router, const 
   MOE_TRY(make_plan(cfg, &p));
   if (!x || !w_router || !topk_ids || !topk_w) return MOE_ERR_ARG;
   MOE_TRY(check_ws(p, ws, ws_bytes));
+  if (router_mfma_ok(p))
+    return launch_router_mfma(p, x, w_router, router_bias, logits, topk_ids, topk_w,
+                              at<int32_t>(ws, p.o_blk), stream);
   float* lg = logits ? logits : at<float>(ws, p.o_logits);
   MOE_TRY(launch_logits(p, x, w_router, router_bias, lg, stream));
-  return launch_select(p, lg, topk_ids, topk_w, stream);
+  return launch_select(p, lg, topk_ids, topk_w, nullptr, stream);
 }
 
 int moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t* expert_offsets,
@@ -225,14 +228,21 @@ static int forward_impl(const moe_config* cfg, const void* x, const moe_weights*
   float* row_w = at<float>(ws, p.o_roww);
 
   MOE_TRY(mark(0));
-  MOE_TRY(launch_logits(p, x, w->w_router, w->router_bias, logits, stream));
+  int32_t* blk = at<int32_t>(ws, p.o_blk);
   if (p.small_route) {
+    MOE_TRY(launch_logits(p, x, w->w_router, w->router_bias, logits, stream));
     MOE_TRY(launch_route_permute_small(p, logits, ids, wts, off, active, meta, tiles, rowtok, inv,
                                        row_w, kTileRows, stream));
   } else {
-    MOE_TRY(launch_select(p, logits, ids, wts, stream));
-    MOE_TRY(launch_permute(p, ids, wts, at<int32_t>(ws, p.o_blk), off, active, meta, tiles, rowtok,
-                           inv, row_w, kTileRows, stream));
+    if (router_mfma_ok(p)) {
+      MOE_TRY(launch_router_mfma(p, x, w->w_router, w->router_bias, nullptr, ids, wts, blk,
+                                 stream));
+    } else {
+      MOE_TRY(launch_logits(p, x, w->w_router, w->router_bias, logits, stream));
+      MOE_TRY(launch_select(p, logits, ids, wts, blk, stream));
+    }
+    MOE_TRY(launch_scan_scatter(p, ids, wts, blk, off, active, meta, tiles, rowtok, inv, row_w,
+                                kTileRows, stream));
   }
   MOE_TRY(mark(1));
   if (p.skinny) {

@@ -72,15 +72,54 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
 }
 
 // ----------------------------------------------------------------- wave reductions
+// DPP steps inside each row of 16 lanes (quad swaps, half-row and row mirrors),
+// then the four row results combined through readlane in a fixed order, so the
+// result is the same in every lane and bitwise reproducible.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(int(v), int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) { return __uint_as_float(dpp32<CTRL>(__float_as_uint(v))); }
+__device__ __forceinline__ float lanef(float v, int l) {
+  return __uint_as_float(uint32_t(__builtin_amdgcn_readlane(int(__float_as_uint(v)), l)));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += dppf<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dppf<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dppf<0x141>(v);   // row_half_mirror
+  v += dppf<0x140>(v);   // row_mirror
+  return (lanef(v, 0) + lanef(v, 16)) + (lanef(v, 32) + lanef(v, 48));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  v = fmaxf(v, dppf<0xB1>(v));
+  v = fmaxf(v, dppf<0x4E>(v));
+  v = fmaxf(v, dppf<0x141>(v));
+  v = fmaxf(v, dppf<0x140>(v));
+  return fmaxf(fmaxf(lanef(v, 0), lanef(v, 16)), fmaxf(lanef(v, 32), lanef(v, 48)));
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
+  const uint32_t lo = dpp32<CTRL>(uint32_t(v)), hi = dpp32<CTRL>(uint32_t(v >> 32));
+  const uint64_t w = (uint64_t(hi) << 32) | lo;
+  return w > v ? w : v;
+}
+__device__ __forceinline__ uint64_t lane_u64(uint64_t v, int l) {
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v)), l));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v >> 32)), l));
+  return (uint64_t(hi) << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = dpp_max_u64<0xB1>(v);
+  v = dpp_max_u64<0x4E>(v);
+  v = dpp_max_u64<0x141>(v);
+  v = dpp_max_u64<0x140>(v);
+  uint64_t a = lane_u64(v, 0), b = lane_u64(v, 16), c = lane_u64(v, 32), d = lane_u64(v, 48);
+  a = a > b ? a : b;
+  c = c > d ? c : d;
+  return a > c ? a : c;
 }
 
 // Total order key for (score desc, index asc) arg-max: larger key wins.
@@ -92,14 +131,6 @@ __device__ __forceinline__ uint64_t rank_key(float s, int idx) {
 }
 __device__ __forceinline__ int key_index(uint64_t k) { return int(0xFFFFFFFFu - uint32_t(k)); }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint64_t w = __shfl_xor(v, o, kWave);
-    v = w > v ? w : v;
-  }
-  return v;
-}
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 

@@ -19,7 +19,7 @@ struct Plan {
   int H, I, E, G, Gk, k, S, act, wt;
   int64_t Rk;           // routed rows T*k
   int64_t R;            // all rows T*(k+S)
-  int nblk;             // permutation blocks of 256 tokens
+  int nblk;             // permutation blocks of 64 tokens
   bool skinny;          // skinny expert kernels (else matrix-core tiles)
   bool small_route;     // selection + permutation in one block
   bool fused_down;      // forward: down projection fused with the combine
@@ -35,7 +35,14 @@ int check_launch();
 
 int launch_logits(const Plan& p, const void* x, const void* wr, const float* bias, float* logits,
                   hipStream_t st);
-int launch_select(const Plan& p, const float* logits, int32_t* ids, float* w, hipStream_t st);
+int launch_select(const Plan& p, const float* logits, int32_t* ids, float* w, int32_t* blk,
+                  hipStream_t st);
+bool router_mfma_ok(const Plan& p);
+int launch_router_mfma(const Plan& p, const void* x, const void* wr, const float* bias,
+                       float* logits_out, int32_t* ids, float* w, int32_t* blk, hipStream_t st);
+int launch_scan_scatter(const Plan& p, const int32_t* ids, const float* w, int32_t* blk,
+                        int32_t* offsets, int32_t* active, int32_t* meta, int2* tiles,
+                        int32_t* row_token, int32_t* inv, float* row_w, int BM, hipStream_t st);
 int launch_permute(const Plan& p, const int32_t* ids, const float* w, int32_t* blk,
                    int32_t* offsets, int32_t* active, int32_t* meta, int2* tiles,
                    int32_t* row_token, int32_t* inv, float* row_w, int BM, hipStream_t st);

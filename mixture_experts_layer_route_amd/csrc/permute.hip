@@ -65,52 +65,74 @@ __device__ void build_schedule(int cnt, int EE, int BM, int32_t* offsets, int32_
 }
 
 // ---------------------------------------------------------------------------
-// Histogram per block of 256 tokens.  grid = nblk, block = 256.
+// Histogram per permutation block of 64 tokens (one wave each, four per block).
+// grid = ceil(T/256), block = 256, dynamic LDS = 4*E ints.
 __global__ __launch_bounds__(256) void k_perm_count(const int32_t* __restrict__ ids, int64_t T,
                                                     int k, int E, int32_t* __restrict__ blk) {
   extern __shared__ int cnt_lds[];
-  for (int e = threadIdx.x; e < E; e += 256) cnt_lds[e] = 0;
+  const int wv = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < 4 * E; i += 256) cnt_lds[i] = 0;
   __syncthreads();
   const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (t < T)
-    for (int j = 0; j < k; ++j) atomicAdd(&cnt_lds[ids[t * k + j]], 1);
+    for (int j = 0; j < k; ++j) atomicAdd(&cnt_lds[wv * E + ids[t * k + j]], 1);
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256) blk[int64_t(blockIdx.x) * E + e] = cnt_lds[e];
+  for (int i = threadIdx.x; i < 4 * E; i += 256) {
+    const int64_t b = int64_t(blockIdx.x) * 4 + i / E;
+    if (b * 64 < T) blk[b * E + (i % E)] = cnt_lds[i];
+  }
 }
 
 // Totals, offsets, per-block bases (in place over the histogram) and schedule.
-// One block of 1024 threads.
+// One block of 1024 threads.  The [nblk][E] histogram is walked in chunks of
+// CB blocks staged through LDS with coalesced loads; thread e owns expert e.
 __global__ __launch_bounds__(1024) void k_perm_scan(int32_t* __restrict__ blk, int nblk, int64_t T,
                                                     int E, int S, int BM,
                                                     int32_t* __restrict__ offsets,
                                                     int32_t* __restrict__ active,
                                                     int32_t* __restrict__ meta,
                                                     int2* __restrict__ tiles) {
+  constexpr int CHUNK = 16384;                     // ints staged per pass (64 KB)
   __shared__ int tmp[32];
   __shared__ int offs[1025];
+  __shared__ int stage[CHUNK];
   const int e = threadIdx.x;
+  const int CB = max(1, CHUNK / E);                // blocks per pass
   int cnt = 0;
-  if (e < E)
-    for (int b = 0; b < nblk; ++b) cnt += blk[int64_t(b) * E + e];
-  else if (e < E + S)
-    cnt = int(T);
+  for (int b0 = 0; b0 < nblk; b0 += CB) {
+    const int nb = min(CB, nblk - b0);
+    __syncthreads();
+    for (int i = threadIdx.x; i < nb * E; i += 1024) stage[i] = blk[int64_t(b0) * E + i];
+    __syncthreads();
+    if (e < E)
+      for (int b = 0; b < nb; ++b) cnt += stage[b * E + e];
+  }
+  if (e >= E && e < E + S) cnt = int(T);
   build_schedule(cnt, E + S, BM, offs, active, meta, tiles, tmp);
   __syncthreads();
   if (e <= E + S) offsets[e] = offs[e];
-  if (e < E) {
-    int run = offs[e];
-    for (int b = 0; b < nblk; ++b) {
-      const int c = blk[int64_t(b) * E + e];
-      blk[int64_t(b) * E + e] = run;
-      run += c;
+  int run = e < E ? offs[e] : 0;
+  for (int b0 = 0; b0 < nblk; b0 += CB) {
+    const int nb = min(CB, nblk - b0);
+    __syncthreads();
+    for (int i = threadIdx.x; i < nb * E; i += 1024) stage[i] = blk[int64_t(b0) * E + i];
+    __syncthreads();
+    if (e < E) {
+      for (int b = 0; b < nb; ++b) {
+        const int c = stage[b * E + e];
+        stage[b * E + e] = run;
+        run += c;
+      }
     }
+    __syncthreads();
+    for (int i = threadIdx.x; i < nb * E; i += 1024) blk[int64_t(b0) * E + i] = stage[i];
   }
 }
 
-// Stable scatter per block of 256 tokens (4 waves x 64 tokens).  Within a wave
-// the rank of (t, j) among the wave's rows of expert e is the number of lower
-// lanes whose token also chose e: a 64-bit lane mask per (wave, expert) built
-// with LDS atomic ORs.  grid = nblk, block = 256, LDS = 4*E*8 bytes.
+// Stable scatter, one wave per permutation block of 64 tokens.  The rank of
+// (t, j) among its block's rows of expert e is the number of lower lanes whose
+// token also chose e: a 64-bit lane mask per (wave, expert) built with LDS
+// atomic ORs.  grid = ceil(T/256), block = 256, dynamic LDS = 4*E*8 bytes.
 __global__ __launch_bounds__(256) void k_perm_scatter(
     const int32_t* __restrict__ ids, const float* __restrict__ w, int64_t T, int k, int E, int S,
     const int32_t* __restrict__ blk_base, int32_t* __restrict__ row_token,
@@ -126,11 +148,10 @@ __global__ __launch_bounds__(256) void k_perm_scatter(
   __syncthreads();
   if (!valid) return;
   const unsigned long long lower = (1ull << lane) - 1ull;
-  const int32_t* base = blk_base + int64_t(blockIdx.x) * E;
+  const int32_t* base = blk_base + (int64_t(blockIdx.x) * 4 + wv) * E;
   for (int j = 0; j < k; ++j) {
     const int e = ids[t * k + j];
-    int r = base[e] + __popcll(bits[wv * E + e] & lower);
-    for (int v = 0; v < wv; ++v) r += __popcll(bits[v * E + e]);
+    const int r = base[e] + __popcll(bits[wv * E + e] & lower);
     row_token[r] = int32_t(t);
     inv[t * k + j] = r;
     if (row_w) row_w[r] = w[t * k + j];
@@ -169,7 +190,7 @@ __global__ __launch_bounds__(1024) void k_route_permute_small(
   __shared__ int offs[1025];
   const int wv = threadIdx.x >> 6;
   for (int t = wv; t < T; t += 16)
-    select_token<QMAX>(logits + int64_t(t) * E, E, G, Gk, k, ids_lds + t * k, w_lds + t * k);
+    select_token_wave<QMAX>(logits + int64_t(t) * E, E, G, Gk, k, ids_lds + t * k, w_lds + t * k);
   __syncthreads();
   const int nslot = T * k;
   for (int i = threadIdx.x; i < nslot; i += 1024) {
@@ -206,17 +227,25 @@ __global__ __launch_bounds__(1024) void k_route_permute_small(
 }
 
 // ---------------------------------------------------------------------------
+int launch_scan_scatter(const Plan& p, const int32_t* ids, const float* w, int32_t* blk,
+                        int32_t* offsets, int32_t* active, int32_t* meta, int2* tiles,
+                        int32_t* row_token, int32_t* inv, float* row_w, int BM, hipStream_t st) {
+  const unsigned g4 = unsigned((p.T + 255) / 256);
+  hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, st, blk, p.nblk, p.T, p.E, p.S, BM,
+                     offsets, active, meta, tiles);
+  hipLaunchKernelGGL(k_perm_scatter, dim3(g4), dim3(256), size_t(4) * p.E * 8, st, ids, w, p.T,
+                     p.k, p.E, p.S, blk, row_token, inv, row_w);
+  return check_launch();
+}
+
 int launch_permute(const Plan& p, const int32_t* ids, const float* w, int32_t* blk,
                    int32_t* offsets, int32_t* active, int32_t* meta, int2* tiles,
                    int32_t* row_token, int32_t* inv, float* row_w, int BM, hipStream_t st) {
-  const int nblk = p.nblk;
-  hipLaunchKernelGGL(k_perm_count, dim3(nblk), dim3(256), size_t(p.E) * sizeof(int), st, ids, p.T,
-                     p.k, p.E, blk);
-  hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, st, blk, nblk, p.T, p.E, p.S, BM, offsets,
-                     active, meta, tiles);
-  hipLaunchKernelGGL(k_perm_scatter, dim3(nblk), dim3(256), size_t(4) * p.E * 8, st, ids, w, p.T,
-                     p.k, p.E, p.S, blk, row_token, inv, row_w);
-  return check_launch();
+  const unsigned g4 = unsigned((p.T + 255) / 256);
+  hipLaunchKernelGGL(k_perm_count, dim3(g4), dim3(256), size_t(4) * p.E * sizeof(int), st, ids,
+                     p.T, p.k, p.E, blk);
+  return launch_scan_scatter(p, ids, w, blk, offsets, active, meta, tiles, row_token, inv, row_w,
+                             BM, st);
 }
 
 int launch_schedule(const Plan& p, const int32_t* offsets, int32_t* active, int32_t* meta,

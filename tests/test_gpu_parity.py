@@ -49,7 +49,8 @@ def _print_case(*a):
 
 # ----------------------------------------------------------------------------- routing
 @pytest.mark.parametrize("name,T", [("tiny", None), ("decode", None), ("prefill", 300),
-                                    ("fp8", 130), ("inkling", 257), ("decode", 1)])
+                                    ("fp8", 130), ("inkling", 257), ("decode", 1), ("tiny", 300),
+                                    ("prefill", 8192)])
 def test_route(moe, name, T):
     _print_case("route", name, T)
     shape, cpu, dev = _layer(name, T)
@@ -62,6 +63,22 @@ def test_route(moe, name, T):
     np.testing.assert_allclose(logits.cpu().numpy(), l64, rtol=0, atol=2e-5)
     near, _ = check_routing(ids.cpu().numpy(), w.cpu().numpy(), l64, shape)
     print(f"near-ties {int(near.sum())}/{shape.T}")
+
+
+def test_route_e64_generic_path(moe):
+    """E = 64 bf16 experts in 4 groups (vector-FMA logits + thread-per-token selection)."""
+    _print_case("route e64")
+    shape = synth.LayerShape("e64", T=200, H=512, I=128, E=64, G=4, Gk=2, k=6, S=0, act="bf16",
+                             wt="bf16", x_dist="normal", bias_std=0.3, seed=12)
+    cpu = synth.make_layer(shape)
+    dev = to_device(cpu)
+    cfg = config_for(shape)
+    ws = moe.alloc_workspace(cfg)
+    ids, w = moe.route(cfg, dev["x"], dev["w_router"], dev["router_bias"], ws)
+    torch.cuda.synchronize()
+    l64 = mo.router_logits(np_exact(cpu["x"]), np_exact(cpu["w_router"]), np_exact(cpu["router_bias"]))
+    check_routing(ids.cpu().numpy(), w.cpu().numpy(), l64, shape)
+    _forward_check(moe, shape, cpu, dev)
 
 
 def test_route_forced_ties(moe):
@@ -181,7 +198,8 @@ def _forward_check(moe, shape, cpu, dev, sample=None):
 @pytest.mark.parametrize("name,T", [("tiny", None), ("decode", None), ("decode", 1),
                                     ("decode", 16), ("decode", 40), ("prefill", 300),
                                     ("prefill", 1500), ("fp8", 130), ("fp8", 16),
-                                    ("inkling", 100), ("inkling", 420)])
+                                    ("inkling", 100), ("inkling", 420), ("tiny", 300),
+                                    ("tiny", 65)])
 def test_forward(moe, name, T):
     _print_case("forward", name, T)
     shape, cpu, dev = _layer(name, T)
