@@ -1,0 +1,380 @@
+// Decode-sized batches (a handful of tokens): the expert side of the layer in
+// two persistent kernels after the router logits.
+//
+// With a few tokens the layer is a stream over the chosen experts' weights
+// (TensorFold issue #1247 "Ling-3.0-tiny on a Qualcomm board", list "What it does
+// not cover": each expert runs on just the rows that picked it), so both kernels
+// are organised around that stream:
+//   gate/up: every block first routes the T tokens itself from the logits into
+//     LDS (one wave per token selects; thread e places the rows of expert e in
+//     ascending (token, slot) order; block 0 publishes the routing), then each
+//     wave walks work items (active expert, NI weight rows) round-robin over the
+//     grid with the next item's loads in flight while the current one is
+//     multiplied; h (fp32) goes to the workspace;
+//   down + combine: item = (token t, NR output columns),
+//     y[t,n] = sum_j w[t,j] (h[row(t,j)] . Wd[id(t,j)][n]) + sum_s (h[shared row] . Wd_s[n]),
+//     all slots of a batch loaded before any is used, the next item's weights in
+//     flight while the current one is reduced.
+// A single kernel with a device-wide barrier between the two halves measured
+// slower on MI355X than the launch it saves (the cross-XCD arrival counting and
+// cache write-back cost tens of microseconds), so the halves are two launches.
+#include "moe_internal.h"
+#include "route_select.h"
+
+namespace moe {
+
+template <typename TW>
+__device__ __forceinline__ const TW* dexpert(const TW* routed, const TW* shared, int e, int E,
+                                             int64_t stride) {
+  return e < E ? routed + int64_t(e) * stride : shared + int64_t(e - E) * stride;
+}
+
+struct DecodeArgs {
+  const void* x;
+  const float* logits;
+  const void *wg, *wu, *wd, *shg, *shu, *shd;
+  int32_t* ids;        // [T, k] routing outputs (published by block 0)
+  float* w;            // [T, k]
+  int32_t* offsets;    // [E+S+1]
+  int32_t* row_token;  // [R]
+  int32_t* inv;        // [T, k]
+  float* h;            // [R, I] fp32
+  void* y;             // [T, H]
+  int (*mark)(void*);  // stage timing hook between the two launches (host side), or null
+  void* mark_ctx;
+  int T, H, I, E, S, G, Gk, k;
+};
+
+template <typename TA, typename TW, int NS, int QMAX>
+__global__ __launch_bounds__(256) void k_decode_gateup(DecodeArgs a) {
+  constexpr int NI = 2;            // gate/up weight rows per item
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+  const int T = a.T, H = a.H, I = a.I, E = a.E, S = a.S, k = a.k;
+  const int R = T * (k + S), nslot = T * k;
+  TA* xs = reinterpret_cast<TA*>(lds_raw);
+  int32_t* off_l = reinterpret_cast<int32_t*>(lds_raw + ((size_t(T) * H * sizeof(TA) + 15) & ~size_t(15)));
+  int32_t* act_l = off_l + (E + S + 1);
+  int32_t* rt_l = act_l + (E + S);
+  int32_t* ids_l = rt_l + R;
+  int32_t* inv_l = ids_l + nslot;
+  float* w_l = reinterpret_cast<float*>(inv_l + nslot);
+  __shared__ int tmp[8];
+  __shared__ int n_act_l;
+  unsigned long long* bits_l = reinterpret_cast<unsigned long long*>(
+      (reinterpret_cast<uintptr_t>(w_l + nslot) + 7) & ~uintptr_t(7));                       // [4][E]
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const TA* x = static_cast<const TA*>(a.x);
+  const TW* wg = static_cast<const TW*>(a.wg);
+  const TW* wu = static_cast<const TW*>(a.wu);
+  const TW* wd = static_cast<const TW*>(a.wd);
+  const TW* shg = static_cast<const TW*>(a.shg);
+  const TW* shu = static_cast<const TW*>(a.shu);
+  const TW* shd = static_cast<const TW*>(a.shd);
+
+  // ---------------------------------------------------------------- 1. routing
+  constexpr int CH = 16 / sizeof(TA);
+  for (int c = threadIdx.x; c < T * H / CH; c += 256)
+    *reinterpret_cast<uint4*>(xs + c * CH) = *reinterpret_cast<const uint4*>(x + int64_t(c) * CH);
+  for (int t = wv; t < T; t += 4)
+    select_token_wave<QMAX>(a.logits + int64_t(t) * E, E, a.G, a.Gk, k, ids_l + t * k, w_l + t * k);
+  // slot i = t*k + j.  Wave w owns slots [64w, 64w+64): bit (i % 64) of
+  // bits[w][e] says slot i chose expert e, so a slot's rank among its expert's
+  // rows is a popcount of the lower bits (rows stay in ascending slot order).
+  for (int i = threadIdx.x; i < 4 * E; i += 256) bits_l[i] = 0ull;
+  __syncthreads();
+  if (threadIdx.x < nslot) atomicOr(&bits_l[wv * E + ids_l[threadIdx.x]], 1ull << lane);
+  __syncthreads();
+  const bool pub = blockIdx.x == 0;
+  int tot = 0, nact = 0;
+  for (int e0 = 0; e0 < E + S; e0 += 256) {
+    const int e = e0 + threadIdx.x;
+    int cnt = 0;
+    if (e < E)
+      cnt = __popcll(bits_l[e]) + __popcll(bits_l[E + e]) + __popcll(bits_l[2 * E + e]) +
+            __popcll(bits_l[3 * E + e]);
+    else if (e < E + S)
+      cnt = T;
+    int sum, nsum;
+    const int off = tot + block_exclusive_scan_256(cnt, tmp, sum);
+    const int pos = nact + block_exclusive_scan_256(cnt > 0 ? 1 : 0, tmp, nsum);
+    if (e < E + S) off_l[e] = off;
+    if (cnt > 0) act_l[pos] = e;
+    if (e >= E && e < E + S)
+      for (int t = 0; t < T; ++t) rt_l[off + t] = t;
+    tot += sum;
+    nact += nsum;
+  }
+  if (threadIdx.x == 0) {
+    off_l[E + S] = tot;
+    n_act_l = nact;
+  }
+  __syncthreads();
+  if (threadIdx.x < nslot) {
+    const int i = threadIdx.x, e = ids_l[i];
+    int r = off_l[e] + __popcll(bits_l[wv * E + e] & ((1ull << lane) - 1ull));
+    for (int v = 0; v < wv; ++v) r += __popcll(bits_l[v * E + e]);
+    rt_l[r] = i / k;
+    inv_l[i] = r;
+  }
+  __syncthreads();
+  if (pub) {
+    for (int i = threadIdx.x; i < nslot; i += 256) {
+      a.ids[i] = ids_l[i];
+      a.w[i] = w_l[i];
+      a.inv[i] = inv_l[i];
+    }
+    for (int i = threadIdx.x; i <= E + S; i += 256) a.offsets[i] = off_l[i];
+    for (int i = threadIdx.x; i < R; i += 256) a.row_token[i] = rt_l[i];
+  }
+
+  // ---------------------------------------------------------------- 2. gate/up
+  const int ipe = I / NI;
+  const int total = n_act_l * ipe;
+  const int64_t mstride = int64_t(I) * H;
+  const int gstride = gridDim.x * 4;
+  auto load_gu = [&](int item, Chunk8<TW> (&cg)[NS][NI], Chunk8<TW> (&cu)[NS][NI]) {
+    const int u = item / ipe, i0 = (item - u * ipe) * NI;
+    const int e = act_l[u];
+    const TW* gp = dexpert(wg, shg, e, E, mstride) + int64_t(i0) * H;
+    const TW* up = dexpert(wu, shu, e, E, mstride) + int64_t(i0) * H;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int h = s * 512 + lane * 8;
+      if (h < H) {
+#pragma unroll
+        for (int ii = 0; ii < NI; ++ii) {
+          cg[s][ii].load(gp + int64_t(ii) * H + h);
+          cu[s][ii].load(up + int64_t(ii) * H + h);
+        }
+      }
+    }
+  };
+  auto compute_gu = [&](int item, const Chunk8<TW> (&cg)[NS][NI], const Chunk8<TW> (&cu)[NS][NI]) {
+    const int u = item / ipe, i0 = (item - u * ipe) * NI;
+    const int e = act_l[u];
+    for (int r = off_l[e]; r < off_l[e + 1]; ++r) {
+      const TA* xr = xs + rt_l[r] * H;
+      float ag[NI], au[NI];
+#pragma unroll
+      for (int ii = 0; ii < NI; ++ii) ag[ii] = au[ii] = 0.f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int h = s * 512 + lane * 8;
+        if (h < H) {
+          float xv[8];
+          load8(xr + h, xv);
+#pragma unroll
+          for (int ii = 0; ii < NI; ++ii) {
+            float f[8];
+            cg[s][ii].get(f);
+            ag[ii] = dot8(f, xv, ag[ii]);
+            cu[s][ii].get(f);
+            au[ii] = dot8(f, xv, au[ii]);
+          }
+        }
+      }
+#pragma unroll
+      for (int ii = 0; ii < NI; ++ii) {
+        const float g = wave_sum(ag[ii]);
+        const float v = wave_sum(au[ii]);
+        if (lane == ii) a.h[int64_t(r) * I + i0 + ii] = silu(g) * v;
+      }
+    }
+  };
+  {
+    Chunk8<TW> ga[NS][NI], ua[NS][NI], gb[NS][NI], ub[NS][NI];
+    int item = blockIdx.x * 4 + wv;
+    if (item < total) load_gu(item, ga, ua);
+    while (item < total) {
+      int nxt = item + gstride;
+      if (nxt < total) load_gu(nxt, gb, ub);
+      compute_gu(item, ga, ua);
+      item = nxt;
+      if (item >= total) break;
+      nxt = item + gstride;
+      if (nxt < total) load_gu(nxt, ga, ua);
+      compute_gu(item, gb, ub);
+      item = nxt;
+    }
+  }
+
+}
+
+template <typename TA, typename TW, int NSD>
+__global__ __launch_bounds__(256) void k_decode_down(DecodeArgs a) {
+  constexpr int NR = 4;            // output columns per item
+  constexpr int JB = 8;            // slots per load batch
+  const int T = a.T, H = a.H, I = a.I, E = a.E, S = a.S, k = a.k;
+  const int nslot = T * k;
+  __shared__ int32_t ids_l[256], inv_l[256];
+  __shared__ float w_l[256];
+  __shared__ int32_t offsh_l[32];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const TW* wd = static_cast<const TW*>(a.wd);
+  const TW* shd = static_cast<const TW*>(a.shd);
+  for (int i = threadIdx.x; i < nslot; i += 256) {
+    ids_l[i] = a.ids[i];
+    inv_l[i] = a.inv[i];
+    w_l[i] = a.w[i];
+  }
+  for (int i = threadIdx.x; i < S; i += 256) offsh_l[i] = a.offsets[E + i];
+  __syncthreads();
+
+  const int nblk_n = (H + NR - 1) / NR;
+  const int dtotal = T * nblk_n;
+  const int nsl = k + S;
+  const int64_t dstride = int64_t(H) * I;
+  const int gstride = gridDim.x * 4;
+  auto slot_of = [&](int t, int j, int& e, int& r, float& wt) {
+    if (j < k) {
+      e = ids_l[t * k + j];
+      r = inv_l[t * k + j];
+      wt = w_l[t * k + j];
+    } else {
+      e = E + (j - k);
+      r = offsh_l[j - k] + t;
+      wt = 1.f;
+    }
+  };
+  auto load = [&](int item, int jb, Chunk8<TW> (&cw)[JB][NSD][NR], float (&hv)[JB][NSD][8],
+                  float (&wt)[JB]) {
+    const int t = item / nblk_n, n0 = (item - t * nblk_n) * NR;
+#pragma unroll
+    for (int jj = 0; jj < JB; ++jj) {
+      const int j = jb + jj;
+      wt[jj] = 0.f;
+      if (j < nsl) {
+        int e, r;
+        slot_of(t, j, e, r, wt[jj]);
+        const TW* dp = dexpert(wd, shd, e, E, dstride) + int64_t(n0) * I;
+#pragma unroll
+        for (int s = 0; s < NSD; ++s) {
+          const int kk = s * 512 + lane * 8;
+          if (kk < I) {
+#pragma unroll
+            for (int nn = 0; nn < NR; ++nn)
+              if (n0 + nn < H) cw[jj][s][nn].load(dp + int64_t(nn) * I + kk);
+            load8(a.h + int64_t(r) * I + kk, hv[jj][s]);
+          }
+        }
+      }
+    }
+  };
+  Chunk8<TW> cw[JB][NSD][NR];
+  float hv[JB][NSD][8];
+  float wt[JB];
+  for (int item = blockIdx.x * 4 + wv; item < dtotal; item += gstride) {
+    const int t = item / nblk_n, n0 = (item - t * nblk_n) * NR;
+    float acc[NR];
+#pragma unroll
+    for (int nn = 0; nn < NR; ++nn) acc[nn] = 0.f;
+    for (int jb = 0; jb < nsl; jb += JB) {
+      load(item, jb, cw, hv, wt);
+#pragma unroll
+      for (int jj = 0; jj < JB; ++jj) {
+        if (jb + jj < nsl) {
+#pragma unroll
+          for (int s = 0; s < NSD; ++s) {
+            const int kk = s * 512 + lane * 8;
+            if (kk < I) {
+#pragma unroll
+              for (int nn = 0; nn < NR; ++nn) {
+                float f[8];
+                cw[jj][s][nn].get(f);
+                acc[nn] = fmaf(wt[jj], dot8(f, hv[jj][s], 0.f), acc[nn]);
+              }
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int nn = 0; nn < NR; ++nn) {
+      const float v = wave_sum(acc[nn]);
+      if (lane == nn && n0 + nn < H) {
+        if (sizeof(TA) == 2)
+          static_cast<bf16_t*>(a.y)[int64_t(t) * H + n0 + nn] = f32_to_bf16(v);
+        else
+          static_cast<float*>(a.y)[int64_t(t) * H + n0 + nn] = v;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+static size_t decode_lds(const Plan& p) {
+  const size_t tsize = p.act == MOE_F32 ? 4 : 2;
+  return ((size_t(p.T) * p.H * tsize + 15) & ~size_t(15)) +
+         size_t(2 * (p.E + p.S) + 1 + p.R + 3 * p.T * p.k + 1) * 4 + size_t(4) * p.E * 8 + 8;
+}
+
+bool decode_ffn_ok(const Plan& p) {
+  return p.skinny && p.T <= 16 && p.T * p.k <= 256 && p.S <= 32 && p.H <= 2048 && p.I <= 1024 &&
+         p.I % 2 == 0 && decode_lds(p) <= size_t(64) * 1024;
+}
+
+static int persistent_blocks(const void* kern, size_t lds, int* blocks) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, lds) != hipSuccess) {
+    check_launch();
+    return MOE_ERR_HIP;
+  }
+  *blocks = cus * std::max(1, std::min(per_cu, 2));
+  return MOE_OK;
+}
+
+template <typename TA, typename TW, int NS, int NSD, int Q>
+static int launch_decode_t(const Plan& p, const DecodeArgs& a, hipStream_t st) {
+  const auto k1 = k_decode_gateup<TA, TW, NS, Q>;
+  const auto k2 = k_decode_down<TA, TW, NSD>;
+  const size_t lds = decode_lds(p);
+  int b1 = 0, b2 = 0;
+  MOE_TRY(persistent_blocks(reinterpret_cast<const void*>(k1), lds, &b1));
+  MOE_TRY(persistent_blocks(reinterpret_cast<const void*>(k2), 0, &b2));
+  hipLaunchKernelGGL(k1, dim3(b1), dim3(256), lds, st, a);
+  MOE_TRY(check_launch());
+  if (a.mark) MOE_TRY(a.mark(a.mark_ctx));
+  hipLaunchKernelGGL(k2, dim3(b2), dim3(256), 0, st, a);
+  return check_launch();
+}
+
+int launch_decode_ffn(const Plan& p, const void* x, const float* logits, const moe_weights* w,
+                      int32_t* ids, float* wts, int32_t* offsets, int32_t* row_token,
+                      int32_t* inv, float* h, void* y, int (*mark)(void*), void* mark_ctx,
+                      hipStream_t st) {
+  DecodeArgs a{};
+  a.x = x; a.logits = logits;
+  a.wg = w->w_gate; a.wu = w->w_up; a.wd = w->w_down;
+  a.shg = w->sh_gate; a.shu = w->sh_up; a.shd = w->sh_down;
+  a.ids = ids; a.w = wts; a.offsets = offsets; a.row_token = row_token; a.inv = inv;
+  a.h = h; a.y = y; a.mark = mark; a.mark_ctx = mark_ctx;
+  a.T = int(p.T); a.H = p.H; a.I = p.I; a.E = p.E; a.S = p.S; a.G = p.G; a.Gk = p.Gk; a.k = p.k;
+  const int ns = (p.H + 511) / 512, nsd = (p.I + 511) / 512;
+#define MOE_DQ(TA, TW, NSV, NSDV)                                            \
+  {                                                                          \
+    if (p.E <= 64) return launch_decode_t<TA, TW, NSV, NSDV, 1>(p, a, st);   \
+    if (p.E <= 128) return launch_decode_t<TA, TW, NSV, NSDV, 2>(p, a, st);  \
+    if (p.E <= 256) return launch_decode_t<TA, TW, NSV, NSDV, 4>(p, a, st);  \
+    if (p.E <= 512) return launch_decode_t<TA, TW, NSV, NSDV, 8>(p, a, st);  \
+    return launch_decode_t<TA, TW, NSV, NSDV, 16>(p, a, st);                 \
+  }
+#define MOE_DNS(TA, TW, NSDV)                  \
+  {                                            \
+    if (ns <= 1) MOE_DQ(TA, TW, 1, NSDV)       \
+    if (ns == 2) MOE_DQ(TA, TW, 2, NSDV)       \
+    if (ns == 3) MOE_DQ(TA, TW, 3, NSDV)       \
+    MOE_DQ(TA, TW, 4, NSDV)                    \
+  }
+  if (p.wt == MOE_F32) {
+    if (nsd <= 1) MOE_DNS(float, float, 1)
+    MOE_DNS(float, float, 2)
+  }
+  if (nsd <= 1) MOE_DNS(bf16_t, bf16_t, 1)
+  MOE_DNS(bf16_t, bf16_t, 2)
+#undef MOE_DNS
+#undef MOE_DQ
+}
+
+}  // namespace moe

@@ -15,38 +15,6 @@
 
 namespace moe {
 
-// Eight weights as they sit in memory (16 bytes of bf16 or 32 bytes of fp32).
-template <typename TW> struct Chunk8;
-template <> struct Chunk8<bf16_t> {
-  uint4 v;
-  __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
-  __device__ __forceinline__ void get(float (&o)[8]) const {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      o[2 * i] = __uint_as_float(w[i] << 16);
-      o[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-    }
-  }
-};
-template <> struct Chunk8<float> {
-  float4 a, b;
-  __device__ __forceinline__ void load(const float* p) {
-    a = *reinterpret_cast<const float4*>(p);
-    b = *reinterpret_cast<const float4*>(p + 4);
-  }
-  __device__ __forceinline__ void get(float (&o)[8]) const {
-    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
-    o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
-  }
-};
-
-__device__ __forceinline__ float dot8(const float (&a)[8], const float (&b)[8], float acc) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc = fmaf(a[i], b[i], acc);
-  return acc;
-}
-
 template <typename TW>
 __device__ __forceinline__ const TW* expert_base(const TW* routed, const TW* shared, int e, int E,
                                                  int64_t stride) {

@@ -12,7 +12,7 @@ namespace moe {
 
 static thread_local char g_hip_error[256] = "no HIP error recorded";
 
-static int record_hip_error(hipError_t err) {
+int record_hip_error(hipError_t err) {
   snprintf(g_hip_error, sizeof(g_hip_error), "HIP error %d: %s", int(err), hipGetErrorString(err));
   return MOE_ERR_HIP;
 }
@@ -105,12 +105,6 @@ static int check_experts(const Plan& p, const moe_weights* w) {
   }
   return MOE_OK;
 }
-
-#define MOE_TRY(expr)              \
-  do {                             \
-    const int rc_ = (expr);        \
-    if (rc_ != MOE_OK) return rc_; \
-  } while (0)
 
 // Expert FFN on permuted rows (schedule already in the workspace).
 static int run_experts(const Plan& p, const void* x, const int32_t* off, const int32_t* rowtok,
@@ -229,6 +223,21 @@ static int forward_impl(const moe_config* cfg, const void* x, const moe_weights*
 
   MOE_TRY(mark(0));
   int32_t* blk = at<int32_t>(ws, p.o_blk);
+  if (p.fused_down && decode_ffn_ok(p)) {
+    // decode: the logits, then gate/up (routing in every block) and down + combine
+    MOE_TRY(launch_logits(p, x, w->w_router, w->router_bias, logits, stream));
+    MOE_TRY(mark(1));
+    struct Hook { hipEvent_t ev; hipStream_t st; } hook{ev ? ev[2] : nullptr, stream};
+    auto hook_fn = [](void* c) -> int {
+      const Hook* hk = static_cast<const Hook*>(c);
+      const hipError_t err = hipEventRecord(hk->ev, hk->st);
+      return err == hipSuccess ? MOE_OK : record_hip_error(err);
+    };
+    MOE_TRY(launch_decode_ffn(p, x, logits, w, ids, wts, off, rowtok, inv, at<float>(ws, p.o_h), y,
+                              ev ? +hook_fn : nullptr, &hook, stream));
+    MOE_TRY(mark(3));
+    return mark(4);
+  }
   if (p.small_route) {
     MOE_TRY(launch_logits(p, x, w->w_router, w->router_bias, logits, stream));
     MOE_TRY(launch_route_permute_small(p, logits, ids, wts, off, active, meta, tiles, rowtok, inv,

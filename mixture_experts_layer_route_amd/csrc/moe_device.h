@@ -52,6 +52,38 @@ __device__ __forceinline__ void load8(const float* p, float (&o)[8]) {
   o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
 }
 
+// Eight weights as they sit in memory (16 bytes of bf16 or 32 bytes of fp32).
+template <typename TW> struct Chunk8;
+template <> struct Chunk8<bf16_t> {
+  uint4 v;
+  __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void get(float (&o)[8]) const {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = __uint_as_float(w[i] << 16);
+      o[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+};
+template <> struct Chunk8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ void get(float (&o)[8]) const {
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+    o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+  }
+};
+
+__device__ __forceinline__ float dot8(const float (&a)[8], const float (&b)[8], float acc) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc = fmaf(a[i], b[i], acc);
+  return acc;
+}
+
 // OCP e4m3 (bias 7, 3 mantissa bits, max 448, no infinities), round to nearest
 // even, saturating.  Built from the format definition: normals are
 // (8 + m) * 2^(e-10) for e = 1..15 (code e<<3 | m), subnormals m * 2^-9.
@@ -120,6 +152,24 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   a = a > b ? a : b;
   c = c > d ? c : d;
   return a > c ? a : c;
+}
+
+// Exclusive scan over a block of 256 threads; `tmp` holds >= 4 ints.  All threads call it.
+__device__ __forceinline__ int block_exclusive_scan_256(int v, int* tmp, int& total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) tmp[wv] = x;
+  __syncthreads();
+  int base = 0;
+  for (int i = 0; i < wv; ++i) base += tmp[i];
+  total = tmp[0] + tmp[1] + tmp[2] + tmp[3];
+  __syncthreads();
+  return base + x - v;
 }
 
 // Total order key for (score desc, index asc) arg-max: larger key wins.

@@ -30,8 +30,15 @@ struct Plan {
       o_h, o_ypw, o_yp32, o_xq, o_sx, o_hq, o_shq, total;
 };
 
+#define MOE_TRY(expr)              \
+  do {                             \
+    const int rc_ = (expr);        \
+    if (rc_ != MOE_OK) return rc_; \
+  } while (0)
+
 int make_plan(const moe_config* cfg, Plan* p);
 int check_launch();
+int record_hip_error(hipError_t err);
 
 int launch_logits(const Plan& p, const void* x, const void* wr, const float* bias, float* logits,
                   hipStream_t st);
@@ -52,6 +59,13 @@ int launch_route_permute_small(const Plan& p, const float* logits, int32_t* ids,
                                int32_t* offsets, int32_t* active, int32_t* meta, int2* tiles,
                                int32_t* row_token, int32_t* inv, float* row_w, int BM,
                                hipStream_t st);
+bool decode_ffn_ok(const Plan& p);
+// Decode path: gate/up (with in-kernel routing) then down + combine; `mark` (may be null)
+// is called between the two launches.
+int launch_decode_ffn(const Plan& p, const void* x, const float* logits, const moe_weights* w,
+                      int32_t* ids, float* wts, int32_t* offsets, int32_t* row_token,
+                      int32_t* inv, float* h, void* y, int (*mark)(void*), void* mark_ctx,
+                      hipStream_t st);
 int launch_gateup_skinny(const Plan& p, const void* x, const int32_t* row_token,
                          const int32_t* offsets, const int32_t* active, const int32_t* meta,
                          const moe_weights* w, float* h, hipStream_t st);

@@ -32,16 +32,48 @@ __device__ void select_token_wave(const float* __restrict__ l, int E, int G, int
 #pragma unroll
   for (int q = 0; q < QMAX; ++q) {
     const int e = lane + 64 * q;
-    lv[q] = e < E ? l[e] : 0.f;
+    lv[q] = e < E ? l[e] : -__builtin_huge_valf();
   }
   uint64_t kept = ~0ull;
   if (G > 1) {
-    uint64_t gkey = 0;
-    if (lane < G) {
-      float m = l[lane * n];
-      for (int i = 1; i < n; ++i) m = fmaxf(m, l[lane * n + i]);
-      gkey = rank_key(m, lane);
+    // group maxima from the logits already in registers: lane g ends up with group g's score
+    float gm = -__builtin_huge_valf();
+    if ((n & (n - 1)) == 0 && n <= 64) {
+      // groups are aligned runs of n lanes inside one 64-expert slice: segmented
+      // max by DPP inside rows of 16 (plus readlane across rows for n = 32, 64),
+      // then lane g picks group g's value from lane (g*n) % 64 of slice g*n/64
+#pragma unroll
+      for (int q = 0; q < QMAX; ++q) {
+        float v = lv[q];
+        if (n >= 2) v = fmaxf(v, dppf<0xB1>(v));     // quad_perm [1,0,3,2]
+        if (n >= 4) v = fmaxf(v, dppf<0x4E>(v));     // quad_perm [2,3,0,1]
+        if (n >= 8) v = fmaxf(v, dppf<0x141>(v));    // row_half_mirror
+        if (n >= 16) v = fmaxf(v, dppf<0x140>(v));   // row_mirror
+        const float r0 = lanef(v, 0), r1 = lanef(v, 16), r2 = lanef(v, 32), r3 = lanef(v, 48);
+        const int per = 64 / n;                      // groups in this slice
+        const int g = lane - q * per;                // this lane's group inside slice q
+        const float sh = __shfl(v, (g * n) & 63, 64);   // whole wave active here
+        if (g >= 0 && g < per && lane < G) {
+          if (n >= 64) gm = fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+          else if (n == 32) gm = g == 0 ? fmaxf(r0, r1) : fmaxf(r2, r3);
+          else gm = sh;
+        }
+      }
+    } else if (n % 64 == 0) {
+      // a group is n/64 whole slices
+#pragma unroll
+      for (int q = 0; q < QMAX; ++q) {
+        const float v = wave_max(lv[q]);
+        if (lane == (64 * q) / n) gm = fmaxf(gm, v);
+      }
+    } else {
+      if (lane < G) {
+        float m = l[lane * n];
+        for (int i = 1; i < n; ++i) m = fmaxf(m, l[lane * n + i]);
+        gm = m;
+      }
     }
+    uint64_t gkey = lane < G ? rank_key(gm, lane) : 0ull;
     kept = 0;
     for (int r = 0; r < Gk; ++r) {
       const uint64_t win = wave_max_u64(gkey);

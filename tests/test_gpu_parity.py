@@ -199,7 +199,7 @@ def _forward_check(moe, shape, cpu, dev, sample=None):
                                     ("decode", 16), ("decode", 40), ("prefill", 300),
                                     ("prefill", 1500), ("fp8", 130), ("fp8", 16),
                                     ("inkling", 100), ("inkling", 420), ("tiny", 300),
-                                    ("tiny", 65)])
+                                    ("tiny", 65), ("inkling", 8), ("decode", 7)])
 def test_forward(moe, name, T):
     _print_case("forward", name, T)
     shape, cpu, dev = _layer(name, T)
