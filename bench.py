@@ -48,30 +48,75 @@ def parse():
     ap.add_argument("--sets", type=int, default=0, help="weight copies rotated per step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="host time budget for the oracle baseline (0 = skip)")
+    ap.add_argument("--event-every", type=int, default=8,
+                    help="attach kernel start/stop events to every n-th timed step")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB five times (a known byte "
+                         "count for scaling the profiler's FETCH_SIZE / WRITE_SIZE) and exit")
     return ap.parse_args()
 
 
-def dominant(shape, stage_ms, U):
-    """Roofline of the gate/up projection (the largest stage on every workload)."""
-    T, H, I, E, k, S = shape.T, shape.H, shape.I, shape.E, shape.k, shape.S
-    Rk = T * k
-    ms = stage_ms["gateup"]
-    wbytes = 1 if shape.wt == "e4m3" else (4 if shape.wt == "f32" else 2)
-    if shape.name in ("prefill",):
-        flops = 2.0 * (Rk + T * S) * H * 2 * I
+def copy_calibration(mib):
+    import torch
+    n = mib << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.mul(src, 1.0, out=dst)      # one elementwise kernel: reads n bytes, writes n
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "repeats": 5}),
+          flush=True)
+
+
+def measured_traffic(workload, which):
+    """HBM bytes per launch of kernel `which` from the committed counter summary
+    (profiles/<workload>_traffic.json: rocprofv3 FETCH_SIZE and WRITE_SIZE, scaled by a
+    copy-kernel calibration).  None when there is none, or when the kernel sources have
+    changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    h = hashlib.sha256()
+    src = os.path.join(ROOT, "mixture_experts_layer_route_amd", "csrc")
+    for name in sorted(os.listdir(src)):
+        h.update(name.encode())
+        with open(os.path.join(src, name), "rb") as f:
+            h.update(f.read())
+    if rec.get("sources_sha256") != h.hexdigest() or which not in rec.get("kernels", {}):
+        return None
+    return rec["kernels"][which]["hbm_bytes_per_launch"]
+
+
+def kernel_roofline(shape, which, ms, U):
+    """Roofline entry of one expert kernel ("gateup" or "down") from its measured
+    average duration `ms`: weight-stream bytes for few rows per expert, matrix-core
+    flops for large batches."""
+    T, H, I, k, S = shape.T, shape.H, shape.I, shape.k, shape.S
+    R = T * (k + S)
+    mats = 2 if which == "gateup" else 1          # gate+up, or down
+    name = ("gate/up expert kernel (SwiGLU fused)" if which == "gateup"
+            else "down expert kernel (routing weight applied)")
+    if shape.name == "prefill":
+        flops = 2.0 * R * H * I * mats
         achieved = flops / (ms * 1e-3) / 1e12
         return {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
-                "kernel": "gate/up grouped GEMM + SwiGLU",
-                "per_launch": f"{flops / 1e9:.2f} GFLOP = 2*R*H*2I, R={Rk + T * S}"}
-    # weight-stream bound: each touched expert's gate and up matrices once
-    per_expert = 2 * I * H * wbytes + (2 * (I // 128) * (H // 128) * 4 if shape.wt == "e4m3" else 0)
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic(shape.name, which),
+                "kernel": name, "kernel_us": round(ms * 1e3, 2),
+                "per_launch": f"{flops / 1e9:.2f} GFLOP = 2*R*H*I*{mats}, R={R} rows"}
+    wbytes = {"e4m3": 1, "f32": 4, "bf16": 2}[shape.wt]
+    scales = mats * (I // 128) * (H // 128) * 4 if shape.wt == "e4m3" else 0
+    per_expert = mats * I * H * wbytes + scales
     abytes = U * per_expert
     achieved = abytes / (ms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "gate/up expert projection + SwiGLU",
-            "per_launch": f"{abytes} B = {U} touched experts x {per_expert} B (gate+up weights)"}
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(shape.name, which), "kernel": name,
+            "kernel_us": round(ms * 1e3, 2),
+            "per_launch": f"{abytes} B = {U} touched experts x {per_expert} B of weights"}
 
 
 def cpu_baseline(shape, cpu, budget_s):
@@ -107,6 +152,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer is built "
               "and measured on a single MI355X", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     import torch
     import mixture_experts_layer_route_amd as moe
     import synth
@@ -151,27 +199,43 @@ def main():
     K, W = args.steps, args.warmup
     for i in range(W):
         moe.forward(cfg, x, None, ws, y=y, wst=wsts[i % nsets])
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.TIMED_STAGES)] for _ in range(K)]
-    for row in ev:
+    # start/stop events attached to the gate/up and down kernel dispatches of every
+    # n-th timed step (each attached event costs a few microseconds of queue time)
+    every = max(1, args.event_every)
+    timed = list(range(0, K, every))
+    ev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(moe.TIMED_EVENTS)] for i in timed}
+    for row in ev.values():
         for e in row:
             e.record()
     torch.cuda.synchronize()
-    arrays = [(ctypes.c_void_p * moe.TIMED_STAGES)(*[e.cuda_event for e in row]) for row in ev]
+    arrays = {i: (ctypes.c_void_p * moe.TIMED_EVENTS)(*[e.cuda_event for e in row])
+              for i, row in ev.items()}
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for i in range(K):
-        moe.forward_timed(cfg, x, wsts[i % nsets], ws, y, arrays[i])
+        if i in arrays:
+            moe.forward_timed(cfg, x, wsts[i % nsets], ws, y, arrays[i])
+        else:
+            moe.forward(cfg, x, None, ws, y=y, wst=wsts[i % nsets])
     end.record()
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / K
-    names = ("route", "gateup", "down", "combine")
-    stage_ms = {n: float(np.mean([ev[i][s].elapsed_time(ev[i][s + 1]) for i in range(K)]))
-                for s, n in enumerate(names)}
-    log("stage ms: " + ", ".join(f"{n} {v * 1e3:.1f} us" for n, v in stage_ms.items()))
+    kern_ms = {"gateup": float(np.mean([r[0].elapsed_time(r[1]) for r in ev.values()])),
+               "down": float(np.mean([r[2].elapsed_time(r[3]) for r in ev.values()]))}
+    # the same steps with no events at all
+    start.record()
+    for i in range(K):
+        moe.forward(cfg, x, None, ws, y=y, wst=wsts[i % nsets])
+    end.record()
+    torch.cuda.synchronize()
+    ms_plain = start.elapsed_time(end) / K
+    log(f"step {ms_per_step * 1e3:.2f} us (untimed kernels {ms_plain * 1e3:.2f} us); kernels: "
+        + ", ".join(f"{n} {v * 1e3:.2f} us" for n, v in kern_ms.items()))
     tokens_per_s = shape.T / (ms_per_step * 1e-3)
+    which = max(kern_ms, key=kern_ms.get)
+    roof = kernel_roofline(shape, which, kern_ms[which], U)
 
-    roof = dominant(shape, stage_ms, U)
     res = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": K, "warmup": W, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
@@ -181,7 +245,9 @@ def main():
         "config": {"workload": shape.name, "T": shape.T, "H": shape.H, "I": shape.I,
                    "E": shape.E, "G": shape.G, "Gk": shape.Gk, "k": shape.k, "S": shape.S,
                    "weight_sets": nsets, "touched_experts": U},
-        "stage_us": {n: round(v * 1e3, 2) for n, v in stage_ms.items()},
+        "kernel_us": {n: round(v * 1e3, 2) for n, v in kern_ms.items()},
+        "kernel_events_on_steps": f"every {every}th ({len(timed)} of {K})",
+        "ms_per_step_without_kernel_events": round(ms_plain, 5),
         "parity_rel_l2": float(f"{err:.3e}"),
         "roofline": roof,
     }

@@ -173,18 +173,19 @@ int moe_forward(const moe_config* cfg, const void* x, const moe_weights* w, void
                 void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
- * moe_forward with stage timing, for benchmarks and profilers: identical work
- * and results, plus hipEventRecord(stage_events[i], stream) at the stage
- * boundaries: [0] before the router; [1] after routing and permutation; [2]
- * after the gate/up projection with SwiGLU (and the e4m3 quantisation of x);
- * [3] after the down projection (and the e4m3 quantisation of h); [4] after
- * the combine ([3] and [4] coincide when the down projection is fused with
- * the combine).  `stage_events` holds MOE_TIMED_STAGES caller-created events.
+ * moe_forward with kernel timing, for benchmarks: identical work and results;
+ * the four caller-created events are attached to two kernel dispatches
+ * themselves (hipExtLaunchKernel start/stop events, so no packet is added
+ * between kernels): kernel_events[0], [1] start and stop of the gate/up expert
+ * kernel (SwiGLU fused; for up to 16 tokens it also recomputes the routing),
+ * [2], [3] start and stop of the down-projection kernel (fused with the
+ * combine for up to 16 tokens).  hipEventElapsedTime(ev[0], ev[1]) is then
+ * that kernel's duration.  MOE_ERR_ARG if any of the events is NULL.
  */
-#define MOE_TIMED_STAGES 5
+#define MOE_TIMED_EVENTS 4
 int moe_forward_timed(const moe_config* cfg, const void* x, const moe_weights* w, void* y,
                       int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
-                      hipStream_t stream, hipEvent_t* stage_events);
+                      hipStream_t stream, hipEvent_t* kernel_events);
 
 /* Static description of a status code (for MOE_ERR_HIP: the last HIP error text
    seen by this thread).  Never NULL. */

@@ -37,7 +37,7 @@ class MoeWeights(ctypes.Structure):
 
 ENTRY_POINTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn",
                 "moe_combine", "moe_forward", "moe_forward_timed", "moe_strerror")
-TIMED_STAGES = 5   # MOE_TIMED_STAGES: router+permute | gate/up | down | combine boundaries
+TIMED_EVENTS = 4   # MOE_TIMED_EVENTS: start/stop of the gate/up kernel, start/stop of the down kernel
 
 _lib = None
 
@@ -170,8 +170,9 @@ def forward(cfg, x, weights: dict, ws, y: Optional[torch.Tensor] = None,
 
 
 def forward_timed(cfg, x, wst: MoeWeights, ws, y, events_array) -> None:
-    """moe_forward plus hipEventRecord at the stage boundaries.  `events_array` is a
-    ctypes array of MOE_TIMED_STAGES hipEvent_t handles (torch.cuda.Event.cuda_event)."""
+    """moe_forward with start/stop events attached to the gate/up and down kernel
+    dispatches.  `events_array` is a ctypes array of MOE_TIMED_EVENTS hipEvent_t
+    handles (torch.cuda.Event(enable_timing=True).cuda_event)."""
     _check(load_library().moe_forward_timed(ctypes.byref(cfg), _ptr(x), ctypes.byref(wst), _ptr(y),
                                             None, None, _ptr(ws), ws.numel(), _stream(),
                                             events_array))

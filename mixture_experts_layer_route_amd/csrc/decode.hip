@@ -40,8 +40,6 @@ struct DecodeArgs {
   int32_t* inv;        // [T, k]
   float* h;            // [R, I] fp32
   void* y;             // [T, H]
-  int (*mark)(void*);  // stage timing hook between the two launches (host side), or null
-  void* mark_ctx;
   int T, H, I, E, S, G, Gk, k;
 };
 
@@ -333,23 +331,21 @@ static int launch_decode_t(const Plan& p, const DecodeArgs& a, hipStream_t st) {
   int b1 = 0, b2 = 0;
   MOE_TRY(persistent_blocks(reinterpret_cast<const void*>(k1), lds, &b1));
   MOE_TRY(persistent_blocks(reinterpret_cast<const void*>(k2), 0, &b2));
-  hipLaunchKernelGGL(k1, dim3(b1), dim3(256), lds, st, a);
+  launch_kernel(p, kTimeGateUp, k1, dim3(b1), dim3(256), lds, st, a);
   MOE_TRY(check_launch());
-  if (a.mark) MOE_TRY(a.mark(a.mark_ctx));
-  hipLaunchKernelGGL(k2, dim3(b2), dim3(256), 0, st, a);
+  launch_kernel(p, kTimeDown, k2, dim3(b2), dim3(256), 0, st, a);
   return check_launch();
 }
 
 int launch_decode_ffn(const Plan& p, const void* x, const float* logits, const moe_weights* w,
                       int32_t* ids, float* wts, int32_t* offsets, int32_t* row_token,
-                      int32_t* inv, float* h, void* y, int (*mark)(void*), void* mark_ctx,
-                      hipStream_t st) {
+                      int32_t* inv, float* h, void* y, hipStream_t st) {
   DecodeArgs a{};
   a.x = x; a.logits = logits;
   a.wg = w->w_gate; a.wu = w->w_up; a.wd = w->w_down;
   a.shg = w->sh_gate; a.shu = w->sh_up; a.shd = w->sh_down;
   a.ids = ids; a.w = wts; a.offsets = offsets; a.row_token = row_token; a.inv = inv;
-  a.h = h; a.y = y; a.mark = mark; a.mark_ctx = mark_ctx;
+  a.h = h; a.y = y;
   a.T = int(p.T); a.H = p.H; a.I = p.I; a.E = p.E; a.S = p.S; a.G = p.G; a.Gk = p.Gk; a.k = p.k;
   const int ns = (p.H + 511) / 512, nsd = (p.I + 511) / 512;
 #define MOE_DQ(TA, TW, NSV, NSDV)                                            \

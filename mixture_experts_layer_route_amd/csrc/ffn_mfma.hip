@@ -607,10 +607,10 @@ int launch_gateup_mfma(const Plan& p, const void* x, const int32_t* row_token,
     a.sh0 = (const bf16_t*)w->sh_gate; a.sh1 = (const bf16_t*)w->sh_up;
     a.out16 = (bf16_t*)h; a.K = p.H; a.N = p.I; a.E = p.E;
     if (p.I % (v2::BN / 2) == 0 && p.H % 64 == 0)
-      hipLaunchKernelGGL(k_gemm_bf16_v2<true>, dim3(unsigned(p.max_tiles * (p.I / (v2::BN / 2)))),
-                         dim3(256), 0, st, a);
+      launch_kernel(p, kTimeGateUp, k_gemm_bf16_v2<true>,
+                    dim3(unsigned(p.max_tiles * (p.I / (v2::BN / 2)))), dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL(k_gemm_bf16<true>, dim3(grid), dim3(256), 0, st, a);
+      launch_kernel(p, kTimeGateUp, k_gemm_bf16<true>, dim3(grid), dim3(256), 0, st, a);
   } else {
     GemmFp8Args a{};
     a.a = xq; a.a_scale = sx; a.row_token = row_token; a.offsets = offsets; a.tiles = tiles;
@@ -618,7 +618,7 @@ int launch_gateup_mfma(const Plan& p, const void* x, const int32_t* row_token,
     a.sh0 = (const uint8_t*)w->sh_gate; a.sh1 = (const uint8_t*)w->sh_up;
     a.s0 = w->s_gate; a.s1 = w->s_up; a.shs0 = w->sh_s_gate; a.shs1 = w->sh_s_up;
     a.hout = (float*)h; a.K = p.H; a.N = p.I; a.E = p.E;
-    hipLaunchKernelGGL(k_gemm_fp8<true>, dim3(grid), dim3(256), 0, st, a);
+    launch_kernel(p, kTimeGateUp, k_gemm_fp8<true>, dim3(grid), dim3(256), 0, st, a);
   }
   return check_launch();
 }
@@ -633,17 +633,17 @@ int launch_down_mfma(const Plan& p, const void* h, const int32_t* offsets, const
     a.w0 = (const bf16_t*)w->w_down; a.sh0 = (const bf16_t*)w->sh_down;
     a.row_w = row_w; a.out16 = out16; a.out32 = out32; a.K = p.I; a.N = p.H; a.E = p.E;
     if (p.H % v2::BN == 0 && p.I % 64 == 0)
-      hipLaunchKernelGGL(k_gemm_bf16_v2<false>, dim3(unsigned(p.max_tiles * (p.H / v2::BN))),
-                         dim3(256), 0, st, a);
+      launch_kernel(p, kTimeDown, k_gemm_bf16_v2<false>,
+                    dim3(unsigned(p.max_tiles * (p.H / v2::BN))), dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL(k_gemm_bf16<false>, dim3(grid), dim3(256), 0, st, a);
+      launch_kernel(p, kTimeDown, k_gemm_bf16<false>, dim3(grid), dim3(256), 0, st, a);
   } else {
     GemmFp8Args a{};
     a.a = (const uint8_t*)h; a.a_scale = sh_scale; a.offsets = offsets; a.tiles = tiles;
     a.meta = meta; a.w0 = (const uint8_t*)w->w_down; a.sh0 = (const uint8_t*)w->sh_down;
     a.s0 = w->s_down; a.shs0 = w->sh_s_down; a.row_w = row_w; a.out16 = out16; a.out32 = out32;
     a.K = p.I; a.N = p.H; a.E = p.E;
-    hipLaunchKernelGGL(k_gemm_fp8<false>, dim3(grid), dim3(256), 0, st, a);
+    launch_kernel(p, kTimeDown, k_gemm_fp8<false>, dim3(grid), dim3(256), 0, st, a);
   }
   return check_launch();
 }

@@ -282,8 +282,8 @@ static void gateup(const Plan& p, const void* x, const int32_t* rt, const int32_
   constexpr int NI = 2, RC = 4;
   dim3 grid(unsigned(p.max_active), unsigned((p.I + 4 * NI - 1) / (4 * NI)));
   const size_t lds = size_t(RC) * std::min(p.H, kPass) * sizeof(TA);
-  hipLaunchKernelGGL((k_gateup_skinny<TA, TW, NI, RC>), grid, dim3(256), lds, st, (const TA*)x, rt,
-                     off, act, meta, (const TW*)w->w_gate, (const TW*)w->w_up,
+  launch_kernel(p, kTimeGateUp, k_gateup_skinny<TA, TW, NI, RC>, grid, dim3(256), lds, st,
+                (const TA*)x, rt, off, act, meta, (const TW*)w->w_gate, (const TW*)w->w_up,
                      (const TW*)w->sh_gate, (const TW*)w->sh_up, h, p.H, p.I, p.E);
 }
 
@@ -303,11 +303,11 @@ int launch_down_skinny(const Plan& p, const float* h, const int32_t* offsets,
   constexpr int NR = 2, RC = 4;
   dim3 grid(unsigned(p.max_active), unsigned((p.H + 4 * NR - 1) / (4 * NR)));
   if (p.wt == MOE_F32)
-    hipLaunchKernelGGL((k_down_skinny<float, NR, RC>), grid, dim3(256), 0, st, h, offsets, active,
+    launch_kernel(p, kTimeDown, k_down_skinny<float, NR, RC>, grid, dim3(256), 0, st, h, offsets, active,
                        meta, (const float*)w->w_down, (const float*)w->sh_down, y_perm, p.H, p.I,
                        p.E);
   else
-    hipLaunchKernelGGL((k_down_skinny<bf16_t, NR, RC>), grid, dim3(256), 0, st, h, offsets, active,
+    launch_kernel(p, kTimeDown, k_down_skinny<bf16_t, NR, RC>, grid, dim3(256), 0, st, h, offsets, active,
                        meta, (const bf16_t*)w->w_down, (const bf16_t*)w->sh_down, y_perm, p.H,
                        p.I, p.E);
   return check_launch();
@@ -320,11 +320,11 @@ int launch_down_combine_skinny(const Plan& p, const float* h, const int32_t* ids
   dim3 grid(unsigned((p.H + NR - 1) / NR), unsigned((p.T + 3) / 4));
   const int T = int(p.T);
   if (p.wt == MOE_F32)
-    hipLaunchKernelGGL((k_down_combine_skinny<float, float, NR>), grid, dim3(256), 0, st, h, ids,
+    launch_kernel(p, kTimeDown, k_down_combine_skinny<float, float, NR>, grid, dim3(256), 0, st, h, ids,
                        wts, inv, (const float*)w->w_down, (const float*)w->sh_down, (float*)y, T,
                        p.H, p.I, p.E, p.k, p.S);
   else
-    hipLaunchKernelGGL((k_down_combine_skinny<bf16_t, bf16_t, NR>), grid, dim3(256), 0, st, h,
+    launch_kernel(p, kTimeDown, k_down_combine_skinny<bf16_t, bf16_t, NR>, grid, dim3(256), 0, st, h,
                        ids, wts, inv, (const bf16_t*)w->w_down, (const bf16_t*)w->sh_down,
                        (bf16_t*)y, T, p.H, p.I, p.E, p.k, p.S);
   return check_launch();

@@ -201,15 +201,11 @@ static int forward_impl(const moe_config* cfg, const void* x, const moe_weights*
                         hipStream_t stream, hipEvent_t* ev) {
   Plan p;
   MOE_TRY(make_plan(cfg, &p));
+  if (ev)
+    for (int i = 0; i < MOE_TIMED_EVENTS; ++i) p.ev[i] = ev[i];
   if (!x || !y || !w || !w->w_router) return MOE_ERR_ARG;
   MOE_TRY(check_experts(p, w));
   MOE_TRY(check_ws(p, ws, ws_bytes));
-  auto mark = [&](int i) -> int {
-    if (!ev) return MOE_OK;
-    const hipError_t err = hipEventRecord(ev[i], stream);
-    if (err != hipSuccess) return record_hip_error(err);
-    return MOE_OK;
-  };
   int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, p.o_ids);
   float* wts = topk_w_out ? topk_w_out : at<float>(ws, p.o_w);
   float* logits = at<float>(ws, p.o_logits);
@@ -221,22 +217,12 @@ static int forward_impl(const moe_config* cfg, const void* x, const moe_weights*
   int32_t* inv = at<int32_t>(ws, p.o_inv);
   float* row_w = at<float>(ws, p.o_roww);
 
-  MOE_TRY(mark(0));
   int32_t* blk = at<int32_t>(ws, p.o_blk);
   if (p.fused_down && decode_ffn_ok(p)) {
     // decode: the logits, then gate/up (routing in every block) and down + combine
     MOE_TRY(launch_logits(p, x, w->w_router, w->router_bias, logits, stream));
-    MOE_TRY(mark(1));
-    struct Hook { hipEvent_t ev; hipStream_t st; } hook{ev ? ev[2] : nullptr, stream};
-    auto hook_fn = [](void* c) -> int {
-      const Hook* hk = static_cast<const Hook*>(c);
-      const hipError_t err = hipEventRecord(hk->ev, hk->st);
-      return err == hipSuccess ? MOE_OK : record_hip_error(err);
-    };
-    MOE_TRY(launch_decode_ffn(p, x, logits, w, ids, wts, off, rowtok, inv, at<float>(ws, p.o_h), y,
-                              ev ? +hook_fn : nullptr, &hook, stream));
-    MOE_TRY(mark(3));
-    return mark(4);
+    return launch_decode_ffn(p, x, logits, w, ids, wts, off, rowtok, inv, at<float>(ws, p.o_h), y,
+                             stream);
   }
   if (p.small_route) {
     MOE_TRY(launch_logits(p, x, w->w_router, w->router_bias, logits, stream));
@@ -253,27 +239,18 @@ static int forward_impl(const moe_config* cfg, const void* x, const moe_weights*
     MOE_TRY(launch_scan_scatter(p, ids, wts, blk, off, active, meta, tiles, rowtok, inv, row_w,
                                 kTileRows, stream));
   }
-  MOE_TRY(mark(1));
   if (p.skinny) {
     float* h = at<float>(ws, p.o_h);
     MOE_TRY(launch_gateup_skinny(p, x, rowtok, off, active, meta, w, h, stream));
-    MOE_TRY(mark(2));
-    if (p.fused_down) {
-      MOE_TRY(launch_down_combine_skinny(p, h, ids, wts, inv, w, y, stream));
-      MOE_TRY(mark(3));
-      return mark(4);
-    }
+    if (p.fused_down) return launch_down_combine_skinny(p, h, ids, wts, inv, w, y, stream);
     float* yp = at<float>(ws, p.o_yp32);
     MOE_TRY(launch_down_skinny(p, h, off, active, meta, w, yp, stream));
-    MOE_TRY(mark(3));
-    MOE_TRY(launch_combine(p, yp, off, inv, wts, y, stream));
-    return mark(4);
+    return launch_combine(p, yp, off, inv, wts, y, stream);
   }
   bf16_t* ypw = at<bf16_t>(ws, p.o_ypw);
   if (p.wt == MOE_BF16) {
     bf16_t* h = at<bf16_t>(ws, p.o_h);
     MOE_TRY(launch_gateup_mfma(p, x, rowtok, off, tiles, meta, w, h, nullptr, nullptr, stream));
-    MOE_TRY(mark(2));
     MOE_TRY(launch_down_mfma(p, h, off, tiles, meta, w, row_w, nullptr, ypw, nullptr, stream));
   } else {
     uint8_t* xq = at<uint8_t>(ws, p.o_xq);
@@ -283,13 +260,10 @@ static int forward_impl(const moe_config* cfg, const void* x, const moe_weights*
     float* h = at<float>(ws, p.o_h);
     MOE_TRY(launch_quant(p, x, true, p.T, p.H, xq, sx, stream));
     MOE_TRY(launch_gateup_mfma(p, x, rowtok, off, tiles, meta, w, h, xq, sx, stream));
-    MOE_TRY(mark(2));
     MOE_TRY(launch_quant(p, h, false, p.R, p.I, hq, shq, stream));
     MOE_TRY(launch_down_mfma(p, hq, off, tiles, meta, w, row_w, nullptr, ypw, shq, stream));
   }
-  MOE_TRY(mark(3));
-  MOE_TRY(launch_combine_preweighted(p, ypw, off, inv, y, stream));
-  return mark(4);
+  return launch_combine_preweighted(p, ypw, off, inv, y, stream);
 }
 
 int moe_forward(const moe_config* cfg, const void* x, const moe_weights* w, void* y,
@@ -300,11 +274,11 @@ int moe_forward(const moe_config* cfg, const void* x, const moe_weights* w, void
 
 int moe_forward_timed(const moe_config* cfg, const void* x, const moe_weights* w, void* y,
                       int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
-                      hipStream_t stream, hipEvent_t* stage_events) {
-  if (!stage_events) return MOE_ERR_ARG;
-  for (int i = 0; i < MOE_TIMED_STAGES; ++i)
-    if (!stage_events[i]) return MOE_ERR_ARG;
-  return forward_impl(cfg, x, w, y, topk_ids_out, topk_w_out, ws, ws_bytes, stream, stage_events);
+                      hipStream_t stream, hipEvent_t* kernel_events) {
+  if (!kernel_events) return MOE_ERR_ARG;
+  for (int i = 0; i < MOE_TIMED_EVENTS; ++i)
+    if (!kernel_events[i]) return MOE_ERR_ARG;
+  return forward_impl(cfg, x, w, y, topk_ids_out, topk_w_out, ws, ws_bytes, stream, kernel_events);
 }
 
 const char* moe_strerror(int status) {

@@ -1,6 +1,7 @@
 // Host-side plan and kernel launchers of the MoE library (internal).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -28,7 +29,24 @@ struct Plan {
   // workspace carve (byte offsets)
   size_t o_logits, o_ids, o_w, o_blk, o_off, o_meta, o_active, o_tiles, o_rowtok, o_inv, o_roww,
       o_h, o_ypw, o_yp32, o_xq, o_sx, o_hq, o_shq, total;
+  // optional timing events bound to kernel dispatches: [0],[1] start/stop of the
+  // gate/up expert kernel, [2],[3] of the down kernel (all null when not timed)
+  hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
 };
+
+enum TimedKernel { kUntimed = -1, kTimeGateUp = 0, kTimeDown = 1 };
+
+// Launch `kern`; when the plan carries events for `slot`, the start/stop events are
+// attached to this dispatch itself (no extra packets between kernels).
+template <typename... KA, typename... A>
+inline void launch_kernel(const Plan& p, int slot, void (*kern)(KA...), dim3 grid, dim3 block,
+                          size_t lds, hipStream_t st, A... args) {
+  if (slot >= 0 && p.ev[2 * slot])
+    hipExtLaunchKernelGGL(kern, grid, block, uint32_t(lds), st, p.ev[2 * slot],
+                          p.ev[2 * slot + 1], 0u, args...);
+  else
+    hipLaunchKernelGGL(kern, grid, block, lds, st, args...);
+}
 
 #define MOE_TRY(expr)              \
   do {                             \
@@ -60,12 +78,10 @@ int launch_route_permute_small(const Plan& p, const float* logits, int32_t* ids,
                                int32_t* row_token, int32_t* inv, float* row_w, int BM,
                                hipStream_t st);
 bool decode_ffn_ok(const Plan& p);
-// Decode path: gate/up (with in-kernel routing) then down + combine; `mark` (may be null)
-// is called between the two launches.
+// Decode path: gate/up (with in-kernel routing) then down + combine.
 int launch_decode_ffn(const Plan& p, const void* x, const float* logits, const moe_weights* w,
                       int32_t* ids, float* wts, int32_t* offsets, int32_t* row_token,
-                      int32_t* inv, float* h, void* y, int (*mark)(void*), void* mark_ctx,
-                      hipStream_t st);
+                      int32_t* inv, float* h, void* y, hipStream_t st);
 int launch_gateup_skinny(const Plan& p, const void* x, const int32_t* row_token,
                          const int32_t* offsets, const int32_t* active, const int32_t* meta,
                          const moe_weights* w, float* h, hipStream_t st);
