@@ -22,7 +22,6 @@ namespace moe {
 constexpr int TM = 128;   // rows per tile (the schedule's BM)
 constexpr int TN = 128;   // output columns (or weight rows) per tile
 
-__device__ __forceinline__ int swz16(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
 
 template <typename T>
 __device__ __forceinline__ const T* expert_mat(const T* routed, const T* shared, int e, int E,
@@ -51,13 +50,31 @@ struct GemmBf16Args {
   int K, N, E;                // K: reduction length; N: output width (I for h, H for y)
 };
 
+// Work item of a grouped-GEMM workgroup.  Workgroup b runs on XCD b % 8; the
+// n = ntiles * ncol real items (tile-major, column block fastest) are split into 8
+// contiguous runs, one per XCD, so that the workgroups sharing an expert's weight
+// slabs and a tile's activation rows share one L2.  The grid must hold at least
+// 8 * ceil(n / 8) workgroups; the surplus returns false.
+__device__ __forceinline__ bool xcd_item(int ntiles, int ncol, int& tile, int& ct) {
+  const int n = ntiles * ncol;
+  const int per = (n + 7) >> 3;
+  const int slot = int(blockIdx.x >> 3);
+  const int j = int(blockIdx.x & 7) * per + slot;
+  if (slot >= per || j >= n) return false;
+  tile = j / ncol;
+  ct = j - tile * ncol;
+  return true;
+}
+
+// grid for xcd_item: max_items rounded up to a multiple of the 8 XCDs
+static inline unsigned xcd_grid(int64_t max_items) { return unsigned((max_items + 7) / 8 * 8); }
+
 template <bool GATEUP>
 __global__ __launch_bounds__(256) void k_gemm_bf16(GemmBf16Args p) {
   constexpr int BK = 64;
   const int ncol = GATEUP ? p.N / 64 : p.N / TN;   // gate/up tile = 64 h columns
-  const int tile = blockIdx.x / ncol;
-  const int ct = blockIdx.x - tile * ncol;
-  if (tile >= p.meta[1]) return;
+  int tile, ct;
+  if (!xcd_item(p.meta[1], ncol, tile, ct)) return;
   const int2 te = p.tiles[tile];
   const int e = te.x, m0 = te.y;
   const int base = p.offsets[e];
@@ -223,12 +240,16 @@ constexpr int A_U4 = BM * 8, B_U4 = BN * 8;                         // uint4 per
 template <bool GATEUP>
 __global__ __launch_bounds__(256) void k_gemm_bf16_v2(GemmBf16Args p) {
   using namespace v2;
-  __shared__ uint4 sA0[A_U4], sA1[A_U4], sA2[A_U4];
-  __shared__ uint4 sB0[B_U4], sB1[B_U4], sB2[B_U4];
+  __shared__ uint4 smem[3 * (A_U4 + B_U4)];
+  uint4* const sA0 = smem;
+  uint4* const sA1 = smem + A_U4;
+  uint4* const sA2 = smem + 2 * A_U4;
+  uint4* const sB0 = smem + 3 * A_U4;
+  uint4* const sB1 = sB0 + B_U4;
+  uint4* const sB2 = sB0 + 2 * B_U4;
   const int ncol = GATEUP ? p.N / (BN / 2) : p.N / BN;
-  const int tile = blockIdx.x / ncol;
-  const int ct = blockIdx.x - tile * ncol;
-  if (tile >= p.meta[1]) return;
+  int tile, ct;
+  if (!xcd_item(p.meta[1], ncol, tile, ct)) return;
   const int2 te = p.tiles[tile];
   const int e = te.x, m0 = te.y;
   const int base = p.offsets[e];
@@ -237,14 +258,14 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_v2(GemmBf16Args p) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int wm = wv >> 1, wn = wv & 1;
   const int64_t K = p.K;
-  const int kcl = ((lane & 7) ^ (lane >> 3)) * 8;   // logical chunk this lane fetches (elements)
 
   const bf16_t* ag[AJ];
 #pragma unroll
   for (int i = 0; i < AJ; ++i) {
     const int r = 8 * (wv + W * i) + (lane >> 3);
     const int m = min(m0 + r, cnt - 1);
-    ag[i] = (GATEUP ? p.a + int64_t(p.row_token[base + m]) * K : p.a + int64_t(base + m) * K) + kcl;
+    ag[i] = (GATEUP ? p.a + int64_t(p.row_token[base + m]) * K : p.a + int64_t(base + m) * K) +
+            dma_chunk(lane, wv + W * i) * 8;
   }
   const bf16_t* bg[BJ];
   {
@@ -255,9 +276,11 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_v2(GemmBf16Args p) {
       if (GATEUP) {
         const int c0 = ct * (BN / 2);
         bg[i] = (r < BN / 2 ? expert_mat(p.w0, p.sh0, e, p.E, st) + int64_t(c0 + r) * K
-                            : expert_mat(p.w1, p.sh1, e, p.E, st) + int64_t(c0 + r - BN / 2) * K) + kcl;
+                            : expert_mat(p.w1, p.sh1, e, p.E, st) + int64_t(c0 + r - BN / 2) * K) +
+                dma_chunk(lane, wv + W * i) * 8;
       } else {
-        bg[i] = expert_mat(p.w0, p.sh0, e, p.E, st) + int64_t(ct * BN + r) * K + kcl;
+        bg[i] = expert_mat(p.w0, p.sh0, e, p.E, st) + int64_t(ct * BN + r) * K +
+                dma_chunk(lane, wv + W * i) * 8;
       }
     }
   }
@@ -292,12 +315,15 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_v2(GemmBf16Args p) {
       bfr[b] = __builtin_bit_cast(bf16x8, sb[swz16(row, chunk)]);
     }
   };
-  auto compute = [&](const uint4* sa, const uint4* sb) {
+  auto compute = [&](const uint4* sa, const uint4* sb, auto&& between) {
     bf16x8 af[2][MI], bfr[2][NI];
     load_frags(sa, sb, 0, af[0], bfr[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    between();   // the slab refill is issued while the first fragments are read
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       if (ks + 1 < 4) load_frags(sa, sb, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);   // keep the next fragments' reads ahead of these MFMAs
 #pragma unroll
       for (int a = 0; a < MI; ++a)
 #pragma unroll
@@ -313,9 +339,8 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_v2(GemmBf16Args p) {
 #define MOE_V2_STEP(KT, SA, SB, NA, NB)                    \
   {                                                        \
     if ((KT) + 1 < nk) wait_vm_lgkm0<L>(); else wait_vm_lgkm0<0>(); \
-    __builtin_amdgcn_s_barrier();                          \
-    if ((KT) + 2 < nk) issue((KT) + 2, NA, NB);            \
-    compute(SA, SB);                                       \
+    block_sync_nowait();                                   \
+    compute(SA, SB, [&] { if ((KT) + 2 < nk) issue((KT) + 2, NA, NB); }); \
   }
   for (int kt = 0; kt < nk; kt += 3) {
     MOE_V2_STEP(kt, sA0, sB0, sA2, sB2)
@@ -324,7 +349,44 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_v2(GemmBf16Args p) {
   }
 #undef MOE_V2_STEP
 
-  // epilogue (registers only)
+  // Epilogue.  bf16 outputs go through LDS (the ring is free: every slab has been
+  // read and no load is in flight) so that each row leaves as whole 16-byte
+  // pieces; the unweighted fp32 output is stored straight from the registers.
+  if (GATEUP || !p.out32) {
+    constexpr int OC = GATEUP ? BN / 2 : BN;   // output columns of the tile
+    constexpr int LS = OC + 8;                 // staging row stride (bf16), padded
+    bf16_t* st = reinterpret_cast<bf16_t*>(smem);
+    __syncthreads();
+#pragma unroll
+    for (int a = 0; a < MI; ++a) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 64 + a * 32 + acc_row(r, lane);
+        if (GATEUP) {
+#pragma unroll
+          for (int b = 0; b < NI / 2; ++b) {
+            const float g = acc[a][b][r], u = acc[a][b + NI / 2][r];
+            st[row * LS + wn * 64 + b * 32 + (lane & 31)] = f32_to_bf16(silu(g) * u);
+          }
+        } else {
+          const float wr = m0 + row < cnt ? p.row_w[base + m0 + row] : 0.f;
+#pragma unroll
+          for (int b = 0; b < NI; ++b)
+            st[row * LS + wn * 128 + b * 32 + (lane & 31)] = f32_to_bf16(acc[a][b][r] * wr);
+        }
+      }
+    }
+    __syncthreads();
+    constexpr int CPR = OC / 8;                // 16-byte pieces per row
+    const int rows = min(BM, cnt - m0);
+    const int col0 = ct * OC;
+    for (int i = tid; i < rows * CPR; i += 256) {
+      const int row = i / CPR, c = i - row * CPR;
+      const uint4 v = *reinterpret_cast<const uint4*>(st + row * LS + c * 8);
+      *reinterpret_cast<uint4*>(p.out16 + int64_t(base + m0 + row) * p.N + col0 + c * 8) = v;
+    }
+    return;
+  }
 #pragma unroll
   for (int a = 0; a < MI; ++a) {
 #pragma unroll
@@ -332,24 +394,9 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_v2(GemmBf16Args p) {
       const int row = wm * 64 + a * 32 + acc_row(r, lane);
       if (m0 + row >= cnt) continue;
       const int64_t grow = int64_t(base + m0 + row);
-      if (GATEUP) {
 #pragma unroll
-        for (int b = 0; b < NI / 2; ++b) {
-          const int col = ct * (BN / 2) + wn * 64 + b * 32 + (lane & 31);
-          const float g = acc[a][b][r], u = acc[a][b + NI / 2][r];
-          p.out16[grow * p.N + col] = f32_to_bf16(silu(g) * u);
-        }
-      } else {
-        const float wr = p.out32 ? 1.f : p.row_w[grow];
-#pragma unroll
-        for (int b = 0; b < NI; ++b) {
-          const int col = ct * BN + wn * 128 + b * 32 + (lane & 31);
-          if (p.out32)
-            p.out32[grow * p.N + col] = acc[a][b][r];
-          else
-            p.out16[grow * p.N + col] = f32_to_bf16(acc[a][b][r] * wr);
-        }
-      }
+      for (int b = 0; b < NI; ++b)
+        p.out32[grow * p.N + ct * BN + wn * 128 + b * 32 + (lane & 31)] = acc[a][b][r];
     }
   }
 }
@@ -387,9 +434,8 @@ template <bool GATEUP>
 __global__ __launch_bounds__(256) void k_gemm_fp8(GemmFp8Args p) {
   constexpr int BK = 128;
   const int ncol = GATEUP ? p.N / 64 : p.N / TN;
-  const int tile = blockIdx.x / ncol;
-  const int ct = blockIdx.x - tile * ncol;
-  if (tile >= p.meta[1]) return;
+  int tile, ct;
+  if (!xcd_item(p.meta[1], ncol, tile, ct)) return;
   const int2 te = p.tiles[tile];
   const int e = te.x, m0 = te.y;
   const int base = p.offsets[e];
@@ -599,7 +645,7 @@ int launch_gateup_mfma(const Plan& p, const void* x, const int32_t* row_token,
                        const int32_t* offsets, const int2* tiles, const int32_t* meta,
                        const moe_weights* w, void* h, const uint8_t* xq, const float* sx,
                        hipStream_t st) {
-  const unsigned grid = unsigned(p.max_tiles * (p.I / 64));
+  const unsigned grid = xcd_grid(p.max_tiles * (p.I / 64));
   if (p.wt == MOE_BF16) {
     GemmBf16Args a{};
     a.a = (const bf16_t*)x; a.row_token = row_token; a.offsets = offsets; a.tiles = tiles;
@@ -608,7 +654,7 @@ int launch_gateup_mfma(const Plan& p, const void* x, const int32_t* row_token,
     a.out16 = (bf16_t*)h; a.K = p.H; a.N = p.I; a.E = p.E;
     if (p.I % (v2::BN / 2) == 0 && p.H % 64 == 0)
       launch_kernel(p, kTimeGateUp, k_gemm_bf16_v2<true>,
-                    dim3(unsigned(p.max_tiles * (p.I / (v2::BN / 2)))), dim3(256), 0, st, a);
+                    dim3(xcd_grid(p.max_tiles * (p.I / (v2::BN / 2)))), dim3(256), 0, st, a);
     else
       launch_kernel(p, kTimeGateUp, k_gemm_bf16<true>, dim3(grid), dim3(256), 0, st, a);
   } else {
@@ -626,7 +672,7 @@ int launch_gateup_mfma(const Plan& p, const void* x, const int32_t* row_token,
 int launch_down_mfma(const Plan& p, const void* h, const int32_t* offsets, const int2* tiles,
                      const int32_t* meta, const moe_weights* w, const float* row_w, float* out32,
                      bf16_t* out16, const float* sh_scale, hipStream_t st) {
-  const unsigned grid = unsigned(p.max_tiles * (p.H / TN));
+  const unsigned grid = xcd_grid(p.max_tiles * (p.H / TN));
   if (p.wt == MOE_BF16) {
     GemmBf16Args a{};
     a.a = (const bf16_t*)h; a.offsets = offsets; a.tiles = tiles; a.meta = meta;
@@ -634,7 +680,7 @@ int launch_down_mfma(const Plan& p, const void* h, const int32_t* offsets, const
     a.row_w = row_w; a.out16 = out16; a.out32 = out32; a.K = p.I; a.N = p.H; a.E = p.E;
     if (p.H % v2::BN == 0 && p.I % 64 == 0)
       launch_kernel(p, kTimeDown, k_gemm_bf16_v2<false>,
-                    dim3(unsigned(p.max_tiles * (p.H / v2::BN))), dim3(256), 0, st, a);
+                    dim3(xcd_grid(p.max_tiles * (p.H / v2::BN))), dim3(256), 0, st, a);
     else
       launch_kernel(p, kTimeDown, k_gemm_bf16<false>, dim3(grid), dim3(256), 0, st, a);
   } else {

@@ -8,6 +8,32 @@
 
 namespace moe {
 
+// Workgroup barrier that also keeps the compiler from moving memory operations
+// across it (s_barrier alone is not a memory barrier to the compiler); it adds no
+// wait of its own, the explicit waitcnt before it decides what has landed.
+__device__ __forceinline__ void block_sync_nowait() {
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+#ifndef MOE_SWZ_SHIFT
+#define MOE_SWZ_SHIFT 1
+#endif
+// Matrix tiles in LDS are 128-byte rows of eight 16-byte chunks.  swz16 gives the
+// LDS position (in 16-byte units) of chunk `chunk` of row `row`: chunks are XOR-
+// swizzled by (row >> 1) & 7, so that 16 consecutive rows read at the same chunk
+// (what one ds_read_b128 serves together) land on 16 distinct 16-byte slots of the
+// 256-byte bank line.
+__device__ __forceinline__ int swz16(int row, int chunk) {
+  return row * 8 + (chunk ^ ((row >> MOE_SWZ_SHIFT) & 7));
+}
+// A wave's direct-to-LDS load of 64 x 16 bytes fills rows 8j .. 8j+7 in LDS order
+// (lane L writes position L % 8 of row 8j + L / 8): the logical chunk lane L must
+// fetch so that the tile ends up swizzled as swz16 reads it.
+__device__ __forceinline__ int dma_chunk(int lane, int j) {
+  return (lane & 7) ^ (((8 * j + (lane >> 3)) >> MOE_SWZ_SHIFT) & 7);
+}
+
 constexpr int kWave = 64;
 
 typedef uint16_t bf16_t;  // raw bfloat16 bits

@@ -160,14 +160,15 @@ __global__ __launch_bounds__(256) void k_router_mfma(
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t t0 = int64_t(blockIdx.x) * BT;
-  const int kcl = ((lane & 7) ^ (lane >> 3)) * 8;
   const bf16_t* xg[AJ];
 #pragma unroll
   for (int i = 0; i < AJ; ++i)
-    xg[i] = x + min<int64_t>(t0 + 8 * (wv + 4 * i) + (lane >> 3), T - 1) * H + kcl;
+    xg[i] = x + min<int64_t>(t0 + 8 * (wv + 4 * i) + (lane >> 3), T - 1) * H +
+            dma_chunk(lane, wv + 4 * i) * 8;
   const bf16_t* wg[BJ];
 #pragma unroll
-  for (int i = 0; i < BJ; ++i) wg[i] = wr + int64_t(8 * (wv + 4 * i) + (lane >> 3)) * H + kcl;
+  for (int i = 0; i < BJ; ++i)
+    wg[i] = wr + int64_t(8 * (wv + 4 * i) + (lane >> 3)) * H + dma_chunk(lane, wv + 4 * i) * 8;
   auto issue = [&](int kt, int stage) {
     uint4* st = ring + stage * STU4;
     const int ko = kt * 64;
@@ -184,7 +185,6 @@ __global__ __launch_bounds__(256) void k_router_mfma(
     for (int b = 0; b < NE; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
-  auto swz = [](int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); };
   auto compute = [&](int stage) {
     const uint4* xc = ring + stage * STU4;
     const uint4* wc = xc + XU4;
@@ -194,10 +194,10 @@ __global__ __launch_bounds__(256) void k_router_mfma(
       bf16x8 af[2], bfr[NE];
 #pragma unroll
       for (int a = 0; a < 2; ++a)
-        af[a] = __builtin_bit_cast(bf16x8, xc[swz(a * 32 + (lane & 31), chunk)]);
+        af[a] = __builtin_bit_cast(bf16x8, xc[swz16(a * 32 + (lane & 31), chunk)]);
 #pragma unroll
       for (int b = 0; b < NE; ++b)
-        bfr[b] = __builtin_bit_cast(bf16x8, wc[swz(wv * 32 * NE + b * 32 + (lane & 31), chunk)]);
+        bfr[b] = __builtin_bit_cast(bf16x8, wc[swz16(wv * 32 * NE + b * 32 + (lane & 31), chunk)]);
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -210,12 +210,12 @@ __global__ __launch_bounds__(256) void k_router_mfma(
   if (nk > 1) issue(1, 1);
   for (int kt = 0; kt < nk; ++kt) {
     if (kt + 1 < nk) wait_vm_lgkm0_r<L>(); else wait_vm_lgkm0_r<0>();
-    __builtin_amdgcn_s_barrier();
+    block_sync_nowait();
     if (kt + 2 < nk) issue(kt + 2, (kt + 2) % 3);
     compute(kt % 3);
   }
   wait_vm_lgkm0_r<0>();
-  __builtin_amdgcn_s_barrier();      // every wave is done with the ring before it is overlaid
+  block_sync_nowait();      // every wave is done with the ring before it is overlaid
 
   // logits tile -> LDS [token][expert] (stride E+1), bias added
 #pragma unroll
