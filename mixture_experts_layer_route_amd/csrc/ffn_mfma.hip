@@ -231,22 +231,63 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | ((N >> 4) << 14));
 }
 
-namespace v2 {
-constexpr int BM = 128, BN = 256, W = 4, MI = 2, NI = 4;
-constexpr int AJ = BM / (8 * W), BJ = BN / (8 * W), L = AJ + BJ;   // loads per lane per slab
-constexpr int A_U4 = BM * 8, B_U4 = BN * 8;                         // uint4 per slab
-}  // namespace v2
+// Tile configuration of the pipelined bf16 kernel: BM x BN outputs per workgroup
+// of W = WM x WN waves, each owning (BM / WM) x (BN / WN) outputs as MI x NI
+// blocks of 32 x 32; K moves in slabs of BK through a 3-stage LDS ring.  Tile rows
+// in LDS are BK * 2 bytes = CH chunks of 16 bytes, XOR-swizzled by
+// (row >> SH) & (CH - 1) so that the 16 rows one ds_read_b128 serves together at
+// one chunk fall on 16 distinct 16-byte slots of the 256-byte bank line.  One
+// wave-wide direct-to-LDS load writes 1 KB = RPD consecutive tile rows.
+template <int BM_, int BN_, int BK_, int WM_, int WN_>
+struct BfTile {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, W = WM * WN, NT = 64 * W;
+  // waves per SIMD the register budget is sized for: two workgroups per CU when
+  // a workgroup is 4 waves (its LDS ring is then kept under half the CU's LDS)
+  static constexpr int WPE = W == 4 ? 2 : 2;
+  static constexpr int MI = BM / WM / 32, NI = BN / WN / 32;
+  static constexpr int CH = BK / 8, SH = CH == 8 ? 1 : 2, RPD = 64 / CH;
+  static constexpr int AJ = BM / (RPD * W), BJ = BN / (RPD * W), L = AJ + BJ;  // loads per lane per slab
+  static constexpr int A_U4 = BM * CH, STAGE_U4 = (BM + BN) * CH;
+  static constexpr int RING_U4 = 3 * STAGE_U4;
+  static constexpr int LSG = BN / 2 + 8, LSD = BN + 8;   // epilogue staging row strides (bf16)
+  static constexpr int STG_U4 = BM * LSD * 2 / 16;
+  static constexpr int SMEM_U4 = RING_U4 > STG_U4 ? RING_U4 : STG_U4;
+  static_assert(BK == 32 || BK == 64, "slab depth");
+  static_assert(AJ * RPD * W == BM && BJ * RPD * W == BN, "load tiling");
+  static_assert(MI >= 1 && NI >= 2 && NI % 2 == 0, "wave tiling");
+  __device__ static __forceinline__ int pos(int row, int chunk) {
+    return row * CH + (chunk ^ ((row >> SH) & (CH - 1)));
+  }
+  // logical chunk lane `lane` fetches when its wave's load fills rows RPD*j ..
+  __device__ static __forceinline__ int dma_chunk(int lane, int j) {
+    return (lane % CH) ^ (((RPD * j + lane / CH) >> SH) & (CH - 1));
+  }
+};
 
-template <bool GATEUP>
-__global__ __launch_bounds__(256) void k_gemm_bf16_v2(GemmBf16Args p) {
-  using namespace v2;
-  __shared__ uint4 smem[3 * (A_U4 + B_U4)];
-  uint4* const sA0 = smem;
-  uint4* const sA1 = smem + A_U4;
-  uint4* const sA2 = smem + 2 * A_U4;
-  uint4* const sB0 = smem + 3 * A_U4;
-  uint4* const sB1 = sB0 + B_U4;
-  uint4* const sB2 = sB0 + 2 * B_U4;
+#ifndef MOE_BF_BM
+#define MOE_BF_BM 128
+#endif
+#ifndef MOE_BF_BN
+#define MOE_BF_BN 256
+#endif
+#ifndef MOE_BF_BK
+#define MOE_BF_BK 64
+#endif
+#ifndef MOE_BF_WM
+#define MOE_BF_WM 2
+#endif
+#ifndef MOE_BF_WN
+#define MOE_BF_WN 4
+#endif
+using BfCfg = BfTile<MOE_BF_BM, MOE_BF_BN, MOE_BF_BK, MOE_BF_WM, MOE_BF_WN>;
+
+template <bool GATEUP, class C>
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
+void k_gemm_bf16_v2(GemmBf16Args p) {
+  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, WM = C::WM, WN = C::WN, W = C::W;
+  constexpr int MI = C::MI, NI = C::NI, CH = C::CH, RPD = C::RPD, AJ = C::AJ, BJ = C::BJ;
+  constexpr int L = C::L, NT = C::NT;
+  __shared__ uint4 smem[C::SMEM_U4];
   const int ncol = GATEUP ? p.N / (BN / 2) : p.N / BN;
   int tile, ct;
   if (!xcd_item(p.meta[1], ncol, tile, ct)) return;
@@ -256,37 +297,40 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_v2(GemmBf16Args p) {
   const int cnt = p.offsets[e + 1] - base;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int wm = wv >> 1, wn = wv & 1;
+  const int wm = wv / WN, wn = wv % WN;
   const int64_t K = p.K;
 
   const bf16_t* ag[AJ];
 #pragma unroll
   for (int i = 0; i < AJ; ++i) {
-    const int r = 8 * (wv + W * i) + (lane >> 3);
+    const int r = RPD * (wv + W * i) + lane / CH;
     const int m = min(m0 + r, cnt - 1);
     ag[i] = (GATEUP ? p.a + int64_t(p.row_token[base + m]) * K : p.a + int64_t(base + m) * K) +
-            dma_chunk(lane, wv + W * i) * 8;
+            C::dma_chunk(lane, wv + W * i) * 8;
   }
   const bf16_t* bg[BJ];
   {
     const int64_t st = int64_t(p.N) * K;
 #pragma unroll
     for (int i = 0; i < BJ; ++i) {
-      const int r = 8 * (wv + W * i) + (lane >> 3);
+      const int r = RPD * (wv + W * i) + lane / CH;
       if (GATEUP) {
         const int c0 = ct * (BN / 2);
         bg[i] = (r < BN / 2 ? expert_mat(p.w0, p.sh0, e, p.E, st) + int64_t(c0 + r) * K
                             : expert_mat(p.w1, p.sh1, e, p.E, st) + int64_t(c0 + r - BN / 2) * K) +
-                dma_chunk(lane, wv + W * i) * 8;
+                C::dma_chunk(lane, wv + W * i) * 8;
       } else {
         bg[i] = expert_mat(p.w0, p.sh0, e, p.E, st) + int64_t(ct * BN + r) * K +
-                dma_chunk(lane, wv + W * i) * 8;
+                C::dma_chunk(lane, wv + W * i) * 8;
       }
     }
   }
 
-  auto issue = [&](int kt, uint4* sa, uint4* sb) {
-    const int64_t ko = int64_t(kt) * 64;
+  // slab kt into ring slot `slot`: A rows then B rows
+  auto issue = [&](int kt, int slot) {
+    const int64_t ko = int64_t(kt) * BK;
+    uint4* sa = smem + slot * C::STAGE_U4;
+    uint4* sb = sa + C::A_U4;
 #pragma unroll
     for (int i = 0; i < AJ; ++i) dma16(ag[i] + ko, sa + (wv + W * i) * 64);
 #pragma unroll
@@ -300,30 +344,45 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_v2(GemmBf16Args p) {
     for (int b = 0; b < NI; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+  // down, weighted output: this lane's row weights, loaded while the K loop runs
+  float roww[GATEUP ? 1 : MI][GATEUP ? 1 : 16];
+  if (!GATEUP) {
+#pragma unroll
+    for (int a = 0; a < (GATEUP ? 1 : MI); ++a)
+#pragma unroll
+      for (int r = 0; r < (GATEUP ? 1 : 16); ++r) {
+        const int row = wm * (BM / WM) + a * 32 + acc_row(r, lane);
+        roww[a][r] = (p.out32 || m0 + row >= cnt) ? 0.f : p.row_w[base + m0 + row];
+      }
+  }
 
-  // fragments of k-step ks+1 are read while the MFMAs of k-step ks run
   auto load_frags = [&](const uint4* sa, const uint4* sb, int ks, bf16x8 (&af)[MI], bf16x8 (&bfr)[NI]) {
     const int chunk = ks * 2 + (lane >> 5);
 #pragma unroll
     for (int a = 0; a < MI; ++a)
-      af[a] = __builtin_bit_cast(bf16x8, sa[swz16(wm * 64 + a * 32 + (lane & 31), chunk)]);
+      af[a] = __builtin_bit_cast(bf16x8, sa[C::pos(wm * (BM / WM) + a * 32 + (lane & 31), chunk)]);
 #pragma unroll
     for (int b = 0; b < NI; ++b) {
       // gate/up: blocks 0..NI/2-1 are gate columns, NI/2.. the matching up columns
-      const int row = GATEUP ? ((b < NI / 2 ? 0 : BN / 2) + wn * 64 + (b % (NI / 2)) * 32 + (lane & 31))
-                             : (wn * 128 + b * 32 + (lane & 31));
-      bfr[b] = __builtin_bit_cast(bf16x8, sb[swz16(row, chunk)]);
+      const int row = GATEUP ? ((b < NI / 2 ? 0 : BN / 2) + wn * (BN / 2 / WN) + (b % (NI / 2)) * 32 + (lane & 31))
+                             : (wn * (BN / WN) + b * 32 + (lane & 31));
+      bfr[b] = __builtin_bit_cast(bf16x8, sb[C::pos(row, chunk)]);
     }
   };
-  auto compute = [&](const uint4* sa, const uint4* sb, auto&& between) {
+  // multiply the slab in `slot`; fragments of sub-step ks+1 are read while the
+  // MFMAs of ks run; `between` (the refill) is issued after the first reads
+  auto compute = [&](int slot, auto&& between) {
+    const uint4* sa = smem + slot * C::STAGE_U4;
+    const uint4* sb = sa + C::A_U4;
+    constexpr int KS = BK / 16;
     bf16x8 af[2][MI], bfr[2][NI];
     load_frags(sa, sb, 0, af[0], bfr[0]);
     __builtin_amdgcn_sched_barrier(0);
-    between();   // the slab refill is issued while the first fragments are read
+    between();
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (ks + 1 < 4) load_frags(sa, sb, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);   // keep the next fragments' reads ahead of these MFMAs
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) load_frags(sa, sb, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int a = 0; a < MI; ++a)
 #pragma unroll
@@ -332,47 +391,47 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_v2(GemmBf16Args p) {
     }
   };
 
-  const int nk = int(K / 64);
-  issue(0, sA0, sB0);
-  if (nk > 1) issue(1, sA1, sB1);
-  // one step: wait for slab kt, barrier, refill the slot freed by slab kt-1 with kt+2, multiply kt
-#define MOE_V2_STEP(KT, SA, SB, NA, NB)                    \
-  {                                                        \
-    if ((KT) + 1 < nk) wait_vm_lgkm0<L>(); else wait_vm_lgkm0<0>(); \
-    block_sync_nowait();                                   \
-    compute(SA, SB, [&] { if ((KT) + 2 < nk) issue((KT) + 2, NA, NB); }); \
+  const int nk = int(K / BK);
+  issue(0, 0);
+  if (nk > 1) issue(1, 1);
+  // step kt: wait for slab kt, barrier, refill the slot slab kt-1 used with kt+2, multiply kt
+#define MOE_BF_STEP(KT, SLOT, NSLOT)                                      \
+  {                                                                       \
+    if ((KT) + 1 < nk) wait_vm_lgkm0<L>(); else wait_vm_lgkm0<0>();       \
+    block_sync_nowait();                                                  \
+    compute(SLOT, [&] { if ((KT) + 2 < nk) issue((KT) + 2, NSLOT); });    \
   }
   for (int kt = 0; kt < nk; kt += 3) {
-    MOE_V2_STEP(kt, sA0, sB0, sA2, sB2)
-    if (kt + 1 < nk) MOE_V2_STEP(kt + 1, sA1, sB1, sA0, sB0)
-    if (kt + 2 < nk) MOE_V2_STEP(kt + 2, sA2, sB2, sA1, sB1)
+    MOE_BF_STEP(kt, 0, 2)
+    if (kt + 1 < nk) MOE_BF_STEP(kt + 1, 1, 0)
+    if (kt + 2 < nk) MOE_BF_STEP(kt + 2, 2, 1)
   }
-#undef MOE_V2_STEP
+#undef MOE_BF_STEP
 
   // Epilogue.  bf16 outputs go through LDS (the ring is free: every slab has been
   // read and no load is in flight) so that each row leaves as whole 16-byte
   // pieces; the unweighted fp32 output is stored straight from the registers.
   if (GATEUP || !p.out32) {
     constexpr int OC = GATEUP ? BN / 2 : BN;   // output columns of the tile
-    constexpr int LS = OC + 8;                 // staging row stride (bf16), padded
-    bf16_t* st = reinterpret_cast<bf16_t*>(smem);
+    constexpr int LS = GATEUP ? C::LSG : C::LSD;
+    bf16_t* stg = reinterpret_cast<bf16_t*>(smem);
     __syncthreads();
 #pragma unroll
     for (int a = 0; a < MI; ++a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = wm * 64 + a * 32 + acc_row(r, lane);
+        const int row = wm * (BM / WM) + a * 32 + acc_row(r, lane);
         if (GATEUP) {
 #pragma unroll
           for (int b = 0; b < NI / 2; ++b) {
             const float g = acc[a][b][r], u = acc[a][b + NI / 2][r];
-            st[row * LS + wn * 64 + b * 32 + (lane & 31)] = f32_to_bf16(silu(g) * u);
+            stg[row * LS + wn * (BN / 2 / WN) + b * 32 + (lane & 31)] = f32_to_bf16(silu(g) * u);
           }
         } else {
-          const float wr = m0 + row < cnt ? p.row_w[base + m0 + row] : 0.f;
+          const float wr = roww[GATEUP ? 0 : a][GATEUP ? 0 : r];
 #pragma unroll
           for (int b = 0; b < NI; ++b)
-            st[row * LS + wn * 128 + b * 32 + (lane & 31)] = f32_to_bf16(acc[a][b][r] * wr);
+            stg[row * LS + wn * (BN / WN) + b * 32 + (lane & 31)] = f32_to_bf16(acc[a][b][r] * wr);
         }
       }
     }
@@ -380,9 +439,9 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_v2(GemmBf16Args p) {
     constexpr int CPR = OC / 8;                // 16-byte pieces per row
     const int rows = min(BM, cnt - m0);
     const int col0 = ct * OC;
-    for (int i = tid; i < rows * CPR; i += 256) {
+    for (int i = tid; i < rows * CPR; i += NT) {
       const int row = i / CPR, c = i - row * CPR;
-      const uint4 v = *reinterpret_cast<const uint4*>(st + row * LS + c * 8);
+      const uint4 v = *reinterpret_cast<const uint4*>(stg + row * LS + c * 8);
       *reinterpret_cast<uint4*>(p.out16 + int64_t(base + m0 + row) * p.N + col0 + c * 8) = v;
     }
     return;
@@ -391,15 +450,23 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_v2(GemmBf16Args p) {
   for (int a = 0; a < MI; ++a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row = wm * 64 + a * 32 + acc_row(r, lane);
+      const int row = wm * (BM / WM) + a * 32 + acc_row(r, lane);
       if (m0 + row >= cnt) continue;
       const int64_t grow = int64_t(base + m0 + row);
 #pragma unroll
       for (int b = 0; b < NI; ++b)
-        p.out32[grow * p.N + ct * BN + wn * 128 + b * 32 + (lane & 31)] = acc[a][b][r];
+        p.out32[grow * p.N + ct * BN + wn * (BN / WN) + b * 32 + (lane & 31)] = acc[a][b][r];
     }
   }
 }
+
+// shapes the pipelined bf16 kernel covers (else the register-staged one runs)
+static bool bf_pipelined_ok(const Plan& p) {
+  return p.wt == MOE_BF16 && p.I % (BfCfg::BN / 2) == 0 && p.H % BfCfg::BN == 0 &&
+         p.H % BfCfg::BK == 0 && p.I % BfCfg::BK == 0;
+}
+
+int gemm_tile_rows(const Plan& p) { return bf_pipelined_ok(p) ? BfCfg::BM : TM; }
 
 // ===========================================================================
 // Block FP8.  Weights e4m3 with one fp32 scale per 128x128 block; activations
@@ -652,9 +719,9 @@ int launch_gateup_mfma(const Plan& p, const void* x, const int32_t* row_token,
     a.meta = meta; a.w0 = (const bf16_t*)w->w_gate; a.w1 = (const bf16_t*)w->w_up;
     a.sh0 = (const bf16_t*)w->sh_gate; a.sh1 = (const bf16_t*)w->sh_up;
     a.out16 = (bf16_t*)h; a.K = p.H; a.N = p.I; a.E = p.E;
-    if (p.I % (v2::BN / 2) == 0 && p.H % 64 == 0)
-      launch_kernel(p, kTimeGateUp, k_gemm_bf16_v2<true>,
-                    dim3(xcd_grid(p.max_tiles * (p.I / (v2::BN / 2)))), dim3(256), 0, st, a);
+    if (bf_pipelined_ok(p))
+      launch_kernel(p, kTimeGateUp, k_gemm_bf16_v2<true, BfCfg>,
+                    dim3(xcd_grid(p.max_tiles * (p.I / (BfCfg::BN / 2)))), dim3(BfCfg::NT), 0, st, a);
     else
       launch_kernel(p, kTimeGateUp, k_gemm_bf16<true>, dim3(grid), dim3(256), 0, st, a);
   } else {
@@ -678,9 +745,9 @@ int launch_down_mfma(const Plan& p, const void* h, const int32_t* offsets, const
     a.a = (const bf16_t*)h; a.offsets = offsets; a.tiles = tiles; a.meta = meta;
     a.w0 = (const bf16_t*)w->w_down; a.sh0 = (const bf16_t*)w->sh_down;
     a.row_w = row_w; a.out16 = out16; a.out32 = out32; a.K = p.I; a.N = p.H; a.E = p.E;
-    if (p.H % v2::BN == 0 && p.I % 64 == 0)
-      launch_kernel(p, kTimeDown, k_gemm_bf16_v2<false>,
-                    dim3(xcd_grid(p.max_tiles * (p.H / v2::BN))), dim3(256), 0, st, a);
+    if (bf_pipelined_ok(p))
+      launch_kernel(p, kTimeDown, k_gemm_bf16_v2<false, BfCfg>,
+                    dim3(xcd_grid(p.max_tiles * (p.H / BfCfg::BN))), dim3(BfCfg::NT), 0, st, a);
     else
       launch_kernel(p, kTimeDown, k_gemm_bf16<false>, dim3(grid), dim3(256), 0, st, a);
   } else {

@@ -56,8 +56,8 @@ int make_plan(const moe_config* c, Plan* p) {
   q.small_route = T <= 64 && T * k <= 256;
   q.fused_down = q.skinny && T <= 16;
   q.max_active = std::min<int64_t>(E, q.Rk) + S;
-  q.max_tiles = q.Rk / kTileRows + std::min<int64_t>(E, q.Rk) +
-                int64_t(S) * ((T + kTileRows - 1) / kTileRows);
+  q.bm = gemm_tile_rows(q);
+  q.max_tiles = q.Rk / q.bm + std::min<int64_t>(E, q.Rk) + int64_t(S) * ((T + q.bm - 1) / q.bm);
 
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o = align256(o + bytes); return at; };
@@ -172,7 +172,7 @@ int moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t* expert_
   MOE_TRY(check_ws(p, ws, ws_bytes));
   return launch_permute(p, topk_ids, nullptr, at<int32_t>(ws, p.o_blk), expert_offsets,
                         at<int32_t>(ws, p.o_active), at<int32_t>(ws, p.o_meta),
-                        at<int2>(ws, p.o_tiles), row_token, inv_rows, nullptr, kTileRows, stream);
+                        at<int2>(ws, p.o_tiles), row_token, inv_rows, nullptr, p.bm, stream);
 }
 
 int moe_expert_ffn(const moe_config* cfg, const void* x, const int32_t* expert_offsets,
@@ -184,7 +184,7 @@ int moe_expert_ffn(const moe_config* cfg, const void* x, const int32_t* expert_o
   MOE_TRY(check_experts(p, w));
   MOE_TRY(check_ws(p, ws, ws_bytes));
   MOE_TRY(launch_schedule(p, expert_offsets, at<int32_t>(ws, p.o_active),
-                          at<int32_t>(ws, p.o_meta), at<int2>(ws, p.o_tiles), kTileRows, stream));
+                          at<int32_t>(ws, p.o_meta), at<int2>(ws, p.o_tiles), p.bm, stream));
   return run_experts(p, x, expert_offsets, row_token, w, ws, y_perm, nullptr, nullptr, stream);
 }
 
@@ -227,7 +227,7 @@ static int forward_impl(const moe_config* cfg, const void* x, const moe_weights*
   if (p.small_route) {
     MOE_TRY(launch_logits(p, x, w->w_router, w->router_bias, logits, stream));
     MOE_TRY(launch_route_permute_small(p, logits, ids, wts, off, active, meta, tiles, rowtok, inv,
-                                       row_w, kTileRows, stream));
+                                       row_w, p.bm, stream));
   } else {
     if (router_mfma_ok(p)) {
       MOE_TRY(launch_router_mfma(p, x, w->w_router, w->router_bias, nullptr, ids, wts, blk,
@@ -237,7 +237,7 @@ static int forward_impl(const moe_config* cfg, const void* x, const moe_weights*
       MOE_TRY(launch_select(p, logits, ids, wts, blk, stream));
     }
     MOE_TRY(launch_scan_scatter(p, ids, wts, blk, off, active, meta, tiles, rowtok, inv, row_w,
-                                kTileRows, stream));
+                                p.bm, stream));
   }
   if (p.skinny) {
     float* h = at<float>(ws, p.o_h);

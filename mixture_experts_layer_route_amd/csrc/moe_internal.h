@@ -11,7 +11,6 @@
 
 namespace moe {
 
-constexpr int kTileRows = 128;   // M rows per tile of the matrix-core expert kernels
 
 // Everything a call needs to know about a config, computed on the host from
 // host-known sizes only (never from routing results).
@@ -25,6 +24,7 @@ struct Plan {
   bool small_route;     // selection + permutation in one block
   bool fused_down;      // forward: down projection fused with the combine
   int64_t max_active;   // upper bound on experts with rows
+  int bm;               // M rows per tile of the matrix-core expert kernels
   int64_t max_tiles;    // upper bound on M tiles
   // workspace carve (byte offsets)
   size_t o_logits, o_ids, o_w, o_blk, o_off, o_meta, o_active, o_tiles, o_rowtok, o_inv, o_roww,
@@ -78,6 +78,8 @@ int launch_route_permute_small(const Plan& p, const float* logits, int32_t* ids,
                                int32_t* row_token, int32_t* inv, float* row_w, int BM,
                                hipStream_t st);
 bool decode_ffn_ok(const Plan& p);
+// M rows per tile the matrix-core expert kernels use for this plan
+int gemm_tile_rows(const Plan& p);
 // Decode path: gate/up (with in-kernel routing) then down + combine.
 int launch_decode_ffn(const Plan& p, const void* x, const float* logits, const moe_weights* w,
                       int32_t* ids, float* wts, int32_t* offsets, int32_t* row_token,
