@@ -155,9 +155,6 @@ int moe_route(const moe_config* cfg, const void* x, const void* w_router, const 
   MOE_TRY(make_plan(cfg, &p));
   if (!x || !w_router || !topk_ids || !topk_w) return MOE_ERR_ARG;
   MOE_TRY(check_ws(p, ws, ws_bytes));
-  if (router_mfma_ok(p))
-    return launch_router_mfma(p, x, w_router, router_bias, logits, topk_ids, topk_w,
-                              at<int32_t>(ws, p.o_blk), stream);
   float* lg = logits ? logits : at<float>(ws, p.o_logits);
   MOE_TRY(launch_logits(p, x, w_router, router_bias, lg, stream));
   return launch_select(p, lg, topk_ids, topk_w, nullptr, stream);
@@ -229,13 +226,8 @@ static int forward_impl(const moe_config* cfg, const void* x, const moe_weights*
     MOE_TRY(launch_route_permute_small(p, logits, ids, wts, off, active, meta, tiles, rowtok, inv,
                                        row_w, p.bm, stream));
   } else {
-    if (router_mfma_ok(p)) {
-      MOE_TRY(launch_router_mfma(p, x, w->w_router, w->router_bias, nullptr, ids, wts, blk,
-                                 stream));
-    } else {
-      MOE_TRY(launch_logits(p, x, w->w_router, w->router_bias, logits, stream));
-      MOE_TRY(launch_select(p, logits, ids, wts, blk, stream));
-    }
+    MOE_TRY(launch_logits(p, x, w->w_router, w->router_bias, logits, stream));
+    MOE_TRY(launch_select(p, logits, ids, wts, blk, stream));
     MOE_TRY(launch_scan_scatter(p, ids, wts, blk, off, active, meta, tiles, rowtok, inv, row_w,
                                 p.bm, stream));
   }

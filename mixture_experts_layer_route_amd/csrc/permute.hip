@@ -74,8 +74,12 @@ __global__ __launch_bounds__(256) void k_perm_count(const int32_t* __restrict__ 
   for (int i = threadIdx.x; i < 4 * E; i += 256) cnt_lds[i] = 0;
   __syncthreads();
   const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (t < T)
-    for (int j = 0; j < k; ++j) atomicAdd(&cnt_lds[wv * E + ids[t * k + j]], 1);
+  int id[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) id[j] = (t < T && j < k) ? ids[t * k + j] : 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    if (t < T && j < k) atomicAdd(&cnt_lds[wv * E + id[j]], 1);
   __syncthreads();
   for (int i = threadIdx.x; i < 4 * E; i += 256) {
     const int64_t b = int64_t(blockIdx.x) * 4 + i / E;
@@ -84,8 +88,11 @@ __global__ __launch_bounds__(256) void k_perm_count(const int32_t* __restrict__ 
 }
 
 // Totals, offsets, per-block bases (in place over the histogram) and schedule.
-// One block of 1024 threads.  The [nblk][E] histogram is walked in chunks of
-// CB blocks staged through LDS with coalesced loads; thread e owns expert e.
+// One block of 1024 threads.  The [nblk][E] histogram is staged through LDS in
+// chunks with coalesced loads; each expert gets P = 1024 / E' threads (E' = E
+// rounded up to a power of two, P <= 64) that own contiguous runs of blocks, so
+// the per-expert sums and running bases are short per thread and combine by
+// segmented shuffles over the P lanes of the expert.
 __global__ __launch_bounds__(1024) void k_perm_scan(int32_t* __restrict__ blk, int nblk, int64_t T,
                                                     int E, int S, int BM,
                                                     int32_t* __restrict__ offsets,
@@ -95,37 +102,91 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int32_t* __restrict__ blk, i
   constexpr int CHUNK = 16384;                     // ints staged per pass (64 KB)
   __shared__ int tmp[32];
   __shared__ int offs[1025];
+  __shared__ int tot[1024];
   __shared__ int stage[CHUNK];
-  const int e = threadIdx.x;
+  int Ep = 1;
+  while (Ep < E) Ep <<= 1;
+  const int P = min(64, max(1, 1024 / Ep));       // threads per expert
+  const int tid = threadIdx.x;
+  const int ge = tid / P, gj = tid % P;            // expert and part of this thread
+  const bool mine = ge < E;
   const int CB = max(1, CHUNK / E);                // blocks per pass
-  int cnt = 0;
+  auto part_range = [&](int nb, int& lo, int& hi) {
+    const int per = (nb + P - 1) / P;
+    lo = min(nb, gj * per);
+    hi = min(nb, lo + per);
+  };
+  auto seg_sum = [&](int v) {                      // sum over the P lanes of the expert
+    for (int o = 1; o < P; o <<= 1) v += __shfl_xor(v, o, 64);
+    return v;
+  };
+  // global -> LDS, every load of a thread issued before the first store
+  auto load_chunk = [&](int b0, int nb) {
+    constexpr int PER = CHUNK / 1024;
+    const int n = nb * E;
+    int v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = tid + u * 1024;
+      v[u] = i < n ? blk[int64_t(b0) * E + i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = tid + u * 1024;
+      if (i < n) stage[i] = v[u];
+    }
+  };
+  const bool one_chunk = nblk <= CB;               // then the staged copy is kept for pass 2
+  int part = 0;
   for (int b0 = 0; b0 < nblk; b0 += CB) {
     const int nb = min(CB, nblk - b0);
     __syncthreads();
-    for (int i = threadIdx.x; i < nb * E; i += 1024) stage[i] = blk[int64_t(b0) * E + i];
+    load_chunk(b0, nb);
     __syncthreads();
-    if (e < E)
-      for (int b = 0; b < nb; ++b) cnt += stage[b * E + e];
+    if (mine) {
+      int lo, hi;
+      part_range(nb, lo, hi);
+      for (int b = lo; b < hi; ++b) part += stage[b * E + ge];
+    }
   }
+  const int sum = seg_sum(part);
+  if (mine && gj == 0) tot[ge] = sum;
+  __syncthreads();
+  const int e = tid;
+  int cnt = e < E ? tot[e] : 0;
   if (e >= E && e < E + S) cnt = int(T);
   build_schedule(cnt, E + S, BM, offs, active, meta, tiles, tmp);
   __syncthreads();
   if (e <= E + S) offsets[e] = offs[e];
-  int run = e < E ? offs[e] : 0;
+  int run = mine ? offs[ge] : 0;
   for (int b0 = 0; b0 < nblk; b0 += CB) {
     const int nb = min(CB, nblk - b0);
     __syncthreads();
-    for (int i = threadIdx.x; i < nb * E; i += 1024) stage[i] = blk[int64_t(b0) * E + i];
+    if (!one_chunk) load_chunk(b0, nb);
     __syncthreads();
-    if (e < E) {
-      for (int b = 0; b < nb; ++b) {
-        const int c = stage[b * E + e];
-        stage[b * E + e] = run;
-        run += c;
+    int lo = 0, hi = 0, s = 0;
+    if (mine) {
+      part_range(nb, lo, hi);
+      for (int b = lo; b < hi; ++b) s += stage[b * E + ge];
+    }
+    // exclusive prefix of the parts over the expert's lanes
+    int incl = s;
+    for (int o = 1; o < P; o <<= 1) {
+      const int y = __shfl_up(incl, o, P);
+      if (gj >= o) incl += y;
+    }
+    const int chunk_total = seg_sum(s);
+    if (mine) {
+      int r = run + incl - s;
+      for (int b = lo; b < hi; ++b) {
+        const int c = stage[b * E + ge];
+        stage[b * E + ge] = r;
+        r += c;
       }
     }
+    run += chunk_total;
     __syncthreads();
-    for (int i = threadIdx.x; i < nb * E; i += 1024) blk[int64_t(b0) * E + i] = stage[i];
+    for (int i = tid; i < nb * E; i += 1024) blk[int64_t(b0) * E + i] = stage[i];
   }
 }
 
@@ -143,18 +204,32 @@ __global__ __launch_bounds__(256) void k_perm_scatter(
   __syncthreads();
   const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
   const bool valid = t < T;
-  if (valid)
-    for (int j = 0; j < k; ++j) atomicOr(&bits[wv * E + ids[t * k + j]], 1ull << lane);
+  // the token's k <= 16 ids and weights, all loads issued before any is used
+  int id[16];
+  float wt[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    id[j] = (valid && j < k) ? ids[t * k + j] : 0;
+    wt[j] = (valid && j < k && row_w) ? w[t * k + j] : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    if (valid && j < k) atomicOr(&bits[wv * E + id[j]], 1ull << lane);
   __syncthreads();
   if (!valid) return;
   const unsigned long long lower = (1ull << lane) - 1ull;
   const int32_t* base = blk_base + (int64_t(blockIdx.x) * 4 + wv) * E;
-  for (int j = 0; j < k; ++j) {
-    const int e = ids[t * k + j];
-    const int r = base[e] + __popcll(bits[wv * E + e] & lower);
+  int bs[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) bs[j] = j < k ? base[id[j]] : 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (j >= k) break;
+    const int e = id[j];
+    const int r = bs[j] + __popcll(bits[wv * E + e] & lower);
     row_token[r] = int32_t(t);
     inv[t * k + j] = r;
-    if (row_w) row_w[r] = w[t * k + j];
+    if (row_w) row_w[r] = wt[j];
   }
   for (int s = 0; s < S; ++s) {
     const int64_t r = T * k + int64_t(s) * T + t;

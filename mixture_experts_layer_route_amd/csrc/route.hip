@@ -10,8 +10,8 @@
 //
 // Two logits kernels: a vector-FMA one for few tokens or fp32 layers (activation
 // rows staged in LDS, every weight load of a wave issued before any is used), and
-// a matrix-core one for bf16 batches that also selects the experts of its 64
-// tokens (one thread each) and counts them per 64-token block for the
+// a matrix-core one for bf16 batches; then one selection kernel (a wave per
+// token) that also counts the chosen experts per 64-token block for the
 // permutation.
 #include <algorithm>
 
@@ -86,47 +86,11 @@ __global__ __launch_bounds__(256) void k_router_logits_fma(
 }
 
 // ---------------------------------------------------------------------------
-// Thread-per-token selection over global logits, 256 tokens per block, plus the
-// per-64-token-block expert counts used by the permutation (when blk != null).
-// grid = ceil(T/256), block = 256, dynamic LDS = (4*E + 256*G) * 4 bytes.
-template <int K>
-__global__ __launch_bounds__(256) void k_router_select(
-    const float* __restrict__ logits, int64_t T, int E, int G, int Gk, int32_t* __restrict__ ids,
-    float* __restrict__ w, int32_t* __restrict__ blk) {
-  extern __shared__ int sel_lds[];
-  int* cnt = sel_lds;                                        // [4][E]
-  float* gs = reinterpret_cast<float*>(sel_lds + 4 * E);     // [G][256]
-  const int wv = threadIdx.x >> 6;
-  for (int i = threadIdx.x; i < 4 * E; i += 256) cnt[i] = 0;
-  __syncthreads();
-  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (t < T) {
-    int32_t id[K];
-    float wt[K];
-    select_token_thread<K>(logits + t * E, 1, E, G, Gk, gs + threadIdx.x, 256, id, wt);
-#pragma unroll
-    for (int j = 0; j < K; ++j) {
-      ids[t * K + j] = id[j];
-      w[t * K + j] = wt[j];
-      if (blk) atomicAdd(&cnt[wv * E + id[j]], 1);
-    }
-  }
-  __syncthreads();
-  if (!blk) return;
-  for (int i = threadIdx.x; i < 4 * E; i += 256) {
-    const int64_t b = int64_t(blockIdx.x) * 4 + i / E;
-    if (b * 64 < T) blk[b * E + (i % E)] = cnt[i];
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Matrix-core logits for bf16 batches, E = 128*NE experts, 64 tokens per block:
-// l = X W_r^T with v_mfma_f32_32x32x16_bf16.  H moves global -> LDS in slabs of
-// 64 through a 3-stage ring of direct-to-LDS loads (lane L of a load fills row
-// L/8, slot L%8 with logical chunk (L%8)^(L/8)); wave w owns experts
-// [32*NE*w, 32*NE*(w+1)).  The logits tile then overlays the ring in LDS, wave 0
-// selects the experts of the 64 tokens (one thread each) and the block's expert
-// counts are written for the permutation.  grid = ceil(T/64), block = 256.
+// Matrix-core router logits for bf16 batches: l = X W_r^T (+ bias), fp32 [T, E].
+// One workgroup of 4 waves (2 x 2, each 32 tokens x 32 experts, one 32x32 MFMA
+// block) per 64-token x 64-expert tile, so a batch spreads over many CUs.  H moves
+// global -> LDS in slabs of 64 through a 3-stage ring of direct-to-LDS loads; the
+// rows are swizzled as swz16 reads them.  grid = (ceil(T/64), E/64), block = 256.
 typedef __attribute__((address_space(3))) void lvoid_t;
 __device__ __forceinline__ void dma16_r(const void* g, void* lds) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>((lvoid_t*)lds)));
@@ -142,67 +106,46 @@ __device__ __forceinline__ void wait_vm_lgkm0_r() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | ((N >> 4) << 14));
 }
 
-template <int NE, int K>
-__global__ __launch_bounds__(256) void k_router_mfma(
-    const bf16_t* __restrict__ x, const bf16_t* __restrict__ wr, const float* __restrict__ bias,
-    int64_t T, int H, int G, int Gk, float* __restrict__ logits_out, int32_t* __restrict__ ids,
-    float* __restrict__ w, int32_t* __restrict__ blk) {
-  constexpr int E = 128 * NE, BT = 64, LDL = E + 1;
-  constexpr int XU4 = BT * 8, WU4 = E * 8, STU4 = XU4 + WU4;          // uint4 per stage
-  constexpr int RING_BYTES = 3 * STU4 * 16;
-  constexpr int LG_BYTES = BT * LDL * 4 + BT * 64 * 4 + E * 4;        // logits + group scratch + counts
-  constexpr int LDS_BYTES = RING_BYTES > LG_BYTES ? RING_BYTES : LG_BYTES;
-  constexpr int AJ = BT / 32, BJ = E / 32, L = AJ + BJ;                // loads per lane per slab
-  __shared__ __align__(16) uint4 ring[LDS_BYTES / 16];
-  float* lg = reinterpret_cast<float*>(ring);                          // after the K loop
-  float* gs = lg + BT * LDL;
-  int* cnt = reinterpret_cast<int*>(gs + BT * 64);
-
+__global__ __launch_bounds__(256) void k_logits_mfma(const bf16_t* __restrict__ x,
+                                                     const bf16_t* __restrict__ wr,
+                                                     const float* __restrict__ bias, int64_t T,
+                                                     int H, int E, float* __restrict__ logits) {
+  constexpr int BT = 64, BE = 64, XU4 = BT * 8, STU4 = XU4 + BE * 8;   // uint4 per stage
+  constexpr int L = 4;                                                  // loads per lane per slab
+  __shared__ uint4 ring[3 * STU4];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wm = wv >> 1, wn = wv & 1;
   const int64_t t0 = int64_t(blockIdx.x) * BT;
-  const bf16_t* xg[AJ];
+  const int e0 = blockIdx.y * BE;
+  const bf16_t* xg[2];
+  const bf16_t* wg[2];
 #pragma unroll
-  for (int i = 0; i < AJ; ++i)
-    xg[i] = x + min<int64_t>(t0 + 8 * (wv + 4 * i) + (lane >> 3), T - 1) * H +
-            dma_chunk(lane, wv + 4 * i) * 8;
-  const bf16_t* wg[BJ];
-#pragma unroll
-  for (int i = 0; i < BJ; ++i)
-    wg[i] = wr + int64_t(8 * (wv + 4 * i) + (lane >> 3)) * H + dma_chunk(lane, wv + 4 * i) * 8;
+  for (int i = 0; i < 2; ++i) {
+    const int r = 8 * (wv + 4 * i) + (lane >> 3);
+    const int c = dma_chunk(lane, wv + 4 * i) * 8;
+    xg[i] = x + min<int64_t>(t0 + r, T - 1) * H + c;
+    wg[i] = wr + int64_t(e0 + r) * H + c;
+  }
   auto issue = [&](int kt, int stage) {
     uint4* st = ring + stage * STU4;
     const int ko = kt * 64;
 #pragma unroll
-    for (int i = 0; i < AJ; ++i) dma16_r(xg[i] + ko, st + (wv + 4 * i) * 64);
+    for (int i = 0; i < 2; ++i) dma16_r(xg[i] + ko, st + (wv + 4 * i) * 64);
 #pragma unroll
-    for (int i = 0; i < BJ; ++i) dma16_r(wg[i] + ko, st + XU4 + (wv + 4 * i) * 64);
+    for (int i = 0; i < 2; ++i) dma16_r(wg[i] + ko, st + XU4 + (wv + 4 * i) * 64);
   };
-
-  f32x16 acc[2][NE];
+  f32x16 acc;
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < NE; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
   auto compute = [&](int stage) {
     const uint4* xc = ring + stage * STU4;
     const uint4* wc = xc + XU4;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int chunk = ks * 2 + (lane >> 5);
-      bf16x8 af[2], bfr[NE];
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-        af[a] = __builtin_bit_cast(bf16x8, xc[swz16(a * 32 + (lane & 31), chunk)]);
-#pragma unroll
-      for (int b = 0; b < NE; ++b)
-        bfr[b] = __builtin_bit_cast(bf16x8, wc[swz16(wv * 32 * NE + b * 32 + (lane & 31), chunk)]);
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < NE; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
+      const bf16x8 af = __builtin_bit_cast(bf16x8, xc[swz16(wm * 32 + (lane & 31), chunk)]);
+      const bf16x8 bfr = __builtin_bit_cast(bf16x8, wc[swz16(wn * 32 + (lane & 31), chunk)]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr, acc, 0, 0, 0);
     }
   };
   const int nk = H / 64;
@@ -214,52 +157,106 @@ __global__ __launch_bounds__(256) void k_router_mfma(
     if (kt + 2 < nk) issue(kt + 2, (kt + 2) % 3);
     compute(kt % 3);
   }
-  wait_vm_lgkm0_r<0>();
-  block_sync_nowait();      // every wave is done with the ring before it is overlaid
-
-  // logits tile -> LDS [token][expert] (stride E+1), bias added
+  const int e = e0 + wn * 32 + (lane & 31);
+  const float b = bias ? bias[e] : 0.f;
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < NE; ++b) {
-      const int e = wv * 32 * NE + b * 32 + (lane & 31);
-      const float be = bias ? bias[e] : 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = a * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        lg[t * LDL + e] = acc[a][b][r] + be;
-      }
-    }
-  for (int i = tid; i < E; i += 256) cnt[i] = 0;
-  __syncthreads();
-  const int nt = int(min<int64_t>(BT, T - t0));
-  if (logits_out)
-    for (int i = tid; i < nt * E; i += 256) logits_out[t0 * E + i] = lg[(i / E) * LDL + i % E];
-  if (wv == 0 && lane < nt) {
-    const int64_t t = t0 + lane;
-    int32_t id[K];
-    float wt[K];
-    select_token_thread<K>(lg + lane * LDL, 1, E, G, Gk, gs + lane, 64, id, wt);
-#pragma unroll
-    for (int j = 0; j < K; ++j) {
-      ids[t * K + j] = id[j];
-      w[t * K + j] = wt[j];
-      atomicAdd(&cnt[id[j]], 1);
-    }
+  for (int r = 0; r < 16; ++r) {
+    const int64_t t = t0 + wm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    if (t < T) logits[t * E + e] = acc[r] + b;
   }
-  __syncthreads();
-  if (blk)
-    for (int i = tid; i < E; i += 256) blk[int64_t(blockIdx.x) * E + i] = cnt[i];
 }
 
 // ---------------------------------------------------------------------------
-bool router_mfma_ok(const Plan& p) {
-  return p.act == MOE_BF16 && (p.E == 128 || p.E == 256) && p.H % 64 == 0 && p.G <= 64 &&
-         p.T > 16;
+// Group-limited top-k from fp32 logits, one wave per token (wave-wide arg-max
+// rounds), 16 waves per 64-token block; each block writes its per-expert row
+// counts for the permutation.  grid = ceil(T/64), block = 1024.
+template <int QMAX>
+__global__ __launch_bounds__(1024) void k_select_wave(const float* __restrict__ logits, int64_t T,
+                                                      int E, int G, int Gk, int k,
+                                                      int32_t* __restrict__ ids,
+                                                      float* __restrict__ w,
+                                                      int32_t* __restrict__ blk) {
+  __shared__ int cnt[1024];
+  for (int i = threadIdx.x; i < E; i += 1024) cnt[i] = 0;
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  for (int i = 0; i < 4; ++i) {
+    const int64_t t = int64_t(blockIdx.x) * 64 + wv + 16 * i;
+    if (t >= T) break;   // uniform over the wave
+    const int id = select_token_wave<QMAX>(logits + t * E, E, G, Gk, k, ids + t * k, w + t * k);
+    if (lane < k) atomicAdd(&cnt[id], 1);
+  }
+  __syncthreads();
+  if (blk)
+    for (int i = threadIdx.x; i < E; i += 1024) blk[int64_t(blockIdx.x) * E + i] = cnt[i];
+}
+
+// ---------------------------------------------------------------------------
+// Same selection with sixteen lanes per token (select_token_row), four tokens per
+// wave, 64 tokens per block of 16 waves.  grid = ceil(T/64), block = 1024.
+template <int V>
+__global__ __launch_bounds__(1024) void k_select_rows(const float* __restrict__ logits, int64_t T,
+                                                      int E, int G, int Gk, int k,
+                                                      int32_t* __restrict__ ids,
+                                                      float* __restrict__ w,
+                                                      int32_t* __restrict__ blk) {
+  __shared__ int cnt[256];
+  for (int i = threadIdx.x; i < E; i += 1024) cnt[i] = 0;
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, r16 = lane & 15;
+  const int64_t t = int64_t(blockIdx.x) * 64 + wv * 4 + (lane >> 4);
+  const bool live = t < T;
+  const float* l = logits + (live ? t : T - 1) * E + V * r16;
+  float lv[V];
+  if constexpr (V % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < V; i += 4) {
+      const float4 q = *reinterpret_cast<const float4*>(l + i);
+      lv[i] = q.x; lv[i + 1] = q.y; lv[i + 2] = q.z; lv[i + 3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < V; ++i) lv[i] = l[i];
+  }
+  int id;
+  float wt;
+  select_token_row<V>(lv, E, G, Gk, k, id, wt);
+  if (live && r16 < k) {
+    ids[t * k + r16] = id;
+    w[t * k + r16] = wt;
+    atomicAdd(&cnt[id], 1);
+  }
+  __syncthreads();
+  if (blk)
+    for (int i = threadIdx.x; i < E; i += 1024) blk[int64_t(blockIdx.x) * E + i] = cnt[i];
+}
+
+// the row selection covers E = 16 V (V <= 16) with groups spanning a power-of-two
+// number of lanes, or whole groups inside a lane
+static bool select_rows_ok(const Plan& p) {
+  if (p.E % 16 || p.E > 256 || p.k > 16) return false;
+  const int V = p.E / 16, n = p.E / p.G;
+  if (p.G == 1) return true;
+  if (n >= V) {
+    const int span = n / V;
+    return n % V == 0 && (span & (span - 1)) == 0 && span <= 16;
+  }
+  return V % n == 0;
+}
+
+// ---------------------------------------------------------------------------
+bool logits_mfma_ok(const Plan& p) {
+  return p.act == MOE_BF16 && p.E % 64 == 0 && p.H % 64 == 0 && p.T > 16;
 }
 
 int launch_logits(const Plan& p, const void* x, const void* wr, const float* bias, float* logits,
                   hipStream_t st) {
+  if (logits_mfma_ok(p)) {
+    const dim3 grid(unsigned((p.T + 63) / 64), unsigned(p.E / 64));
+    hipLaunchKernelGGL(k_logits_mfma, grid, dim3(256), 0, st, (const bf16_t*)x, (const bf16_t*)wr,
+                       bias, p.T, p.H, p.E, logits);
+    return check_launch();
+  }
   const int tsize = p.act == MOE_F32 ? 4 : 2;
   const int hpass = std::min(p.H, 2048);
   const int RT = int(std::max<int64_t>(1, std::min<int64_t>(16, 32768 / (int64_t(hpass) * tsize))));
@@ -274,50 +271,42 @@ int launch_logits(const Plan& p, const void* x, const void* wr, const float* bia
   return check_launch();
 }
 
-#define MOE_K_SWITCH(K_VAL, MACRO) \
-  switch (K_VAL) {                 \
-    case 1: MACRO(1); break;       \
-    case 2: MACRO(2); break;       \
-    case 3: MACRO(3); break;       \
-    case 4: MACRO(4); break;       \
-    case 5: MACRO(5); break;       \
-    case 6: MACRO(6); break;       \
-    case 7: MACRO(7); break;       \
-    case 8: MACRO(8); break;       \
-    case 9: MACRO(9); break;       \
-    case 10: MACRO(10); break;     \
-    case 11: MACRO(11); break;     \
-    case 12: MACRO(12); break;     \
-    case 13: MACRO(13); break;     \
-    case 14: MACRO(14); break;     \
-    case 15: MACRO(15); break;     \
-    default: MACRO(16); break;     \
-  }
 
 int launch_select(const Plan& p, const float* logits, int32_t* ids, float* w, int32_t* blk,
                   hipStream_t st) {
-  const dim3 grid(unsigned((p.T + 255) / 256));
-  const size_t lds = (size_t(4) * p.E + size_t(256) * p.G) * 4;
-#define MOE_SEL(KK)                                                                        \
-  hipLaunchKernelGGL(k_router_select<KK>, grid, dim3(256), lds, st, logits, p.T, p.E, p.G, \
-                     p.Gk, ids, w, blk)
-  MOE_K_SWITCH(p.k, MOE_SEL)
-#undef MOE_SEL
-  return check_launch();
-}
-
-int launch_router_mfma(const Plan& p, const void* x, const void* wr, const float* bias,
-                       float* logits_out, int32_t* ids, float* w, int32_t* blk, hipStream_t st) {
   const dim3 grid(unsigned((p.T + 63) / 64));
-#define MOE_RM(KK)                                                                            \
-  if (p.E == 128)                                                                             \
-    hipLaunchKernelGGL((k_router_mfma<1, KK>), grid, dim3(256), 0, st, (const bf16_t*)x,     \
-                       (const bf16_t*)wr, bias, p.T, p.H, p.G, p.Gk, logits_out, ids, w, blk); \
-  else                                                                                        \
-    hipLaunchKernelGGL((k_router_mfma<2, KK>), grid, dim3(256), 0, st, (const bf16_t*)x,     \
-                       (const bf16_t*)wr, bias, p.T, p.H, p.G, p.Gk, logits_out, ids, w, blk)
-  MOE_K_SWITCH(p.k, MOE_RM)
-#undef MOE_RM
+  if (select_rows_ok(p)) {
+    const int V = p.E / 16;
+#define MOE_SR(VV)                                                                              \
+  hipLaunchKernelGGL(k_select_rows<VV>, grid, dim3(1024), 0, st, logits, p.T, p.E, p.G, p.Gk, \
+                     p.k, ids, w, blk)
+    if (V == 1) MOE_SR(1);
+    else if (V == 2) MOE_SR(2);
+    else if (V == 4) MOE_SR(4);
+    else if (V == 8) MOE_SR(8);
+    else if (V == 16) MOE_SR(16);
+    else if (V == 3) MOE_SR(3);
+    else if (V == 5) MOE_SR(5);
+    else if (V == 6) MOE_SR(6);
+    else if (V == 7) MOE_SR(7);
+    else if (V <= 12) {
+      if (V == 9) MOE_SR(9); else if (V == 10) MOE_SR(10); else if (V == 11) MOE_SR(11); else MOE_SR(12);
+    } else {
+      if (V == 13) MOE_SR(13); else if (V == 14) MOE_SR(14); else MOE_SR(15);
+    }
+#undef MOE_SR
+    return check_launch();
+  }
+  if (p.E <= 64)
+    hipLaunchKernelGGL(k_select_wave<1>, grid, dim3(1024), 0, st, logits, p.T, p.E, p.G, p.Gk, p.k, ids, w, blk);
+  else if (p.E <= 128)
+    hipLaunchKernelGGL(k_select_wave<2>, grid, dim3(1024), 0, st, logits, p.T, p.E, p.G, p.Gk, p.k, ids, w, blk);
+  else if (p.E <= 256)
+    hipLaunchKernelGGL(k_select_wave<4>, grid, dim3(1024), 0, st, logits, p.T, p.E, p.G, p.Gk, p.k, ids, w, blk);
+  else if (p.E <= 512)
+    hipLaunchKernelGGL(k_select_wave<8>, grid, dim3(1024), 0, st, logits, p.T, p.E, p.G, p.Gk, p.k, ids, w, blk);
+  else
+    hipLaunchKernelGGL(k_select_wave<16>, grid, dim3(1024), 0, st, logits, p.T, p.E, p.G, p.Gk, p.k, ids, w, blk);
   return check_launch();
 }
 

@@ -22,10 +22,11 @@ __device__ __forceinline__ float key_score(uint64_t key) {
 // One wave per token (low latency, for a handful of tokens).  `l` points to the
 // token's E logits.  Lane g < G holds group g's score (G <= 64); each lane holds
 // experts lane + 64q, q < QMAX, as keys; each of the Gk (then k) rounds is one
-// wave-wide arg-max.  Must be called with the whole wave active.
+// wave-wide arg-max.  Must be called with the whole wave active.  Returns, in
+// lane j < k, the id of the j-th chosen expert.
 template <int QMAX>
-__device__ void select_token_wave(const float* __restrict__ l, int E, int G, int Gk, int k,
-                                  int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
+__device__ int select_token_wave(const float* __restrict__ l, int E, int G, int Gk, int k,
+                                 int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
   const int lane = threadIdx.x & 63;
   const int n = E / G;
   float lv[QMAX];
@@ -108,65 +109,107 @@ __device__ void select_token_wave(const float* __restrict__ l, int E, int G, int
     ids_out[lane] = idsel;
     w_out[lane] = p / z;
   }
+  return idsel;
 }
 
 // ---------------------------------------------------------------------------
-// One thread per token (throughput, for many tokens).  The token's logits are at
-// l[e * stride] (LDS or global).  `gscratch` holds G floats per thread at
-// gscratch[g * gstride].  Keys of the K best experts are kept sorted in
-// registers by insertion.  Returns the K ids and weights through the pointers.
-template <int K>
-__device__ void select_token_thread(const float* l, int stride, int E, int G, int Gk,
-                                    float* gscratch, int gstride, int32_t* __restrict__ ids_out,
-                                    float* __restrict__ w_out) {
+// Sixteen lanes per token (a DPP row): four tokens per wave, every reduction stays
+// inside the row.  Lane r of the row holds experts [V*r, V*r + V) (E = 16 V).
+// Groups of n = E/G experts: either a group spans n/V whole lanes (n >= V, n/V a
+// power of two), or a lane holds V/n whole groups (n < V); G <= 64.  Keys are
+// (score, index) as in select_token_wave.  Returns, in row lane j < k, the j-th
+// chosen expert and its weight through `id_out` / `w_out`.
+__device__ __forceinline__ uint64_t row_max_u64(uint64_t v) {
+  v = dpp_max_u64<0xB1>(v);    // quad_perm [1,0,3,2]
+  v = dpp_max_u64<0x4E>(v);    // quad_perm [2,3,0,1]
+  v = dpp_max_u64<0x141>(v);   // row_half_mirror
+  return dpp_max_u64<0x140>(v);   // row_mirror
+}
+__device__ __forceinline__ float row_sum(float v) {
+  v += dppf<0xB1>(v);
+  v += dppf<0x4E>(v);
+  v += dppf<0x141>(v);
+  return v + dppf<0x140>(v);
+}
+__device__ __forceinline__ float row_segmax(float v, int span) {   // max over aligned runs of `span` lanes
+  if (span >= 2) v = fmaxf(v, dppf<0xB1>(v));
+  if (span >= 4) v = fmaxf(v, dppf<0x4E>(v));
+  if (span >= 8) v = fmaxf(v, dppf<0x141>(v));
+  if (span >= 16) v = fmaxf(v, dppf<0x140>(v));
+  return v;
+}
+
+template <int V>
+__device__ void select_token_row(const float (&lv)[V], int E, int G, int Gk, int k, int& id_out,
+                                 float& w_out) {
+  const int r16 = threadIdx.x & 15;
   const int n = E / G;
   uint64_t kept = ~0ull;
   if (G > 1) {
-    for (int g = 0; g < G; ++g) {
-      float m = l[(g * n) * stride];
-      for (int i = 1; i < n; ++i) m = fmaxf(m, l[(g * n + i) * stride]);
-      gscratch[g * gstride] = m;
-    }
-    kept = 0;
-    for (int r = 0; r < Gk; ++r) {
-      uint64_t best = 0;
-      for (int g = 0; g < G; ++g) {
-        if ((kept >> g) & 1ull) continue;
-        const uint64_t key = rank_key(gscratch[g * gstride], g);
-        best = key > best ? key : best;
+    if (n >= V) {
+      // one group per lane, spanning n / V lanes
+      float m = lv[0];
+#pragma unroll
+      for (int i = 1; i < V; ++i) m = fmaxf(m, lv[i]);
+      m = row_segmax(m, n / V);
+      const int g = (V * r16) / n;
+      uint64_t gk = rank_key(m, g);
+      kept = 0;
+      for (int r = 0; r < Gk; ++r) {
+        const uint64_t win = row_max_u64(gk);
+        const int gw = key_index(win);
+        kept |= 1ull << gw;
+        if (g == gw) gk = 0;
       }
-      kept |= 1ull << key_index(best);
-    }
-  }
-  uint64_t keys[K];
+    } else {
+      // V / n whole groups per lane
+      constexpr int GPL_MAX = V;
+      uint64_t gk[GPL_MAX];
+      const int gpl = V / n;
 #pragma unroll
-  for (int i = 0; i < K; ++i) keys[i] = 0ull;
-  for (int g = 0; g < G; ++g) {
-    if (!((kept >> g) & 1ull)) continue;
-    for (int e = g * n; e < (g + 1) * n; ++e) {
-      const uint64_t c = rank_key(l[e * stride], e);
-      if (c <= keys[K - 1]) continue;
-      // sorted (descending) insertion: keys[i] = max(keys[i], min(keys[i-1], c))
-#pragma unroll
-      for (int i = K - 1; i >= 1; --i) {
-        const uint64_t lo = keys[i - 1] < c ? keys[i - 1] : c;
-        keys[i] = keys[i] > lo ? keys[i] : lo;
+      for (int j = 0; j < GPL_MAX; ++j) {
+        float m = -__builtin_huge_valf();
+        if (j < gpl)
+          for (int i = 0; i < n; ++i) m = fmaxf(m, lv[j * n + i]);
+        gk[j] = j < gpl ? rank_key(m, r16 * gpl + j) : 0ull;
       }
-      keys[0] = keys[0] > c ? keys[0] : c;
+      kept = 0;
+      for (int r = 0; r < Gk; ++r) {
+        uint64_t best = gk[0];
+#pragma unroll
+        for (int j = 1; j < GPL_MAX; ++j) best = gk[j] > best ? gk[j] : best;
+        const uint64_t win = row_max_u64(best);
+        kept |= 1ull << key_index(win);
+#pragma unroll
+        for (int j = 0; j < GPL_MAX; ++j)
+          if (gk[j] == win) gk[j] = 0ull;
+      }
     }
   }
-  const float lmax = key_score(keys[0]);
-  float p[K], z = 0.f;
+  uint64_t kv[V];
 #pragma unroll
-  for (int i = 0; i < K; ++i) {
-    p[i] = __expf(key_score(keys[i]) - lmax);
-    z += p[i];
+  for (int i = 0; i < V; ++i) {
+    const int e = V * r16 + i;
+    kv[i] = ((kept >> (e / n)) & 1ull) ? rank_key(lv[i], e) : 0ull;
   }
+  int idsel = 0;
+  float lsel = 0.f, lmax = 0.f;
+  for (int r = 0; r < k; ++r) {
+    uint64_t best = kv[0];
 #pragma unroll
-  for (int i = 0; i < K; ++i) {
-    ids_out[i] = key_index(keys[i]);
-    w_out[i] = p[i] / z;
+    for (int i = 1; i < V; ++i) best = kv[i] > best ? kv[i] : best;
+    const uint64_t win = row_max_u64(best);
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+      if (kv[i] == win) kv[i] = 0ull;
+    const float lw = key_score(win);
+    if (r == 0) lmax = lw;
+    if (r16 == r) { idsel = key_index(win); lsel = lw; }
   }
+  const float p = r16 < k ? __expf(lsel - lmax) : 0.f;
+  const float z = row_sum(p);
+  id_out = idsel;
+  w_out = p / z;
 }
 
 }  // namespace moe
