@@ -70,15 +70,22 @@ __global__ __launch_bounds__(256) void k_decode_gateup(DecodeArgs a) {
   const TW* shd = static_cast<const TW*>(a.shd);
 
   // ---------------------------------------------------------------- 1. routing
-  constexpr int CH = 16 / sizeof(TA);
-  for (int c = threadIdx.x; c < T * H / CH; c += 256)
-    *reinterpret_cast<uint4*>(xs + c * CH) = *reinterpret_cast<const uint4*>(x + int64_t(c) * CH);
-  for (int t = wv; t < T; t += 4)
-    select_token_wave<QMAX>(a.logits + int64_t(t) * E, E, a.G, a.Gk, k, ids_l + t * k, w_l + t * k);
   // slot i = t*k + j.  Wave w owns slots [64w, 64w+64): bit (i % 64) of
   // bits[w][e] says slot i chose expert e, so a slot's rank among its expert's
   // rows is a popcount of the lower bits (rows stay in ascending slot order).
   for (int i = threadIdx.x; i < 4 * E; i += 256) bits_l[i] = 0ull;
+  // the token rows and the logits travel in one memory round trip: the row
+  // chunks are loaded into registers, the selection's logits loads follow, and
+  // the rows are written to LDS afterwards
+  // the token rows go global -> LDS by direct loads issued first (1 KB per wave
+  // instruction), so they travel together with the selection's logits loads
+  constexpr int CH = 16 / sizeof(TA);
+  const int nch = T * H / CH;
+  for (int c0 = wv * 64; c0 < nch; c0 += 256)
+    if (c0 + lane < nch) dma16(x + int64_t(c0 + lane) * CH, xs + int64_t(c0) * CH);
+  for (int t = wv; t < T; t += 4)
+    select_token_wave<QMAX>(a.logits + int64_t(t) * E, E, a.G, a.Gk, k, ids_l + t * k, w_l + t * k);
+  wait_vm_lgkm0<0>();
   __syncthreads();
   if (threadIdx.x < nslot) atomicOr(&bits_l[wv * E + ids_l[threadIdx.x]], 1ull << lane);
   __syncthreads();
@@ -92,15 +99,17 @@ __global__ __launch_bounds__(256) void k_decode_gateup(DecodeArgs a) {
             __popcll(bits_l[3 * E + e]);
     else if (e < E + S)
       cnt = T;
-    int sum, nsum;
-    const int off = tot + block_exclusive_scan_256(cnt, tmp, sum);
-    const int pos = nact + block_exclusive_scan_256(cnt > 0 ? 1 : 0, tmp, nsum);
+    // one scan for both the row offsets (low 16 bits) and the active-list
+    // positions (high bits): at most T*(k+S) <= 768 rows
+    int sum;
+    const int ex = block_exclusive_scan_256(cnt | (cnt > 0 ? 1 << 16 : 0), tmp, sum);
+    const int off = tot + (ex & 0xFFFF), pos = nact + (ex >> 16);
     if (e < E + S) off_l[e] = off;
     if (cnt > 0) act_l[pos] = e;
     if (e >= E && e < E + S)
       for (int t = 0; t < T; ++t) rt_l[off + t] = t;
-    tot += sum;
-    nact += nsum;
+    tot += sum & 0xFFFF;
+    nact += sum >> 16;
   }
   if (threadIdx.x == 0) {
     off_l[E + S] = tot;

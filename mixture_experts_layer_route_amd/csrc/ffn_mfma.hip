@@ -207,29 +207,6 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmBf16Args p) {
 // the fragment reads undo.  Waits are explicit (vmcnt for the slab about to be
 // read, lgkmcnt(0) so no fragment read is in flight when a slot is refilled)
 // followed by a bare s_barrier.
-typedef __attribute__((address_space(1))) void gvoid_t;
-typedef __attribute__((address_space(3))) void lvoid_t;
-
-// The load is written in asm so that the compiler does not add its own
-// conservative vmcnt(0) before every later LDS read; completion is tracked by
-// the explicit waits below (VMEM loads complete in issue order).  The address
-// and M0 are consumed when the load issues; M0 is saved and restored around it
-// and the only register output is that saved scalar copy.
-__device__ __forceinline__ void dma16(const void* g, void* lds) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>((lvoid_t*)lds)));
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(m0), "v"(g)
-      : "memory");
-}
-// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4]<<14)
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm0() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | ((N >> 4) << 14));
-}
 
 // Tile configuration of the pipelined bf16 kernel: BM x BN outputs per workgroup
 // of W = WM x WN waves, each owning (BM / WM) x (BN / WN) outputs as MI x NI

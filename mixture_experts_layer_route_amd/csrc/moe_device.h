@@ -16,6 +16,30 @@ __device__ __forceinline__ void block_sync_nowait() {
   asm volatile("" ::: "memory");
 }
 
+// Direct global -> LDS load of 16 bytes per lane (global_load_lds_dwordx4): the
+// wave's 64 lanes write 1 KB at `lds` (wave-uniform), lane L at lds + 16 L.
+typedef __attribute__((address_space(3))) void lvoid_t;
+// The load is written in asm so that the compiler does not add its own
+// conservative vmcnt(0) before every later LDS read; completion is tracked by
+// the explicit waits below (VMEM loads complete in issue order).  The address
+// and M0 are consumed when the load issues; M0 is saved and restored around it
+// and the only register output is that saved scalar copy.
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>((lvoid_t*)lds)));
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0), "v"(g)
+      : "memory");
+}
+// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4]<<14)
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | ((N >> 4) << 14));
+}
+
 #ifndef MOE_SWZ_SHIFT
 #define MOE_SWZ_SHIFT 1
 #endif

@@ -86,26 +86,76 @@ __global__ __launch_bounds__(256) void k_router_logits_fma(
 }
 
 // ---------------------------------------------------------------------------
+// Logits for a few tokens (T <= 16): one wave per expert, every load of the
+// expert's row chunks and of the token rows issued from global memory before
+// any is used (one memory round trip per 4 tokens and 2048 hidden units), then a
+// DPP reduction per token.  grid = ceil(E/4), block = 256.
+template <typename TA>
+__global__ __launch_bounds__(256) void k_logits_few(const TA* __restrict__ x,
+                                                    const TA* __restrict__ wr,
+                                                    const float* __restrict__ bias,
+                                                    float* __restrict__ logits, int T, int H,
+                                                    int E) {
+  constexpr int SMAX = 4, TQ = 4;        // 512-wide chunks per pass, tokens per round trip
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= E) return;                    // uniform over the wave
+  const TA* wrow = wr + int64_t(e) * H;
+  float acc[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+  for (int hb = 0; hb < H; hb += 512 * SMAX) {
+    Chunk8<TA> wc[SMAX];
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s) {
+      const int h = hb + s * 512 + lane * 8;
+      if (h < H) wc[s].load(wrow + h);
+    }
+#pragma unroll
+    for (int g = 0; g < 16; g += TQ) {
+      if (g >= T) break;
+      Chunk8<TA> xc[TQ][SMAX];
+#pragma unroll
+      for (int q = 0; q < TQ; ++q)
+#pragma unroll
+        for (int s = 0; s < SMAX; ++s) {
+          const int h = hb + s * 512 + lane * 8;
+          if (g + q < T && h < H) xc[q][s].load(x + int64_t(g + q) * H + h);
+        }
+#pragma unroll
+      for (int s = 0; s < SMAX; ++s) {
+        const int h = hb + s * 512 + lane * 8;
+        if (h < H) {
+          float wv[8];
+          wc[s].get(wv);
+#pragma unroll
+          for (int q = 0; q < TQ; ++q) {
+            if (g + q < T) {
+              float xv[8];
+              xc[q][s].get(xv);
+              acc[g + q] = dot8(xv, wv, acc[g + q]);
+            }
+          }
+        }
+      }
+    }
+  }
+  const float b = bias ? bias[e] : 0.f;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    if (q < T) {
+      const float v = wave_sum(acc[q]);
+      if (lane == 0) logits[int64_t(q) * E + e] = v + b;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Matrix-core router logits for bf16 batches: l = X W_r^T (+ bias), fp32 [T, E].
 // One workgroup of 4 waves (2 x 2, each 32 tokens x 32 experts, one 32x32 MFMA
 // block) per 64-token x 64-expert tile, so a batch spreads over many CUs.  H moves
 // global -> LDS in slabs of 64 through a 3-stage ring of direct-to-LDS loads; the
 // rows are swizzled as swz16 reads them.  grid = (ceil(T/64), E/64), block = 256.
-typedef __attribute__((address_space(3))) void lvoid_t;
-__device__ __forceinline__ void dma16_r(const void* g, void* lds) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>((lvoid_t*)lds)));
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(m0), "v"(g)
-      : "memory");
-}
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm0_r() {
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | ((N >> 4) << 14));
-}
-
 __global__ __launch_bounds__(256) void k_logits_mfma(const bf16_t* __restrict__ x,
                                                      const bf16_t* __restrict__ wr,
                                                      const float* __restrict__ bias, int64_t T,
@@ -130,9 +180,9 @@ __global__ __launch_bounds__(256) void k_logits_mfma(const bf16_t* __restrict__ 
     uint4* st = ring + stage * STU4;
     const int ko = kt * 64;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma16_r(xg[i] + ko, st + (wv + 4 * i) * 64);
+    for (int i = 0; i < 2; ++i) dma16(xg[i] + ko, st + (wv + 4 * i) * 64);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma16_r(wg[i] + ko, st + XU4 + (wv + 4 * i) * 64);
+    for (int i = 0; i < 2; ++i) dma16(wg[i] + ko, st + XU4 + (wv + 4 * i) * 64);
   };
   f32x16 acc;
 #pragma unroll
@@ -152,7 +202,7 @@ __global__ __launch_bounds__(256) void k_logits_mfma(const bf16_t* __restrict__ 
   issue(0, 0);
   if (nk > 1) issue(1, 1);
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) wait_vm_lgkm0_r<L>(); else wait_vm_lgkm0_r<0>();
+    if (kt + 1 < nk) wait_vm_lgkm0<L>(); else wait_vm_lgkm0<0>();
     block_sync_nowait();
     if (kt + 2 < nk) issue(kt + 2, (kt + 2) % 3);
     compute(kt % 3);
@@ -251,6 +301,16 @@ bool logits_mfma_ok(const Plan& p) {
 
 int launch_logits(const Plan& p, const void* x, const void* wr, const float* bias, float* logits,
                   hipStream_t st) {
+  if (p.T <= 16) {
+    const dim3 grid(unsigned((p.E + 3) / 4));
+    if (p.act == MOE_F32)
+      hipLaunchKernelGGL(k_logits_few<float>, grid, dim3(256), 0, st, (const float*)x,
+                         (const float*)wr, bias, logits, int(p.T), p.H, p.E);
+    else
+      hipLaunchKernelGGL(k_logits_few<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)x,
+                         (const bf16_t*)wr, bias, logits, int(p.T), p.H, p.E);
+    return check_launch();
+  }
   if (logits_mfma_ok(p)) {
     const dim3 grid(unsigned((p.T + 63) / 64), unsigned(p.E / 64));
     hipLaunchKernelGGL(k_logits_mfma, grid, dim3(256), 0, st, (const bf16_t*)x, (const bf16_t*)wr,

@@ -33,7 +33,8 @@ __device__ int select_token_wave(const float* __restrict__ l, int E, int G, int 
 #pragma unroll
   for (int q = 0; q < QMAX; ++q) {
     const int e = lane + 64 * q;
-    lv[q] = e < E ? l[e] : -__builtin_huge_valf();
+    const float v = l[min(e, E - 1)];   // clamped load, then masked: no branch around it
+    lv[q] = e < E ? v : -__builtin_huge_valf();
   }
   uint64_t kept = ~0ull;
   if (G > 1) {
