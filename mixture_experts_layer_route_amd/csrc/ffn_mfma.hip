@@ -468,7 +468,9 @@ struct GemmFp8Args {
   const float* shs0;
   const float* shs1;
   const float* row_w;         // down, weighted bf16 output
-  float* hout;                // gate/up: h fp32 [R, I]
+  float* hout;                // gate/up: h fp32 [R, I] (register-staged kernel)
+  uint8_t* qout;              // gate/up: h e4m3 codes [R, I] (pipelined kernel)
+  float* qscale;              // gate/up: h scales [R, I/128] (pipelined kernel)
   bf16_t* out16;              // down: weighted y_perm [R, H] (bf16)
   float* out32;               // down: unweighted y_perm [R, H]
   int K, N, E;
@@ -665,6 +667,286 @@ __global__ __launch_bounds__(256) void k_gemm_fp8(GemmFp8Args p) {
 // Activation quantisation to e4m3, one wave per (row, 128-column block):
 // scale = amax / 448 (fp32 division; 1 for an all-zero block), code = RNE(v / scale).
 // Optional gather: row r reads source row row_token[r].
+// ===========================================================================
+// Block FP8, pipelined.  The slab of one K scale block (128 e4m3 = 128 bytes per
+// tile row) has the same LDS layout as a bf16 slab of 64, so the same ring of
+// direct-to-LDS loads, swizzle and XCD-aware item order apply.  Tile: BM = 128
+// activation rows x BN = 256 weight rows (gate/up: 128 gate + the matching 128 up
+// rows), 8 waves of 64 x 64.  The weight rows are the MFMA's M operand, so a
+// 32-row weight block has one scale per slab and an activation row (a lane) has
+// one; each slab's two 32x32x64 MFMAs go into a fresh block that is folded as
+// acc += slab * (s_act * s_w).  All scales of the tile are staged in LDS before
+// the K loop.  The gate/up epilogue applies SwiGLU and quantises h at once: the
+// tile's 128 h columns are exactly one 128-wide scale block of each row.
+struct Fp8Tile {
+  static constexpr int BM = 128, BN = 256, KB = 128, WM = 2, WN = 4, W = WM * WN, NT = 64 * W;
+  static constexpr int MI = BM / WM / 32, NI = BN / WN / 32;          // 2 x 2 blocks per wave
+  static constexpr int AJ = BM / (8 * W), BJ = BN / (8 * W), L = AJ + BJ;
+  static constexpr int A_U4 = BM * 8, STAGE_U4 = (BM + BN) * 8, RING_U4 = 3 * STAGE_U4;
+  static constexpr int SMAX = 16;                                     // K <= 2048
+};
+
+template <bool GATEUP>
+__global__ __launch_bounds__(Fp8Tile::NT) __attribute__((amdgpu_waves_per_eu(2)))
+void k_gemm_fp8_v2(GemmFp8Args p) {
+  using C = Fp8Tile;
+  constexpr int BM = C::BM, BN = C::BN, W = C::W, WM = C::WM, WN = C::WN, MI = C::MI, NI = C::NI;
+  constexpr int AJ = C::AJ, BJ = C::BJ, L = C::L, NT = C::NT, SMAX = C::SMAX;
+  __shared__ uint4 smem[C::RING_U4];
+  __shared__ float sa_l[BM * SMAX];      // activation scales [row][slab]
+  __shared__ float sw_l[4 * SMAX];       // weight block scales [block][slab]
+  const int ncol = GATEUP ? p.N / (BN / 2) : p.N / BN;
+  int tile, ct;
+  if (!xcd_item(p.meta[1], ncol, tile, ct)) return;
+  const int2 te = p.tiles[tile];
+  const int e = te.x, m0 = te.y;
+  const int base = p.offsets[e];
+  const int cnt = p.offsets[e + 1] - base;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wm = wv / WN, wn = wv % WN;
+  const int64_t K = p.K;
+  const int nkb = int(K / C::KB);
+
+  const uint8_t* ag[AJ];
+#pragma unroll
+  for (int i = 0; i < AJ; ++i) {
+    const int r = 8 * (wv + W * i) + (lane >> 3);
+    const int m = min(m0 + r, cnt - 1);
+    const int64_t arow = GATEUP ? int64_t(p.row_token[base + m]) : int64_t(base + m);
+    ag[i] = p.a + arow * K + dma_chunk(lane, wv + W * i) * 16;
+  }
+  const int64_t mst = int64_t(p.N) * K;             // bytes of one expert matrix
+  const uint8_t* bg[BJ];
+#pragma unroll
+  for (int i = 0; i < BJ; ++i) {
+    const int r = 8 * (wv + W * i) + (lane >> 3);
+    const int c = dma_chunk(lane, wv + W * i) * 16;
+    if (GATEUP) {
+      const int c0 = ct * (BN / 2);
+      bg[i] = (r < BN / 2 ? expert_mat(p.w0, p.sh0, e, p.E, mst) + int64_t(c0 + r) * K
+                          : expert_mat(p.w1, p.sh1, e, p.E, mst) + int64_t(c0 + r - BN / 2) * K) + c;
+    } else {
+      bg[i] = expert_mat(p.w0, p.sh0, e, p.E, mst) + int64_t(ct * BN + r) * K + c;
+    }
+  }
+  auto issue = [&](int kt, int slot) {
+    const int64_t ko = int64_t(kt) * C::KB;
+    uint4* sa = smem + slot * C::STAGE_U4;
+    uint4* sb = sa + C::A_U4;
+#pragma unroll
+    for (int i = 0; i < AJ; ++i) dma16(ag[i] + ko, sa + (wv + W * i) * 64);
+#pragma unroll
+    for (int i = 0; i < BJ; ++i) dma16(bg[i] + ko, sb + (wv + W * i) * 64);
+  };
+  const int nk = nkb;
+  issue(0, 0);
+  if (nk > 1) issue(1, 1);
+
+  // scales of the tile -> LDS (while the first slabs are in flight).  Weight
+  // scale blocks: gate/up [0] gate, [1] up (the tile's 128 h columns = block ct);
+  // down: the two 128-row blocks 2ct, 2ct+1 of the tile's 256 output columns.
+  {
+    const int64_t sst = int64_t(p.N / 128) * nkb;
+    constexpr int SP = BM * SMAX / NT;              // staged scales per thread (4)
+    float sv[SP];
+#pragma unroll
+    for (int u = 0; u < SP; ++u) {                  // clamped loads, all in flight together
+      const int i = min(tid + u * NT, BM * nkb - 1);
+      const int row = i / nkb, kb = i - row * nkb;
+      const int m = min(m0 + row, cnt - 1);
+      const int64_t arow = GATEUP ? int64_t(p.row_token[base + m]) : int64_t(base + m);
+      sv[u] = p.a_scale[arow * nkb + kb];
+    }
+#pragma unroll
+    for (int u = 0; u < SP; ++u) {
+      const int i = tid + u * NT;
+      if (i < BM * nkb) sa_l[(i / nkb) * SMAX + i % nkb] = sv[u];
+    }
+    if (tid < 2 * nkb) {
+      const int blk = tid / nkb, kb = tid - blk * nkb;
+      float v;
+      if (GATEUP)
+        v = (blk == 0 ? expert_mat(p.s0, p.shs0, e, p.E, sst) : expert_mat(p.s1, p.shs1, e, p.E, sst))
+                [int64_t(ct) * nkb + kb];
+      else
+        v = expert_mat(p.s0, p.shs0, e, p.E, sst)[int64_t(2 * ct + blk) * nkb + kb];
+      sw_l[blk * SMAX + kb] = v;
+    }
+  }
+
+  f32x16 acc[MI][NI];
+#pragma unroll
+  for (int a = 0; a < MI; ++a)
+#pragma unroll
+    for (int b = 0; b < NI; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+  // this wave's weight blocks: gate/up b = 0 gate, 1 up (same h columns);
+  // down: output columns wn*64 + 32b
+  auto wrow = [&](int b) {
+    return GATEUP ? (b == 0 ? 0 : BN / 2) + wn * (BN / 2 / WN) + (lane & 31)
+                  : wn * (BN / WN) + b * 32 + (lane & 31);
+  };
+  const int swb0 = GATEUP ? 0 : (wn * (BN / WN)) / 128;   // scale block of weight block b
+  auto compute = [&](int slot, int kt, auto&& between) {
+    const uint4* sa = smem + slot * C::STAGE_U4;
+    const uint4* sb = sa + C::A_U4;
+    i32x8 af[2][MI], bfr[2][NI];
+    auto frags = [&](int ks, i32x8 (&xa)[MI], i32x8 (&xb)[NI]) {
+      const int c0 = ks * 4 + (lane >> 5) * 2;
+#pragma unroll
+      for (int a = 0; a < MI; ++a) {
+        const int row = wm * (BM / WM) + a * 32 + (lane & 31);
+        const uint4 lo = sa[swz16(row, c0)], hi = sa[swz16(row, c0 + 1)];
+        xa[a] = i32x8{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+      }
+#pragma unroll
+      for (int b = 0; b < NI; ++b) {
+        const int row = wrow(b);
+        const uint4 lo = sb[swz16(row, c0)], hi = sb[swz16(row, c0 + 1)];
+        xb[b] = i32x8{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+      }
+    };
+    frags(0, af[0], bfr[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    between();
+    frags(1, af[1], bfr[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    float sact[MI], swt[NI];
+#pragma unroll
+    for (int a = 0; a < MI; ++a) sact[a] = sa_l[(wm * (BM / WM) + a * 32 + (lane & 31)) * SMAX + kt];
+#pragma unroll
+    for (int b = 0; b < NI; ++b) swt[b] = sw_l[(GATEUP ? b : swb0) * SMAX + kt];
+#pragma unroll
+    for (int a = 0; a < MI; ++a)
+#pragma unroll
+      for (int b = 0; b < NI; ++b) {
+        f32x16 sl;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sl[r] = 0.f;
+        sl = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[0][b], af[0][a], sl, 0, 0, 0, 127, 0, 127);
+        sl = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[1][b], af[1][a], sl, 0, 0, 0, 127, 0, 127);
+        const float s = sact[a] * swt[b];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[a][b][r] = fmaf(sl[r], s, acc[a][b][r]);
+      }
+  };
+  __syncthreads();   // scales staged
+#define MOE_F8_STEP(KT, SLOT, NSLOT)                                        \
+  {                                                                         \
+    if ((KT) + 1 < nk) wait_vm_lgkm0<L>(); else wait_vm_lgkm0<0>();         \
+    block_sync_nowait();                                                    \
+    compute(SLOT, KT, [&] { if ((KT) + 2 < nk) issue((KT) + 2, NSLOT); });  \
+  }
+  for (int kt = 0; kt < nk; kt += 3) {
+    MOE_F8_STEP(kt, 0, 2)
+    if (kt + 1 < nk) MOE_F8_STEP(kt + 1, 1, 0)
+    if (kt + 2 < nk) MOE_F8_STEP(kt + 2, 2, 1)
+  }
+#undef MOE_F8_STEP
+
+  // Epilogue.  Accumulator register r of block (a, b) holds weight row (output
+  // column) 8(r/4) + 4(lane/32) + r%4 of the block for activation row lane%32:
+  // four consecutive columns per register group.
+  __syncthreads();   // every wave is done with the ring; it becomes staging space
+  const int rows = min(BM, cnt - m0);
+  if (GATEUP) {
+    // h = silu(g) * u, its row amax over the tile's 128 columns (registers, the
+    // lane 32 apart, then the four waves of the row block through LDS), scale =
+    // amax / 448 (1 for an all-zero block), codes = e4m3(h / scale)
+    float* red = reinterpret_cast<float*>(smem + 2048);       // [WM][MI][32][WN]
+    uint8_t* stg = reinterpret_cast<uint8_t*>(smem);          // [BM][128] codes
+    float hv[MI][16];
+    float am[MI];
+#pragma unroll
+    for (int a = 0; a < MI; ++a) {
+      float m = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        hv[a][r] = silu(acc[a][0][r]) * acc[a][1][r];
+        m = fmaxf(m, fabsf(hv[a][r]));
+      }
+      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      am[a] = m;
+      if (lane < 32) red[((wm * MI + a) * 32 + lane) * WN + wn] = m;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int a = 0; a < MI; ++a) {
+      const float* rr = red + ((wm * MI + a) * 32 + (lane & 31)) * WN;
+      float m = rr[0];
+#pragma unroll
+      for (int j = 1; j < WN; ++j) m = fmaxf(m, rr[j]);
+      const float scale = m > 0.f ? m / 448.0f : 1.0f;
+      const int row = wm * (BM / WM) + a * 32 + (lane & 31);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint32_t pk = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pk |= f32_to_e4m3(hv[a][4 * g + i] / scale) << (8 * i);
+        const int col = wn * (BN / 2 / WN) + 8 * g + 4 * (lane >> 5);
+        *reinterpret_cast<uint32_t*>(stg + row * 128 + col) = pk;
+      }
+      if (wn == 0 && lane < 32 && row < rows)
+        p.qscale[int64_t(base + m0 + row) * (p.N / 128) + ct] = scale;
+    }
+    (void)am;
+    __syncthreads();
+    for (int i = tid; i < rows * 8; i += NT) {
+      const int row = i >> 3, c = i & 7;
+      *reinterpret_cast<uint4*>(p.qout + int64_t(base + m0 + row) * p.N + ct * 128 + c * 16) =
+          *reinterpret_cast<const uint4*>(stg + row * 128 + c * 16);
+    }
+    return;
+  }
+  if (p.out32) {
+#pragma unroll
+    for (int a = 0; a < MI; ++a) {
+      const int row = wm * (BM / WM) + a * 32 + (lane & 31);
+      if (row >= rows) continue;
+#pragma unroll
+      for (int b = 0; b < NI; ++b)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = ct * BN + wn * (BN / WN) + b * 32 + 8 * g + 4 * (lane >> 5);
+          *reinterpret_cast<float4*>(p.out32 + int64_t(base + m0 + row) * p.N + col) =
+              make_float4(acc[a][b][4 * g], acc[a][b][4 * g + 1], acc[a][b][4 * g + 2], acc[a][b][4 * g + 3]);
+        }
+    }
+    return;
+  }
+  // weighted bf16 rows through LDS: each register group is 4 consecutive columns
+  constexpr int LS = BN + 8;
+  bf16_t* stg = reinterpret_cast<bf16_t*>(smem);
+#pragma unroll
+  for (int a = 0; a < MI; ++a) {
+    const int row = wm * (BM / WM) + a * 32 + (lane & 31);
+    const float wr = row < rows ? p.row_w[base + m0 + row] : 0.f;
+#pragma unroll
+    for (int b = 0; b < NI; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = wn * (BN / WN) + b * 32 + 8 * g + 4 * (lane >> 5);
+        uint2 pk;
+        pk.x = uint32_t(f32_to_bf16(acc[a][b][4 * g] * wr)) | (uint32_t(f32_to_bf16(acc[a][b][4 * g + 1] * wr)) << 16);
+        pk.y = uint32_t(f32_to_bf16(acc[a][b][4 * g + 2] * wr)) | (uint32_t(f32_to_bf16(acc[a][b][4 * g + 3] * wr)) << 16);
+        *reinterpret_cast<uint2*>(stg + row * LS + col) = pk;
+      }
+  }
+  __syncthreads();
+  for (int i = tid; i < rows * (BN / 8); i += NT) {
+    const int row = i / (BN / 8), c = i - row * (BN / 8);
+    *reinterpret_cast<uint4*>(p.out16 + int64_t(base + m0 + row) * p.N + ct * BN + c * 8) =
+        *reinterpret_cast<const uint4*>(stg + row * LS + c * 8);
+  }
+}
+
+// shapes the pipelined fp8 kernels cover
+static bool fp8_pipelined_ok(const Plan& p) {
+  return p.wt == MOE_E4M3_B128 && p.I % 128 == 0 && p.H % Fp8Tile::BN == 0 &&
+         p.H / 128 <= Fp8Tile::SMAX && p.I / 128 <= Fp8Tile::SMAX;
+}
+
 template <typename TI>
 __global__ __launch_bounds__(256) void k_quant_e4m3(const TI* __restrict__ in, int64_t rows, int K,
                                                     uint8_t* __restrict__ codes,
@@ -688,7 +970,7 @@ __global__ __launch_bounds__(256) void k_quant_e4m3(const TI* __restrict__ in, i
 int launch_gateup_mfma(const Plan& p, const void* x, const int32_t* row_token,
                        const int32_t* offsets, const int2* tiles, const int32_t* meta,
                        const moe_weights* w, void* h, const uint8_t* xq, const float* sx,
-                       hipStream_t st) {
+                       uint8_t* hq, float* shq, hipStream_t st) {
   const unsigned grid = xcd_grid(p.max_tiles * (p.I / 64));
   if (p.wt == MOE_BF16) {
     GemmBf16Args a{};
@@ -707,8 +989,15 @@ int launch_gateup_mfma(const Plan& p, const void* x, const int32_t* row_token,
     a.meta = meta; a.w0 = (const uint8_t*)w->w_gate; a.w1 = (const uint8_t*)w->w_up;
     a.sh0 = (const uint8_t*)w->sh_gate; a.sh1 = (const uint8_t*)w->sh_up;
     a.s0 = w->s_gate; a.s1 = w->s_up; a.shs0 = w->sh_s_gate; a.shs1 = w->sh_s_up;
-    a.hout = (float*)h; a.K = p.H; a.N = p.I; a.E = p.E;
+    a.hout = (float*)h; a.qout = hq; a.qscale = shq; a.K = p.H; a.N = p.I; a.E = p.E;
+    if (fp8_pipelined_ok(p)) {
+      launch_kernel(p, kTimeGateUp, k_gemm_fp8_v2<true>,
+                    dim3(xcd_grid(p.max_tiles * (p.I / (Fp8Tile::BN / 2)))), dim3(Fp8Tile::NT), 0, st, a);
+      return check_launch();
+    }
     launch_kernel(p, kTimeGateUp, k_gemm_fp8<true>, dim3(grid), dim3(256), 0, st, a);
+    MOE_TRY(check_launch());
+    return launch_quant(p, h, false, p.R, p.I, hq, shq, st);
   }
   return check_launch();
 }
@@ -733,7 +1022,11 @@ int launch_down_mfma(const Plan& p, const void* h, const int32_t* offsets, const
     a.meta = meta; a.w0 = (const uint8_t*)w->w_down; a.sh0 = (const uint8_t*)w->sh_down;
     a.s0 = w->s_down; a.shs0 = w->sh_s_down; a.row_w = row_w; a.out16 = out16; a.out32 = out32;
     a.K = p.I; a.N = p.H; a.E = p.E;
-    launch_kernel(p, kTimeDown, k_gemm_fp8<false>, dim3(grid), dim3(256), 0, st, a);
+    if (fp8_pipelined_ok(p))
+      launch_kernel(p, kTimeDown, k_gemm_fp8_v2<false>,
+                    dim3(xcd_grid(p.max_tiles * (p.H / Fp8Tile::BN))), dim3(Fp8Tile::NT), 0, st, a);
+    else
+      launch_kernel(p, kTimeDown, k_gemm_fp8<false>, dim3(grid), dim3(256), 0, st, a);
   }
   return check_launch();
 }

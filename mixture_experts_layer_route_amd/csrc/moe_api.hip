@@ -120,7 +120,8 @@ static int run_experts(const Plan& p, const void* x, const int32_t* off, const i
   }
   if (p.wt == MOE_BF16) {
     bf16_t* h = at<bf16_t>(ws, p.o_h);
-    MOE_TRY(launch_gateup_mfma(p, x, rowtok, off, tiles, meta, w, h, nullptr, nullptr, st));
+    MOE_TRY(launch_gateup_mfma(p, x, rowtok, off, tiles, meta, w, h, nullptr, nullptr, nullptr,
+                               nullptr, st));
     return launch_down_mfma(p, h, off, tiles, meta, w, row_w, y_perm32, y_perm16, nullptr, st);
   }
   uint8_t* xq = at<uint8_t>(ws, p.o_xq);
@@ -129,8 +130,7 @@ static int run_experts(const Plan& p, const void* x, const int32_t* off, const i
   float* shq = at<float>(ws, p.o_shq);
   float* h = at<float>(ws, p.o_h);
   MOE_TRY(launch_quant(p, x, true, p.T, p.H, xq, sx, st));
-  MOE_TRY(launch_gateup_mfma(p, x, rowtok, off, tiles, meta, w, h, xq, sx, st));
-  MOE_TRY(launch_quant(p, h, false, p.R, p.I, hq, shq, st));
+  MOE_TRY(launch_gateup_mfma(p, x, rowtok, off, tiles, meta, w, h, xq, sx, hq, shq, st));
   return launch_down_mfma(p, hq, off, tiles, meta, w, row_w, y_perm32, y_perm16, shq, st);
 }
 
@@ -242,7 +242,8 @@ static int forward_impl(const moe_config* cfg, const void* x, const moe_weights*
   bf16_t* ypw = at<bf16_t>(ws, p.o_ypw);
   if (p.wt == MOE_BF16) {
     bf16_t* h = at<bf16_t>(ws, p.o_h);
-    MOE_TRY(launch_gateup_mfma(p, x, rowtok, off, tiles, meta, w, h, nullptr, nullptr, stream));
+    MOE_TRY(launch_gateup_mfma(p, x, rowtok, off, tiles, meta, w, h, nullptr, nullptr, nullptr,
+                               nullptr, stream));
     MOE_TRY(launch_down_mfma(p, h, off, tiles, meta, w, row_w, nullptr, ypw, nullptr, stream));
   } else {
     uint8_t* xq = at<uint8_t>(ws, p.o_xq);
@@ -251,8 +252,7 @@ static int forward_impl(const moe_config* cfg, const void* x, const moe_weights*
     float* shq = at<float>(ws, p.o_shq);
     float* h = at<float>(ws, p.o_h);
     MOE_TRY(launch_quant(p, x, true, p.T, p.H, xq, sx, stream));
-    MOE_TRY(launch_gateup_mfma(p, x, rowtok, off, tiles, meta, w, h, xq, sx, stream));
-    MOE_TRY(launch_quant(p, h, false, p.R, p.I, hq, shq, stream));
+    MOE_TRY(launch_gateup_mfma(p, x, rowtok, off, tiles, meta, w, h, xq, sx, hq, shq, stream));
     MOE_TRY(launch_down_mfma(p, hq, off, tiles, meta, w, row_w, nullptr, ypw, shq, stream));
   }
   return launch_combine_preweighted(p, ypw, off, inv, y, stream);

@@ -92,7 +92,7 @@ int launch_down_combine_skinny(const Plan& p, const float* h, const int32_t* ids
 int launch_gateup_mfma(const Plan& p, const void* x, const int32_t* row_token,
                        const int32_t* offsets, const int2* tiles, const int32_t* meta,
                        const moe_weights* w, void* h, const uint8_t* xq, const float* sx,
-                       hipStream_t st);
+                       uint8_t* hq, float* shq, hipStream_t st);
 int launch_down_mfma(const Plan& p, const void* h, const int32_t* offsets, const int2* tiles,
                      const int32_t* meta, const moe_weights* w, const float* row_w, float* out32,
                      bf16_t* out16, const float* sh_scale, hipStream_t st);
