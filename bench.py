@@ -221,8 +221,11 @@ def main():
     end.record()
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / K
-    kern_ms = {"gateup": float(np.mean([r[0].elapsed_time(r[1]) for r in ev.values()])),
-               "down": float(np.mean([r[2].elapsed_time(r[3]) for r in ev.values()]))}
+    samples = {"gateup": [r[0].elapsed_time(r[1]) for r in ev.values()],
+               "down": [r[2].elapsed_time(r[3]) for r in ev.values()]}
+    kern_ms = {n: float(np.mean(v)) for n, v in samples.items()}
+    kern_pct = {n: [round(float(np.percentile(v, q)) * 1e3, 2) for q in (10, 50, 90)]
+                for n, v in samples.items()}
     # the same steps with no events at all
     start.record()
     for i in range(K):
@@ -246,6 +249,7 @@ def main():
                    "E": shape.E, "G": shape.G, "Gk": shape.Gk, "k": shape.k, "S": shape.S,
                    "weight_sets": nsets, "touched_experts": U},
         "kernel_us": {n: round(v * 1e3, 2) for n, v in kern_ms.items()},
+        "kernel_us_p10_p50_p90": kern_pct,
         "kernel_events_on_steps": f"every {every}th ({len(timed)} of {K})",
         "ms_per_step_without_kernel_events": round(ms_plain, 5),
         "parity_rel_l2": float(f"{err:.3e}"),
