@@ -43,7 +43,9 @@ struct DecodeArgs {
   int T, H, I, E, S, G, Gk, k;
 };
 
-template <typename TA, typename TW, int NS, int QMAX>
+// SEL > 0: a wave per token (select_token_wave<SEL>); SEL < 0: sixteen lanes per
+// token, four tokens per wave (select_token_row<-SEL>)
+template <typename TA, typename TW, int NS, int SEL>
 __global__ __launch_bounds__(256) void k_decode_gateup(DecodeArgs a) {
   constexpr int NI = 2;            // gate/up weight rows per item
   extern __shared__ __align__(16) unsigned char lds_raw[];
@@ -83,8 +85,34 @@ __global__ __launch_bounds__(256) void k_decode_gateup(DecodeArgs a) {
   const int nch = T * H / CH;
   for (int c0 = wv * 64; c0 < nch; c0 += 256)
     if (c0 + lane < nch) dma16(x + int64_t(c0 + lane) * CH, xs + int64_t(c0) * CH);
-  for (int t = wv; t < T; t += 4)
-    select_token_wave<QMAX>(a.logits + int64_t(t) * E, E, a.G, a.Gk, k, ids_l + t * k, w_l + t * k);
+  if constexpr (SEL < 0) {
+    constexpr int V = -SEL;
+    const int t = wv * 4 + (lane >> 4), r16 = lane & 15;
+    if (wv * 4 < T) {                                  // uniform over the wave
+      const float* l = a.logits + int64_t(min(t, T - 1)) * E + V * r16;
+      float lv[V];
+      if constexpr (V % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < V; i += 4) {
+          const float4 q = *reinterpret_cast<const float4*>(l + i);
+          lv[i] = q.x; lv[i + 1] = q.y; lv[i + 2] = q.z; lv[i + 3] = q.w;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i) lv[i] = l[i];
+      }
+      int id;
+      float wt;
+      select_token_row<V>(lv, E, a.G, a.Gk, k, id, wt);
+      if (t < T && r16 < k) {
+        ids_l[t * k + r16] = id;
+        w_l[t * k + r16] = wt;
+      }
+    }
+  } else {
+    for (int t = wv; t < T; t += 4)
+      select_token_wave<SEL>(a.logits + int64_t(t) * E, E, a.G, a.Gk, k, ids_l + t * k, w_l + t * k);
+  }
   wait_vm_lgkm0<0>();
   __syncthreads();
   if (threadIdx.x < nslot) atomicOr(&bits_l[wv * E + ids_l[threadIdx.x]], 1ull << lane);
@@ -357,8 +385,15 @@ int launch_decode_ffn(const Plan& p, const void* x, const float* logits, const m
   a.h = h; a.y = y;
   a.T = int(p.T); a.H = p.H; a.I = p.I; a.E = p.E; a.S = p.S; a.G = p.G; a.Gk = p.Gk; a.k = p.k;
   const int ns = (p.H + 511) / 512, nsd = (p.I + 511) / 512;
+  const bool rows = select_rows_ok(p);
 #define MOE_DQ(TA, TW, NSV, NSDV)                                            \
   {                                                                          \
+    if (rows) {                                                              \
+      if (p.E == 128) return launch_decode_t<TA, TW, NSV, NSDV, -8>(p, a, st);  \
+      if (p.E == 256) return launch_decode_t<TA, TW, NSV, NSDV, -16>(p, a, st); \
+      if (p.E == 64) return launch_decode_t<TA, TW, NSV, NSDV, -4>(p, a, st);   \
+      if (p.E == 16) return launch_decode_t<TA, TW, NSV, NSDV, -1>(p, a, st);   \
+    }                                                                        \
     if (p.E <= 64) return launch_decode_t<TA, TW, NSV, NSDV, 1>(p, a, st);   \
     if (p.E <= 128) return launch_decode_t<TA, TW, NSV, NSDV, 2>(p, a, st);  \
     if (p.E <= 256) return launch_decode_t<TA, TW, NSV, NSDV, 4>(p, a, st);  \

@@ -75,6 +75,8 @@ int launch_route_permute_small(const Plan& p, const float* logits, int32_t* ids,
                                int32_t* row_token, int32_t* inv, float* row_w, int BM,
                                hipStream_t st);
 bool decode_ffn_ok(const Plan& p);
+// the sixteen-lanes-per-token selection covers this shape
+bool select_rows_ok(const Plan& p);
 // M rows per tile the matrix-core expert kernels use for this plan
 int gemm_tile_rows(const Plan& p);
 // Decode path: gate/up (with in-kernel routing) then down + combine.

@@ -283,7 +283,7 @@ __global__ __launch_bounds__(1024) void k_select_rows(const float* __restrict__ 
 
 // the row selection covers E = 16 V (V <= 16) with groups spanning a power-of-two
 // number of lanes, or whole groups inside a lane
-static bool select_rows_ok(const Plan& p) {
+bool select_rows_ok(const Plan& p) {
   if (p.E % 16 || p.E > 256 || p.k > 16) return false;
   const int V = p.E / 16, n = p.E / p.G;
   if (p.G == 1) return true;
