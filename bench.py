@@ -31,6 +31,7 @@ BF16_PEAK_TFLOPS = 2516.6        # MI355X dense bf16 MFMA
 FP8_PEAK_TFLOPS = 5033.2         # MI355X dense fp8 MFMA
 WEIGHT_KEYS = ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down", "sh_gate", "sh_up",
                "sh_down", "sh_s_gate", "sh_s_up", "sh_s_down")
+NV_KEYS = ("b_gate", "b_up", "b_down", "g_gate", "g_up", "g_down")
 DEFAULT_SETS = {"tiny": 1, "decode": 8, "prefill": 2, "fp8": 4, "inkling": 1}
 
 
@@ -119,6 +120,16 @@ def kernel_roofline(shape, which, ms, U):
             "per_launch": f"{abytes} B = {U} touched experts x {per_expert} B of weights"}
 
 
+def oracle_experts(mo, cpu, f):
+    """The oracle's expert set over the synthetic layer's stored weights."""
+    nv = sh_nv = None
+    if cpu.get("b_gate") is not None:
+        nv = tuple(f(cpu[n]) for n in NV_KEYS)
+        if cpu.get("sh_b_gate") is not None:
+            sh_nv = tuple(f(cpu["sh_" + n]) for n in NV_KEYS)
+    return mo.Experts(*(f(cpu[n]) for n in WEIGHT_KEYS), nv=nv, sh_nv=sh_nv)
+
+
 def cpu_baseline(shape, cpu, budget_s):
     """The float64 oracle, as it stands, on a bounded sample of the same workload."""
     from oracle import moe_oracle as mo
@@ -128,7 +139,7 @@ def cpu_baseline(shape, cpu, budget_s):
     except Exception:  # pragma: no cover
         threads = os.cpu_count()
     f = lambda t: None if t is None else (t.numpy() if t.dtype.itemsize == 1 else t.float().numpy())
-    ex = mo.Experts(*(f(cpu[n]) for n in WEIGHT_KEYS))
+    ex = oracle_experts(mo, cpu, f)
     x, wr, b = f(cpu["x"]), f(cpu["w_router"]), f(cpu["router_bias"])
     n_tok = min(shape.T, 64)
     xs = x[:n_tok]
@@ -169,7 +180,8 @@ def main():
     dev = {k: (None if v is None else v.cuda()) for k, v in cpu.items()}
     sets = [dev]
     for _ in range(nsets - 1):
-        sets.append({k: (v.clone() if (k in WEIGHT_KEYS and v is not None) else v)
+        sets.append({k: (v.clone() if (k in WEIGHT_KEYS + NV_KEYS or k.startswith("sh_"))
+                         and v is not None else v)
                      for k, v in dev.items()})
     wsts = [moe.weights_struct(s) for s in sets]
     cfg = moe.make_config(shape.T, shape.H, shape.I, shape.E, shape.G, shape.Gk, shape.k,
@@ -189,7 +201,7 @@ def main():
     sample = np.arange(shape.T) if shape.T <= 16 else np.unique(
         np.concatenate([[0, shape.T - 1], rng.choice(shape.T, 14, replace=False)]))
     f = lambda t: None if t is None else (t.numpy() if t.dtype.itemsize == 1 else t.float().numpy())
-    ex = mo.Experts(*(f(cpu[n]) for n in WEIGHT_KEYS))
+    ex = oracle_experts(mo, cpu, f)
     l64 = mo.router_logits(f(cpu["x"]), f(cpu["w_router"]), f(cpu["router_bias"]))
     w64 = mo.renormalise(mo.gate_scores(l64[sample]), g_ids[sample])
     ref = mo.forward_tokenmajor(f(cpu["x"])[sample], ex, g_ids[sample], w64)

@@ -34,6 +34,13 @@ plainest the rest supports):
       per token per 128 along K: scale = fp32(amax) / 448 (fp32 division),
       code = e4m3 round-to-nearest-even of fp32(v / scale), saturating at 448;
       an all-zero block gets scale 1.
+  R10 NVFP4 experts (the 4-bit format TensorFold #1247 names for #874, list "What
+      it does not cover"; its layout is not on the pages) are FP4 E2M1 codes
+      (sign, 2 exponent bits with bias 1, 1 mantissa bit, no inf/NaN), two per byte
+      with element 2i in the low nibble, one E4M3 scale per 16 consecutive
+      elements along the input dimension and one fp32 scale per expert matrix:
+      weight = e2m1(code) * e4m3(block scale) * matrix scale.  Activations stay
+      in their own type (no activation quantisation).
 
 Every floating-point step runs in float64 except the FP8 scale/code decisions
 of R9, which are taken in fp32 as the kernels take them.
@@ -228,27 +235,67 @@ def dequant_blocks(codes, scales, block: int = FP8_BLOCK) -> np.ndarray:
     return vals * sc
 
 
+# --------------------------------------------------------------------------- NVFP4 (R10)
+NVFP4_BLOCK = 16
+
+
+def e2m1_values() -> np.ndarray:
+    """Value of each of the 16 FP4 E2M1 codes: sign bit 3, exponent bits 2..1 (bias 1),
+    mantissa bit 0; exponent field 0 is subnormal m * 0.5."""
+    vals = np.empty(16, dtype=np.float64)
+    for c in range(16):
+        sign = -1.0 if c & 0x8 else 1.0
+        ex = (c >> 1) & 0x3
+        man = c & 0x1
+        vals[c] = sign * (man * 0.5 if ex == 0 else (1.0 + 0.5 * man) * 2.0 ** (ex - 1))
+    return vals
+
+
+def nvfp4_unpack(packed) -> np.ndarray:
+    """[..., K/2] bytes -> [..., K] codes: element 2i in the low nibble, 2i+1 in the high."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = p & 0xF
+    out[..., 1::2] = p >> 4
+    return out
+
+
+def dequant_nvfp4(packed, block_scales, matrix_scale) -> np.ndarray:
+    """[rows, K/2] packed E2M1 codes, [rows, K/16] E4M3 block scales and the fp32 scale
+    of the matrix -> float64 [rows, K] weights (reading R10)."""
+    vals = e2m1_values()[nvfp4_unpack(packed)]
+    sc = np.repeat(e4m3_decode(block_scales), NVFP4_BLOCK, axis=-1)
+    return vals * sc * float(matrix_scale)
+
+
 # --------------------------------------------------------------------------- experts
 class Experts:
     """Routed and shared expert weights, decoded to float64 one expert at a time.
 
     Dense weights: w_gate, w_up [E, I, H], w_down [E, H, I] (any float array holding the
     exact stored values).  FP8 weights: uint8 e4m3 codes plus s_gate, s_up [E, I/128, H/128]
-    and s_down [E, H/128, I/128] fp32 scales.  Shared experts: sh_* arrays of the same form.
+    and s_down [E, H/128, I/128] fp32 scales.  NVFP4 weights: packed E2M1 codes
+    [E, rows, K/2] with `nv` = (b_gate, b_up, b_down, g_gate, g_up, g_down): E4M3 block
+    scales [E, rows, K/16] and fp32 matrix scales [E].  Shared experts: sh_* arrays of the
+    same form (`sh_nv` for NVFP4).  Only FP8 quantises activations.
     """
 
     def __init__(self, w_gate, w_up, w_down, s_gate=None, s_up=None, s_down=None,
                  sh_gate=None, sh_up=None, sh_down=None, sh_s_gate=None, sh_s_up=None,
-                 sh_s_down=None):
+                 sh_s_down=None, nv=None, sh_nv=None):
         self.fp8 = s_gate is not None
-        self.routed = (w_gate, w_up, w_down, s_gate, s_up, s_down)
-        self.shared = (sh_gate, sh_up, sh_down, sh_s_gate, sh_s_up, sh_s_down)
+        self.routed = (w_gate, w_up, w_down, s_gate, s_up, s_down, nv)
+        self.shared = (sh_gate, sh_up, sh_down, sh_s_gate, sh_s_up, sh_s_down, sh_nv)
         self.E = len(w_gate)
         self.S = 0 if sh_gate is None else len(sh_gate)
 
     @staticmethod
     def _decode(pack, e):
-        wg, wu, wd, sg, su, sd = pack
+        wg, wu, wd, sg, su, sd, nv = pack
+        if nv is not None:
+            bg, bu, bd, gg, gu, gd = nv
+            return (dequant_nvfp4(wg[e], bg[e], gg[e]), dequant_nvfp4(wu[e], bu[e], gu[e]),
+                    dequant_nvfp4(wd[e], bd[e], gd[e]))
         if sg is None:
             return _f64(wg[e]), _f64(wu[e]), _f64(wd[e])
         return (dequant_blocks(wg[e], sg[e]), dequant_blocks(wu[e], su[e]),

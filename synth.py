@@ -14,6 +14,8 @@ Shapes and value distributions follow the five workloads of the layer:
   prefill   T=8192, same layer as decode, router bias ~N(0, 0.5) (skewed load)
   fp8       T=2048, same layer, experts e4m3 with one fp32 scale per 128x128
   inkling   T=4096, H=2048, I=512, E=256 ungrouped, k=6, 2 shared experts
+  decode_nvfp4  the decode layer with NVFP4 experts (4-bit E2M1 codes, an E4M3
+            scale per 16 inputs, an fp32 scale per expert matrix)
 
 The Ling-3.0-tiny layer shape (128 routed experts split into 8 groups of 16,
 of which 4 groups survive per token; hidden size 1536; SwiGLU experts) comes
@@ -27,7 +29,7 @@ Inkling architecture".  The intermediate size 512 and the hidden size
 Draw order (numpy PCG64, ``default_rng(seed)``), every tensor drawn in float32:
   x; router weight; router bias (prefill only); then for each expert
   e = 0..E+S-1: gate, up, down (for fp8 each tensor is followed by its
-  per-block scale factors u ~ U(0.5, 2)).
+  per-block scale factors u ~ U(0.5, 2); NVFP4 draws nothing extra).
 """
 from __future__ import annotations
 
@@ -37,7 +39,7 @@ from typing import Optional
 import numpy as np
 import torch
 
-F32, BF16, E4M3 = "f32", "bf16", "e4m3"
+F32, BF16, E4M3, NVFP4 = "f32", "bf16", "e4m3", "nvfp4"
 
 
 @dataclasses.dataclass(frozen=True)
@@ -53,7 +55,7 @@ class LayerShape:
     k: int                 # experts per token
     S: int                 # always-on shared experts
     act: str               # element type of x, router weight and y: f32 | bf16
-    wt: str                # element type of the experts: f32 | bf16 | e4m3
+    wt: str                # element type of the experts: f32 | bf16 | e4m3 | nvfp4
     x_dist: str            # "normal" or "rms" (RMS-normalised N(0,1))
     bias_std: float        # std of the per-expert router bias, 0 = no bias
     seed: int
@@ -75,6 +77,8 @@ WORKLOADS = {
                       act=BF16, wt=E4M3, x_dist="rms", bias_std=0.0, seed=3),
     "inkling": LayerShape("inkling", T=4096, H=2048, I=512, E=256, G=1, Gk=1, k=6, S=2,
                           act=BF16, wt=BF16, x_dist="normal", bias_std=0.0, seed=4),
+    "decode_nvfp4": LayerShape("decode_nvfp4", T=4, H=1536, I=512, E=128, G=8, Gk=4, k=8,
+                               S=0, act=BF16, wt=NVFP4, x_dist="rms", bias_std=0.0, seed=5),
 }
 
 FP8_BLOCK = 128
@@ -111,13 +115,53 @@ def _encode_blocks(rng: np.random.Generator, w: np.ndarray):
     return codes, torch.from_numpy(s)
 
 
+NVFP4_BLOCK = 16
+E2M1_MAG = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float32)
+E2M1_MID = (E2M1_MAG[:-1] + E2M1_MAG[1:]) / 2          # rounding thresholds
+
+
+def _encode_nvfp4(w: np.ndarray):
+    """Store expert matrices [n, rows, K] as NVFP4: packed E2M1 codes [n, rows, K/2]
+    (element 2i in the low nibble), E4M3 block scales [n, rows, K/16] and one fp32 scale
+    per matrix [n].
+
+    matrix scale g = amax / (6 * 448); block scale = e4m3(amax_block / (6 g)) (torch's
+    round-to-nearest-even cast); code = nearest E2M1 value of w / (block scale * g), ties
+    to the even code, saturating at 6.  The stored triple is the weight for every
+    consumer.
+    """
+    n, rows, K = w.shape
+    amax = np.abs(w).reshape(n, -1).max(axis=1)
+    g = np.where(amax > 0, amax / (6.0 * E4M3_MAX), 1.0).astype(np.float32)
+    blocks = w.reshape(n, rows, K // NVFP4_BLOCK, NVFP4_BLOCK)
+    bs = (np.abs(blocks).max(axis=3) / (np.float32(6.0) * g[:, None, None])).astype(np.float32)
+    bs = np.clip(bs, 0.0, E4M3_MAX)
+    bcode = torch.from_numpy(bs).to(torch.float8_e4m3fn)
+    den = (bcode.to(torch.float32).numpy() * g[:, None, None]).astype(np.float32)
+    safe = np.where(den > 0, den, np.float32(1.0))
+    q = (blocks / safe[..., None]).astype(np.float32)
+    q[np.broadcast_to((den <= 0)[..., None], q.shape)] = 0.0
+    q = q.reshape(n, rows, K)
+    a = np.minimum(np.abs(q), np.float32(6.0))
+    idx = np.zeros(a.shape, dtype=np.uint8)
+    for m in E2M1_MID:                                # number of thresholds strictly below a
+        idx += a > m
+    last = E2M1_MID.size - 1
+    idx += (idx <= last) & (a == E2M1_MID[np.minimum(idx, last)]) & (idx % 2 == 1)   # ties: even code
+    codes = (idx | np.where(np.signbit(q), 8, 0)).astype(np.uint8)
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    return torch.from_numpy(packed), bcode.view(torch.uint8), torch.from_numpy(g)
+
+
 def make_layer(shape: LayerShape) -> dict:
     """Draw one layer's inputs.  Returns CPU tensors keyed by argument name.
 
     Keys: x [T,H]; w_router [E,H]; router_bias [E] fp32 or None; w_gate, w_up [E,I,H];
-    w_down [E,H,I]; s_gate, s_up [E,I/128,H/128] and s_down [E,H/128,I/128]
-    (fp8 only, else None); sh_gate, sh_up, sh_down (+ sh_s_*) for the S shared
-    experts, or None when S == 0.
+    w_down [E,H,I] (NVFP4: packed bytes [E,I,H/2] and [E,H,I/2]); s_gate, s_up
+    [E,I/128,H/128] and s_down [E,H/128,I/128] (fp8 only, else None); b_gate, b_up
+    [E,I,H/16], b_down [E,H,I/16] E4M3 block scales and g_gate, g_up, g_down [E] fp32
+    matrix scales (NVFP4 only, else None); sh_* the same for the S shared experts, or
+    None when S == 0.
     """
     rng = np.random.default_rng(shape.seed)
     T, H, I, E, S = shape.T, shape.H, shape.I, shape.E, shape.S
@@ -133,9 +177,10 @@ def make_layer(shape: LayerShape) -> dict:
     if shape.bias_std > 0:
         bias = torch.from_numpy(rng.standard_normal(E, dtype=np.float32) * np.float32(shape.bias_std))
 
-    fp8 = shape.wt == E4M3
+    fp8, nv = shape.wt == E4M3, shape.wt == NVFP4
     mats = {n: [] for n in ("gate", "up", "down")}
     scales = {n: [] for n in ("gate", "up", "down")}
+    gscales = {n: [] for n in ("gate", "up", "down")}
     for _e in range(E + S):
         for name, dims in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I))):
             w = rng.standard_normal(dims, dtype=np.float32) * np.float32(shape.expert_std)
@@ -143,9 +188,15 @@ def make_layer(shape: LayerShape) -> dict:
                 c, s = _encode_blocks(rng, w)
                 mats[name].append(c)
                 scales[name].append(s)
+            elif nv:
+                mats[name].append(w)             # encoded below, all experts at once
             else:
                 mats[name].append(_store(w, shape.wt))
 
+    if nv:
+        for name in ("gate", "up", "down"):
+            c, b, g = _encode_nvfp4(np.stack(mats[name]))
+            mats[name], scales[name], gscales[name] = list(c), list(b), list(g)
     out = {"x": x, "w_router": w_router, "router_bias": bias}
     for name in ("gate", "up", "down"):
         out["w_" + name] = torch.stack(mats[name][:E])
@@ -156,4 +207,12 @@ def make_layer(shape: LayerShape) -> dict:
         else:
             out["s_" + name] = None
             out["sh_s_" + name] = None
+        if nv:
+            out["b_" + name] = torch.stack(scales[name][:E])
+            out["sh_b_" + name] = torch.stack(scales[name][E:]) if S else None
+            out["g_" + name] = torch.stack(gscales[name][:E])
+            out["sh_g_" + name] = torch.stack(gscales[name][E:]) if S else None
+        else:
+            for key in ("b_", "sh_b_", "g_", "sh_g_"):
+                out[key + name] = None
     return out

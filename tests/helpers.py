@@ -9,11 +9,12 @@ from oracle import moe_oracle as mo
 import synth
 
 NEAR_TIE = 1e-4          # float64 logit margin below which either routing is acceptable
-TOL = {"f32": 5e-3, "bf16": 5e-3, "e4m3": 2e-2}   # rel L2 bounds of the layer output
+TOL = {"f32": 5e-3, "bf16": 5e-3, "e4m3": 2e-2, "nvfp4": 5e-3}   # rel L2 bounds of the layer output
 TOL_F32_INTERNAL = 1e-5  # fp32 layers must also be this close (no silent bf16 downcast)
 
 WEIGHT_KEYS = ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down", "sh_gate", "sh_up",
                "sh_down", "sh_s_gate", "sh_s_up", "sh_s_down")
+NV_KEYS = ("b_gate", "b_up", "b_down", "g_gate", "g_up", "g_down")
 
 
 def np_exact(t):
@@ -26,7 +27,12 @@ def np_exact(t):
 
 
 def oracle_experts(layer) -> mo.Experts:
-    return mo.Experts(*(np_exact(layer[n]) for n in WEIGHT_KEYS))
+    nv = sh_nv = None
+    if layer.get("b_gate") is not None:
+        nv = tuple(np_exact(layer[n]) for n in NV_KEYS)
+        if layer.get("sh_b_gate") is not None:
+            sh_nv = tuple(np_exact(layer["sh_" + n]) for n in NV_KEYS)
+    return mo.Experts(*(np_exact(layer[n]) for n in WEIGHT_KEYS), nv=nv, sh_nv=sh_nv)
 
 
 def to_device(layer, device="cuda") -> dict:
