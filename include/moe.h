@@ -63,14 +63,25 @@ extern "C" {
 typedef enum {
   MOE_F32 = 0,        /* IEEE fp32 */
   MOE_BF16 = 1,       /* bfloat16 */
-  MOE_E4M3_B128 = 2   /* expert weights only: OCP e4m3 codes (uint8) with one fp32
+  MOE_E4M3_B128 = 2,  /* expert weights only: OCP e4m3 codes (uint8) with one fp32
                          scale per 128x128 block, value = decode(code) * scale */
+  MOE_NVFP4 = 3       /* expert weights only: FP4 E2M1 codes, two per byte (element 2i
+                         in the low nibble), one OCP e4m3 scale per 16 consecutive
+                         inputs and one fp32 scale per expert matrix,
+                         value = e2m1(code) * e4m3(block scale) * matrix scale.  The
+                         4-bit expert format TensorFold issue #1247 "Ling-3.0-tiny on a
+                         Qualcomm board" names in its list "What it does not cover";
+                         its layout is not on the pages and this one is a reading. */
 } moe_dtype;
 
 /*
  * Layer configuration.  Supported element-type pairs (act_dtype, weight_dtype):
- *   (MOE_F32, MOE_F32), (MOE_BF16, MOE_BF16), (MOE_BF16, MOE_E4M3_B128).
- * Constraints: T >= 1; H, I >= 1 and multiples of 8 (of 128 for e4m3 experts);
+ *   (MOE_F32, MOE_F32), (MOE_BF16, MOE_BF16), (MOE_BF16, MOE_E4M3_B128),
+ *   (MOE_BF16, MOE_NVFP4).
+ * Constraints: T >= 1; H, I >= 1 and multiples of 8 (of 128 for e4m3 experts, of
+ * 32 for NVFP4 experts); NVFP4 experts serve decode batches only: T <= 16,
+ * H <= 2048, I <= 1024, k + S <= 32, moe_forward only (moe_expert_ffn returns
+ * MOE_ERR_UNSUPPORTED for them);
  * E >= 1; G >= 1 with E % G == 0; 1 <= Gk <= G; 1 <= k <= Gk * E / G;
  * k <= 16; E + S <= 1024; T * (k + S) < 2^31.
  */
@@ -84,10 +95,12 @@ typedef struct {
   int32_t topk;           /* k: routed experts per token */
   int32_t num_shared;     /* S: always-on shared experts, weight 1 */
   int32_t act_dtype;      /* x, router weight, y: MOE_F32 | MOE_BF16 */
-  int32_t weight_dtype;   /* experts: MOE_F32 | MOE_BF16 | MOE_E4M3_B128 */
+  int32_t weight_dtype;   /* experts: MOE_F32 | MOE_BF16 | MOE_E4M3_B128 | MOE_NVFP4 */
 } moe_config;
 
-/* Weights of one layer (device pointers).  Scales are used only for MOE_E4M3_B128. */
+/* Weights of one layer (device pointers).  s_* scales are used only for MOE_E4M3_B128,
+ * b_* and g_* only for MOE_NVFP4 (whose w_* arrays then hold packed codes:
+ * gate/up [E, I, H/2] bytes, down [E, H, I/2] bytes). */
 typedef struct {
   const void*  w_router;      /* [E, H] act_dtype */
   const float* router_bias;   /* [E] fp32, added to the logits before the softmax; NULL = none */
@@ -103,6 +116,18 @@ typedef struct {
   const float* sh_s_gate;     /* [S, I/128, H/128] (e4m3 only) */
   const float* sh_s_up;       /* [S, I/128, H/128] */
   const float* sh_s_down;     /* [S, H/128, I/128] */
+  const uint8_t* b_gate;      /* [E, I, H/16] e4m3 block scales (NVFP4 only) */
+  const uint8_t* b_up;        /* [E, I, H/16] */
+  const uint8_t* b_down;      /* [E, H, I/16] */
+  const float* g_gate;        /* [E] fp32 scale of each expert matrix (NVFP4 only) */
+  const float* g_up;          /* [E] */
+  const float* g_down;        /* [E] */
+  const uint8_t* sh_b_gate;   /* [S, I, H/16] (NVFP4 only) */
+  const uint8_t* sh_b_up;     /* [S, I, H/16] */
+  const uint8_t* sh_b_down;   /* [S, H, I/16] */
+  const float* sh_g_gate;     /* [S] */
+  const float* sh_g_up;       /* [S] */
+  const float* sh_g_down;     /* [S] */
 } moe_weights;
 
 /*

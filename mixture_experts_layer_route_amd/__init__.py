@@ -17,8 +17,8 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
-MOE_F32, MOE_BF16, MOE_E4M3_B128 = 0, 1, 2
-_DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "e4m3": MOE_E4M3_B128}
+MOE_F32, MOE_BF16, MOE_E4M3_B128, MOE_NVFP4 = 0, 1, 2, 3
+_DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "e4m3": MOE_E4M3_B128, "nvfp4": MOE_NVFP4}
 
 
 class MoeConfig(ctypes.Structure):
@@ -32,7 +32,9 @@ class MoeConfig(ctypes.Structure):
 class MoeWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "w_router", "router_bias", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
-        "sh_gate", "sh_up", "sh_down", "sh_s_gate", "sh_s_up", "sh_s_down")]
+        "sh_gate", "sh_up", "sh_down", "sh_s_gate", "sh_s_up", "sh_s_down",
+        "b_gate", "b_up", "b_down", "g_gate", "g_up", "g_down",
+        "sh_b_gate", "sh_b_up", "sh_b_down", "sh_g_gate", "sh_g_up", "sh_g_down")]
 
 
 ENTRY_POINTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn",

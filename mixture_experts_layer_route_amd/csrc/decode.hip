@@ -18,6 +18,8 @@
 // A single kernel with a device-wide barrier between the two halves measured
 // slower on MI355X than the launch it saves (the cross-XCD arrival counting and
 // cache write-back cost tens of microseconds), so the halves are two launches.
+#include <type_traits>
+
 #include "moe_internal.h"
 #include "route_select.h"
 
@@ -29,10 +31,80 @@ __device__ __forceinline__ const TW* dexpert(const TW* routed, const TW* shared,
   return e < E ? routed + int64_t(e) * stride : shared + int64_t(e - E) * stride;
 }
 
+// Tag type: expert weights stored as NVFP4 (packed E2M1 codes, e4m3 scale per 16
+// inputs, fp32 scale per matrix).
+struct nvfp4_t {};
+
+template <typename TB>
+__device__ __forceinline__ const TB* nv_expert(const TB* routed, const TB* shared, int e, int E,
+                                               int64_t stride) {
+  return e < E ? routed + int64_t(e) * stride : shared + int64_t(e - E) * stride;
+}
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+// Two e4m3 codes (low byte first) -> two floats.
+__device__ __forceinline__ void e4m3_pair(uint32_t two, float& s0, float& s1) {
+  const auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(two, 1.0f, false);
+  s0 = f[0];
+  s1 = f[1];
+}
+
+// Dot of 16 consecutive E2M1 weights (two dwords of codes, element 2i in the low
+// nibble of byte i) with 16 bf16 activations (eight dwords of bf16 pairs).  Each
+// code byte becomes a bf16 pair exactly (every E2M1 value is a bf16 value), and
+// each pair product is accumulated in fp32 by the packed bf16 dot.
+__device__ __forceinline__ float dot16_fp4_bf16(uint32_t c0, uint32_t c1, const uint32_t* x) {
+  auto w = [](uint32_t c, int sel) {
+    switch (sel) {
+      case 0: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, 0);
+      case 1: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, 1);
+      case 2: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, 2);
+      default: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, 3);
+    }
+  };
+  auto xb = [&](int i) { return __builtin_bit_cast(bf16x2_t, x[i]); };
+  float d0 = 0.f, d1 = 0.f;
+  d0 = __builtin_amdgcn_fdot2_f32_bf16(w(c0, 0), xb(0), d0, false);
+  d1 = __builtin_amdgcn_fdot2_f32_bf16(w(c0, 1), xb(1), d1, false);
+  d0 = __builtin_amdgcn_fdot2_f32_bf16(w(c0, 2), xb(2), d0, false);
+  d1 = __builtin_amdgcn_fdot2_f32_bf16(w(c0, 3), xb(3), d1, false);
+  d0 = __builtin_amdgcn_fdot2_f32_bf16(w(c1, 0), xb(4), d0, false);
+  d1 = __builtin_amdgcn_fdot2_f32_bf16(w(c1, 1), xb(5), d1, false);
+  d0 = __builtin_amdgcn_fdot2_f32_bf16(w(c1, 2), xb(6), d0, false);
+  d1 = __builtin_amdgcn_fdot2_f32_bf16(w(c1, 3), xb(7), d1, false);
+  return d0 + d1;
+}
+
+// Dot of 16 consecutive E2M1 weights with 16 fp32 values.
+__device__ __forceinline__ float dot16_fp4_f32(uint32_t c0, uint32_t c1, const float* v) {
+  auto w = [](uint32_t c, int sel) {
+    switch (sel) {
+      case 0: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
+      case 1: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1);
+      case 2: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2);
+      default: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3);
+    }
+  };
+  float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const auto p = w(c0, b), q = w(c1, b);
+    d0 = fmaf(p[0], v[2 * b], d0);
+    d1 = fmaf(p[1], v[2 * b + 1], d1);
+    d0 = fmaf(q[0], v[8 + 2 * b], d0);
+    d1 = fmaf(q[1], v[8 + 2 * b + 1], d1);
+  }
+  return d0 + d1;
+}
+
 struct DecodeArgs {
   const void* x;
   const float* logits;
   const void *wg, *wu, *wd, *shg, *shu, *shd;
+  // NVFP4 experts only: e4m3 block scales (one per 16 inputs) and fp32 matrix scales
+  const uint8_t *bg, *bu, *bd, *shbg, *shbu, *shbd;
+  const float *gg, *gu, *gd, *shgg, *shgu, *shgd;
   int32_t* ids;        // [T, k] routing outputs (published by block 0)
   float* w;            // [T, k]
   int32_t* offsets;    // [E+S+1]
@@ -42,6 +114,101 @@ struct DecodeArgs {
   void* y;             // [T, H]
   int T, H, I, E, S, G, Gk, k;
 };
+
+// Gate/up item loop for NVFP4 experts.  Item = (active expert, 4 consecutive rows
+// of I); row q of the item is handled by the 16 lanes of DPP row q, lane cc taking
+// 32-input chunks cc, cc+16, ... (16 bytes of codes and two e4m3 scales each), so a
+// row's partial sums meet in one DPP row reduction.  The matrix scales multiply
+// the reduced gate and up values.  The next item's loads are in flight while the
+// current one is multiplied.
+template <int NS>
+__device__ __forceinline__ void decode_gateup_nv(const DecodeArgs& a, const bf16_t* xs,
+                                                 const int32_t* off_l, const int32_t* act_l,
+                                                 const int32_t* rt_l, int n_act, int lane) {
+  struct Buf {
+    uint4 g[NS], u[NS];
+    uint32_t sg[NS], su[NS];
+    float gg, gu;
+  };
+  const int H = a.H, I = a.I, E = a.E;
+  const int H2 = H / 2, H16 = H / 16, HC = H / 32;
+  const int q = lane >> 4, cc = lane & 15;
+  const int ipe = I / 4;
+  const int total = n_act * ipe;
+  const int64_t cstr = int64_t(I) * H2, bstr = int64_t(I) * H16;
+  const int gstride = gridDim.x * 4;
+  const uint8_t* wg = static_cast<const uint8_t*>(a.wg);
+  const uint8_t* wu = static_cast<const uint8_t*>(a.wu);
+  const uint8_t* shg = static_cast<const uint8_t*>(a.shg);
+  const uint8_t* shu = static_cast<const uint8_t*>(a.shu);
+  auto load = [&](int item, Buf& b) {
+    const int u = item / ipe, row = (item - u * ipe) * 4 + q;
+    const int e = act_l[u];
+    const uint8_t* gp = nv_expert(wg, shg, e, E, cstr) + int64_t(row) * H2;
+    const uint8_t* up = nv_expert(wu, shu, e, E, cstr) + int64_t(row) * H2;
+    const uint8_t* gs = nv_expert(a.bg, a.shbg, e, E, bstr) + int64_t(row) * H16;
+    const uint8_t* us = nv_expert(a.bu, a.shbu, e, E, bstr) + int64_t(row) * H16;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int c = cc + 16 * s;
+      if (c < HC) {
+        b.g[s] = *reinterpret_cast<const uint4*>(gp + c * 16);
+        b.u[s] = *reinterpret_cast<const uint4*>(up + c * 16);
+        b.sg[s] = *reinterpret_cast<const uint16_t*>(gs + c * 2);
+        b.su[s] = *reinterpret_cast<const uint16_t*>(us + c * 2);
+      }
+    }
+    b.gg = e < E ? a.gg[e] : a.shgg[e - E];
+    b.gu = e < E ? a.gu[e] : a.shgu[e - E];
+  };
+  auto compute = [&](int item, const Buf& b) {
+    const int u = item / ipe, i0 = (item - u * ipe) * 4;
+    const int e = act_l[u];
+    float sg0[NS], sg1[NS], su0[NS], su1[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      e4m3_pair(b.sg[s], sg0[s], sg1[s]);
+      e4m3_pair(b.su[s], su0[s], su1[s]);
+    }
+    for (int r = off_l[e]; r < off_l[e + 1]; ++r) {
+      const bf16_t* xr = xs + rt_l[r] * H;
+      float ag = 0.f, au = 0.f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int c = cc + 16 * s;
+        if (c < HC) {
+          uint32_t xv[16];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const uint4 t4 = *reinterpret_cast<const uint4*>(xr + c * 32 + v * 8);
+            xv[4 * v] = t4.x; xv[4 * v + 1] = t4.y; xv[4 * v + 2] = t4.z; xv[4 * v + 3] = t4.w;
+          }
+          ag = fmaf(dot16_fp4_bf16(b.g[s].x, b.g[s].y, xv), sg0[s], ag);
+          au = fmaf(dot16_fp4_bf16(b.u[s].x, b.u[s].y, xv), su0[s], au);
+          ag = fmaf(dot16_fp4_bf16(b.g[s].z, b.g[s].w, xv + 8), sg1[s], ag);
+          au = fmaf(dot16_fp4_bf16(b.u[s].z, b.u[s].w, xv + 8), su1[s], au);
+        }
+      }
+      ag = row_sum(ag) * b.gg;
+      au = row_sum(au) * b.gu;
+      if (cc == 0) a.h[int64_t(r) * I + i0 + q] = silu(ag) * au;
+    }
+  };
+  Buf ba, bb;
+  int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item < total) load(item, ba);
+  while (item < total) {
+    int nxt = item + gstride;
+    if (nxt < total) load(nxt, bb);
+    compute(item, ba);
+    item = nxt;
+    if (item >= total) break;
+    nxt = item + gstride;
+    if (nxt < total) load(nxt, ba);
+    compute(item, bb);
+    item = nxt;
+  }
+}
 
 // SEL > 0: a wave per token (select_token_wave<SEL>); SEL < 0: sixteen lanes per
 // token, four tokens per wave (select_token_row<-SEL>)
@@ -163,6 +330,9 @@ __global__ __launch_bounds__(256) void k_decode_gateup(DecodeArgs a) {
   }
 
   // ---------------------------------------------------------------- 2. gate/up
+  if constexpr (std::is_same<TW, nvfp4_t>::value) {
+    decode_gateup_nv<NS>(a, xs, off_l, act_l, rt_l, n_act_l, lane);
+  } else {
   const int ipe = I / NI;
   const int total = n_act_l * ipe;
   const int64_t mstride = int64_t(I) * H;
@@ -232,7 +402,7 @@ __global__ __launch_bounds__(256) void k_decode_gateup(DecodeArgs a) {
       item = nxt;
     }
   }
-
+  }
 }
 
 template <typename TA, typename TW, int NSD>
@@ -336,6 +506,130 @@ __global__ __launch_bounds__(256) void k_decode_down(DecodeArgs a) {
   }
 }
 
+// Down + combine for NVFP4 experts.  Block item = (token t, 4*RG output columns);
+// the four waves split the token's k + S slots (slot j to wave j % 4, SP slots per
+// load batch), so each h row is fetched once per item and the weight rows of
+// every slot stream in parallel.  Within a wave, DPP row q (16 lanes) holds
+// output columns n0 + 4g + q (g < RG), lane cc the 32-input chunks cc, cc+16, ...
+// of h and of the weight row.  The slot weight w[t,j] is folded with the matrix
+// scale of the slot's expert.  Per-wave partial sums meet in LDS and are added in
+// wave order, so the result does not depend on timing.
+template <int NSD, int RG, int SP>
+__global__ __launch_bounds__(256) void k_decode_down_nv(DecodeArgs a) {
+  constexpr int NRB = 4 * RG;
+  const int T = a.T, H = a.H, I = a.I, E = a.E, S = a.S, k = a.k;
+  const int nslot = T * k, nsl = k + S;
+  const int I2 = I / 2, I16 = I / 16, IC = I / 32;
+  __shared__ int32_t ids_l[256], inv_l[256];
+  __shared__ float w_l[256];
+  __shared__ int32_t offsh_l[32];
+  __shared__ float part_l[4][NRB];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int q = lane >> 4, cc = lane & 15;
+  const uint8_t* wd = static_cast<const uint8_t*>(a.wd);
+  const uint8_t* shd = static_cast<const uint8_t*>(a.shd);
+  for (int i = threadIdx.x; i < nslot; i += 256) {
+    ids_l[i] = a.ids[i];
+    inv_l[i] = a.inv[i];
+    w_l[i] = a.w[i];
+  }
+  for (int i = threadIdx.x; i < S; i += 256) offsh_l[i] = a.offsets[E + i];
+  __syncthreads();
+
+  const int nb = (H + NRB - 1) / NRB;
+  const int items = T * nb;
+  const int64_t cstr = int64_t(H) * I2, bstr = int64_t(H) * I16;
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    const int t = item / nb, n0 = (item - t * nb) * NRB;
+    float acc[RG];
+#pragma unroll
+    for (int g = 0; g < RG; ++g) acc[g] = 0.f;
+    for (int j0 = wv; j0 < nsl; j0 += 4 * SP) {
+      uint4 wc[SP][RG][NSD];
+      uint32_t wsc[SP][RG][NSD];
+      float hv[SP][NSD][32];
+      float wt[SP];
+#pragma unroll
+      for (int m = 0; m < SP; ++m) {
+        const int j = j0 + 4 * m;
+        wt[m] = 0.f;
+        if (j < nsl) {
+          int e, r;
+          if (j < k) {
+            e = ids_l[t * k + j];
+            r = inv_l[t * k + j];
+            wt[m] = w_l[t * k + j];
+          } else {
+            e = E + (j - k);
+            r = offsh_l[j - k] + t;
+            wt[m] = 1.f;
+          }
+          wt[m] *= e < E ? a.gd[e] : a.shgd[e - E];
+          const uint8_t* cp = nv_expert(wd, shd, e, E, cstr);
+          const uint8_t* bp = nv_expert(a.bd, a.shbd, e, E, bstr);
+#pragma unroll
+          for (int s = 0; s < NSD; ++s) {
+            const int c = cc + 16 * s;
+            if (c < IC) {
+              const float4* hp = reinterpret_cast<const float4*>(a.h + int64_t(r) * I + c * 32);
+#pragma unroll
+              for (int v = 0; v < 8; ++v) {
+                const float4 f = hp[v];
+                hv[m][s][4 * v] = f.x; hv[m][s][4 * v + 1] = f.y;
+                hv[m][s][4 * v + 2] = f.z; hv[m][s][4 * v + 3] = f.w;
+              }
+#pragma unroll
+              for (int g = 0; g < RG; ++g) {
+                const int n = n0 + 4 * g + q;
+                if (n < H) {
+                  wc[m][g][s] = *reinterpret_cast<const uint4*>(cp + int64_t(n) * I2 + c * 16);
+                  wsc[m][g][s] = *reinterpret_cast<const uint16_t*>(bp + int64_t(n) * I16 + c * 2);
+                }
+              }
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < SP; ++m) {
+        if (j0 + 4 * m < nsl) {
+#pragma unroll
+          for (int g = 0; g < RG; ++g) {
+            const int n = n0 + 4 * g + q;
+            float d = 0.f;
+#pragma unroll
+            for (int s = 0; s < NSD; ++s) {
+              const int c = cc + 16 * s;
+              if (c < IC && n < H) {
+                float s0, s1;
+                e4m3_pair(wsc[m][g][s], s0, s1);
+                d = fmaf(dot16_fp4_f32(wc[m][g][s].x, wc[m][g][s].y, hv[m][s]), s0, d);
+                d = fmaf(dot16_fp4_f32(wc[m][g][s].z, wc[m][g][s].w, hv[m][s] + 16), s1, d);
+              }
+            }
+            acc[g] = fmaf(wt[m], d, acc[g]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+      const float v = row_sum(acc[g]);
+      if (cc == 0) part_l[wv][4 * g + q] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < NRB) {
+      const int n = n0 + threadIdx.x;
+      if (n < H) {
+        const float v = (part_l[0][threadIdx.x] + part_l[1][threadIdx.x]) +
+                        (part_l[2][threadIdx.x] + part_l[3][threadIdx.x]);
+        static_cast<bf16_t*>(a.y)[int64_t(t) * H + n] = f32_to_bf16(v);
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // ---------------------------------------------------------------------------
 static size_t decode_lds(const Plan& p) {
   const size_t tsize = p.act == MOE_F32 ? 4 : 2;
@@ -374,6 +668,35 @@ static int launch_decode_t(const Plan& p, const DecodeArgs& a, hipStream_t st) {
   return check_launch();
 }
 
+template <int NS, int NSD, int Q>
+static int launch_decode_nv_t(const Plan& p, const DecodeArgs& a, hipStream_t st) {
+  const auto k1 = k_decode_gateup<bf16_t, nvfp4_t, NS, Q>;
+  const size_t lds = decode_lds(p);
+  int b1 = 0, b2 = 0;
+  MOE_TRY(persistent_blocks(reinterpret_cast<const void*>(k1), lds, &b1));
+  // columns per down item: as many as keep at least 256 items in flight
+  const int64_t T = p.T;
+  auto items = [&](int rg) { return T * ((p.H + 4 * rg - 1) / (4 * rg)); };
+  const int rg = items(4) >= 256 ? 4 : items(2) >= 256 ? 2 : 1;
+  constexpr int SP = NSD == 1 ? 2 : 1;
+  launch_kernel(p, kTimeGateUp, k1, dim3(b1), dim3(256), lds, st, a);
+  MOE_TRY(check_launch());
+  if (rg == 4) {
+    const auto k2 = k_decode_down_nv<NSD, 4, SP>;
+    MOE_TRY(persistent_blocks(reinterpret_cast<const void*>(k2), 0, &b2));
+    launch_kernel(p, kTimeDown, k2, dim3(int(std::min<int64_t>(b2, items(4)))), dim3(256), 0, st, a);
+  } else if (rg == 2) {
+    const auto k2 = k_decode_down_nv<NSD, 2, SP>;
+    MOE_TRY(persistent_blocks(reinterpret_cast<const void*>(k2), 0, &b2));
+    launch_kernel(p, kTimeDown, k2, dim3(int(std::min<int64_t>(b2, items(2)))), dim3(256), 0, st, a);
+  } else {
+    const auto k2 = k_decode_down_nv<NSD, 1, SP>;
+    MOE_TRY(persistent_blocks(reinterpret_cast<const void*>(k2), 0, &b2));
+    launch_kernel(p, kTimeDown, k2, dim3(int(std::min<int64_t>(b2, items(1)))), dim3(256), 0, st, a);
+  }
+  return check_launch();
+}
+
 int launch_decode_ffn(const Plan& p, const void* x, const float* logits, const moe_weights* w,
                       int32_t* ids, float* wts, int32_t* offsets, int32_t* row_token,
                       int32_t* inv, float* h, void* y, hipStream_t st) {
@@ -382,10 +705,41 @@ int launch_decode_ffn(const Plan& p, const void* x, const float* logits, const m
   a.wg = w->w_gate; a.wu = w->w_up; a.wd = w->w_down;
   a.shg = w->sh_gate; a.shu = w->sh_up; a.shd = w->sh_down;
   a.ids = ids; a.w = wts; a.offsets = offsets; a.row_token = row_token; a.inv = inv;
+  a.bg = w->b_gate; a.bu = w->b_up; a.bd = w->b_down;
+  a.shbg = w->sh_b_gate; a.shbu = w->sh_b_up; a.shbd = w->sh_b_down;
+  a.gg = w->g_gate; a.gu = w->g_up; a.gd = w->g_down;
+  a.shgg = w->sh_g_gate; a.shgu = w->sh_g_up; a.shgd = w->sh_g_down;
   a.h = h; a.y = y;
   a.T = int(p.T); a.H = p.H; a.I = p.I; a.E = p.E; a.S = p.S; a.G = p.G; a.Gk = p.Gk; a.k = p.k;
   const int ns = (p.H + 511) / 512, nsd = (p.I + 511) / 512;
   const bool rows = select_rows_ok(p);
+  if (p.wt == MOE_NVFP4) {
+#define MOE_NQ(NSV, NSDV)                                                    \
+  {                                                                          \
+    if (rows) {                                                              \
+      if (p.E == 128) return launch_decode_nv_t<NSV, NSDV, -8>(p, a, st);    \
+      if (p.E == 256) return launch_decode_nv_t<NSV, NSDV, -16>(p, a, st);   \
+      if (p.E == 64) return launch_decode_nv_t<NSV, NSDV, -4>(p, a, st);     \
+      if (p.E == 16) return launch_decode_nv_t<NSV, NSDV, -1>(p, a, st);     \
+    }                                                                        \
+    if (p.E <= 64) return launch_decode_nv_t<NSV, NSDV, 1>(p, a, st);        \
+    if (p.E <= 128) return launch_decode_nv_t<NSV, NSDV, 2>(p, a, st);       \
+    if (p.E <= 256) return launch_decode_nv_t<NSV, NSDV, 4>(p, a, st);       \
+    if (p.E <= 512) return launch_decode_nv_t<NSV, NSDV, 8>(p, a, st);       \
+    return launch_decode_nv_t<NSV, NSDV, 16>(p, a, st);                      \
+  }
+#define MOE_NNS(NSDV)                 \
+  {                                   \
+    if (ns <= 1) MOE_NQ(1, NSDV)      \
+    if (ns == 2) MOE_NQ(2, NSDV)      \
+    if (ns == 3) MOE_NQ(3, NSDV)      \
+    MOE_NQ(4, NSDV)                   \
+  }
+    if (nsd <= 1) MOE_NNS(1)
+    MOE_NNS(2)
+#undef MOE_NNS
+#undef MOE_NQ
+  }
 #define MOE_DQ(TA, TW, NSV, NSDV)                                            \
   {                                                                          \
     if (rows) {                                                              \

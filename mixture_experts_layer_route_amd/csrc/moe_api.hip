@@ -36,9 +36,13 @@ int make_plan(const moe_config* c, Plan* p) {
   const bool dense32 = act == MOE_F32 && wt == MOE_F32;
   const bool dense16 = act == MOE_BF16 && wt == MOE_BF16;
   const bool fp8 = act == MOE_BF16 && wt == MOE_E4M3_B128;
-  if (!(dense32 || dense16 || fp8)) return MOE_ERR_UNSUPPORTED;
+  const bool nv4 = act == MOE_BF16 && wt == MOE_NVFP4;
+  if (!(dense32 || dense16 || fp8 || nv4)) return MOE_ERR_UNSUPPORTED;
   if (H % 8 || I % 8) return MOE_ERR_UNSUPPORTED;
   if (fp8 && (H % 128 || I % 128)) return MOE_ERR_UNSUPPORTED;
+  // NVFP4 experts: the decode kernels only (a handful of tokens)
+  if (nv4 && (H % 32 || I % 32 || T > 16 || H > 2048 || I > 1024 || k + S > 32))
+    return MOE_ERR_UNSUPPORTED;
   if (E % G || G > 64 || Gk > G) return MOE_ERR_UNSUPPORTED;
   if (int64_t(k) > int64_t(Gk) * (E / G) || k > 16) return MOE_ERR_UNSUPPORTED;
   if (E + S > 1024) return MOE_ERR_UNSUPPORTED;
@@ -52,11 +56,12 @@ int make_plan(const moe_config* c, Plan* p) {
   q.nblk = int((T + 63) / 64);
   const bool mfma_shape = H % 128 == 0 && I % 64 == 0;
   // Few rows per expert on average: the weight stream dominates, skinny kernels.
-  q.skinny = dense32 || (dense16 && (q.Rk <= 8 * int64_t(E) || !mfma_shape));
+  q.skinny = dense32 || nv4 || (dense16 && (q.Rk <= 8 * int64_t(E) || !mfma_shape));
   q.small_route = T <= 64 && T * k <= 256;
   q.fused_down = q.skinny && T <= 16;
   q.max_active = std::min<int64_t>(E, q.Rk) + S;
   q.bm = gemm_tile_rows(q);
+  if (nv4 && !(q.fused_down && decode_ffn_ok(q))) return MOE_ERR_UNSUPPORTED;
   q.max_tiles = q.Rk / q.bm + std::min<int64_t>(E, q.Rk) + int64_t(S) * ((T + q.bm - 1) / q.bm);
 
   size_t o = 0;
@@ -102,6 +107,13 @@ static int check_experts(const Plan& p, const moe_weights* w) {
   if (p.wt == MOE_E4M3_B128) {
     if (!w->s_gate || !w->s_up || !w->s_down) return MOE_ERR_ARG;
     if (p.S > 0 && (!w->sh_s_gate || !w->sh_s_up || !w->sh_s_down)) return MOE_ERR_ARG;
+  }
+  if (p.wt == MOE_NVFP4) {
+    if (!w->b_gate || !w->b_up || !w->b_down || !w->g_gate || !w->g_up || !w->g_down)
+      return MOE_ERR_ARG;
+    if (p.S > 0 && (!w->sh_b_gate || !w->sh_b_up || !w->sh_b_down || !w->sh_g_gate ||
+                    !w->sh_g_up || !w->sh_g_down))
+      return MOE_ERR_ARG;
   }
   return MOE_OK;
 }
@@ -177,6 +189,7 @@ int moe_expert_ffn(const moe_config* cfg, const void* x, const int32_t* expert_o
                    size_t ws_bytes, hipStream_t stream) {
   Plan p;
   MOE_TRY(make_plan(cfg, &p));
+  if (p.wt == MOE_NVFP4) return MOE_ERR_UNSUPPORTED;   // NVFP4 experts: moe_forward only
   if (!x || !expert_offsets || !row_token || !y_perm) return MOE_ERR_ARG;
   MOE_TRY(check_experts(p, w));
   MOE_TRY(check_ws(p, ws, ws_bytes));

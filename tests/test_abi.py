@@ -82,3 +82,36 @@ def test_calls_reject_null_and_small_workspace(lib):
     assert lib.moe_expert_ffn(ctypes.byref(cfg_sh), fake, fake, fake, ctypes.byref(w), fake,
                               fake, 1 << 40, None) == -1
     assert lib.moe_combine(ctypes.byref(cfg), None, fake, fake, fake, fake, None) == -1
+    cfg4 = _cfg(wt="nvfp4")                  # NVFP4 experts need block and matrix scales
+    assert lib.moe_forward(ctypes.byref(cfg4), fake, ctypes.byref(w), fake, None, None, fake,
+                           1 << 40, None) == -1
+    assert lib.moe_expert_ffn(ctypes.byref(cfg4), fake, fake, fake, ctypes.byref(w), fake, fake,
+                              1 << 40, None) == -2        # NVFP4: the forward's decode path only
+
+
+def test_nvfp4_supported_shapes(lib):
+    n = ctypes.c_size_t(0)
+    ok = [dict(wt="nvfp4"), dict(wt="nvfp4", T=1), dict(wt="nvfp4", T=16),
+          dict(wt="nvfp4", S=2), dict(wt="nvfp4", H=640, I=384, E=64, G=4, Gk=2, k=4),
+          dict(wt="nvfp4", T=8, H=1024, I=256, E=256, G=1, Gk=1, k=6, S=2),
+          dict(wt="nvfp4", H=512, I=1024, E=32, G=1, Gk=1, k=4, S=1),
+          dict(wt="nvfp4", T=3, H=512, I=256, E=256, G=64, Gk=8, k=16),
+          dict(wt="nvfp4", T=12, H=2048, I=256, E=16, G=4, Gk=2, k=4)]
+    for kw in ok:
+        assert lib.moe_workspace_size(ctypes.byref(_cfg(**kw)), ctypes.byref(n)) == 0, kw
+    bad = [dict(wt="nvfp4", T=17), dict(wt="nvfp4", H=1520), dict(wt="nvfp4", I=496),
+           dict(wt="nvfp4", act="f32"), dict(wt="nvfp4", H=4096), dict(wt="nvfp4", I=2048),
+           dict(wt="nvfp4", T=16, H=2048)]              # token rows beyond the LDS budget
+    for kw in bad:
+        assert lib.moe_workspace_size(ctypes.byref(_cfg(**kw)), ctypes.byref(n)) == -2, kw
+
+
+def test_weights_struct_matches_header():
+    """The ctypes weight struct lists moe.h's fields in the header's order."""
+    txt = open(os.path.join(ROOT, "include", "moe.h")).read()
+    body = txt[txt.index("typedef struct {", txt.index("moe_config;")):txt.index("} moe_weights;")]
+    names = re.findall(r"^\s*const\s+\w+\*\s+(\w+);", body, re.M)
+    assert names == [n for n, _ in moe.MoeWeights._fields_]
+    cbody = txt[txt.index("typedef struct {"):txt.index("} moe_config;")]
+    cnames = re.findall(r"^\s*int\d+_t\s+(\w+);", cbody, re.M)
+    assert cnames == [n for n, _ in moe.MoeConfig._fields_]
