@@ -32,7 +32,9 @@ FP8_PEAK_TFLOPS = 5033.2         # MI355X dense fp8 MFMA
 WEIGHT_KEYS = ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down", "sh_gate", "sh_up",
                "sh_down", "sh_s_gate", "sh_s_up", "sh_s_down")
 NV_KEYS = ("b_gate", "b_up", "b_down", "g_gate", "g_up", "g_down")
-DEFAULT_SETS = {"tiny": 1, "decode": 8, "prefill": 2, "fp8": 4, "inkling": 1}
+# weight copies rotated per step so that the weight stream comes from HBM, not from
+# the 256 MB last-level cache (one NVFP4 copy of the decode layer is ~170 MB)
+DEFAULT_SETS = {"tiny": 1, "decode": 8, "prefill": 2, "fp8": 4, "inkling": 1, "decode_nvfp4": 16}
 
 
 def log(*a):
@@ -45,7 +47,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode",
-                    choices=["tiny", "decode", "prefill", "fp8", "inkling"])
+                    choices=["tiny", "decode", "prefill", "fp8", "inkling", "decode_nvfp4"])
     ap.add_argument("--sets", type=int, default=0, help="weight copies rotated per step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="host time budget for the oracle baseline (0 = skip)")
@@ -108,9 +110,14 @@ def kernel_roofline(shape, which, ms, U):
                 "traffic": measured_traffic(shape.name, which),
                 "kernel": name, "kernel_us": round(ms * 1e3, 2),
                 "per_launch": f"{flops / 1e9:.2f} GFLOP = 2*R*H*I*{mats}, R={R} rows"}
-    wbytes = {"e4m3": 1, "f32": 4, "bf16": 2}[shape.wt]
-    scales = mats * (I // 128) * (H // 128) * 4 if shape.wt == "e4m3" else 0
-    per_expert = mats * I * H * wbytes + scales
+    wbytes = {"e4m3": 1, "f32": 4, "bf16": 2, "nvfp4": 0.5}[shape.wt]
+    if shape.wt == "e4m3":
+        scales = mats * (I // 128) * (H // 128) * 4
+    elif shape.wt == "nvfp4":
+        scales = mats * (I * H // 16 + 4)          # e4m3 per 16 inputs + fp32 per matrix
+    else:
+        scales = 0
+    per_expert = int(mats * I * H * wbytes) + scales
     abytes = U * per_expert
     achieved = abytes / (ms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -255,7 +262,7 @@ def main():
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": K, "warmup": W, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
-        "dtype": {"f32": "f32", "bf16": "bf16", "e4m3": "e4m3+bf16"}[shape.wt],
+        "dtype": {"f32": "f32", "bf16": "bf16", "e4m3": "e4m3+bf16", "nvfp4": "nvfp4+bf16"}[shape.wt],
         "data": "synthetic",
         "config": {"workload": shape.name, "T": shape.T, "H": shape.H, "I": shape.I,
                    "E": shape.E, "G": shape.G, "Gk": shape.Gk, "k": shape.k, "S": shape.S,

@@ -642,7 +642,8 @@ bool decode_ffn_ok(const Plan& p) {
          p.I % 2 == 0 && decode_lds(p) <= size_t(64) * 1024;
 }
 
-static int persistent_blocks(const void* kern, size_t lds, int* blocks) {
+// Blocks of a persistent launch: every CU gets as many as fit, at most `cap`.
+static int persistent_blocks(const void* kern, size_t lds, int* blocks, int cap = 2) {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
@@ -650,7 +651,7 @@ static int persistent_blocks(const void* kern, size_t lds, int* blocks) {
     check_launch();
     return MOE_ERR_HIP;
   }
-  *blocks = cus * std::max(1, std::min(per_cu, 2));
+  *blocks = cus * std::max(1, std::min(per_cu, cap));
   return MOE_OK;
 }
 
@@ -673,7 +674,10 @@ static int launch_decode_nv_t(const Plan& p, const DecodeArgs& a, hipStream_t st
   const auto k1 = k_decode_gateup<bf16_t, nvfp4_t, NS, Q>;
   const size_t lds = decode_lds(p);
   int b1 = 0, b2 = 0;
-  MOE_TRY(persistent_blocks(reinterpret_cast<const void*>(k1), lds, &b1));
+  // the 4-bit items end in conversion-heavy arithmetic once their data has arrived, so
+  // a third resident block per CU (its VGPRs allow three waves per SIMD) keeps SIMDs
+  // busy while other waves still wait for weights (measured: 17.2 -> 15.9 us per step)
+  MOE_TRY(persistent_blocks(reinterpret_cast<const void*>(k1), lds, &b1, 3));
   // columns per down item: as many as keep at least 256 items in flight
   const int64_t T = p.T;
   auto items = [&](int rg) { return T * ((p.H + 4 * rg - 1) / (4 * rg)); };

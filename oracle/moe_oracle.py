@@ -34,7 +34,7 @@ plainest the rest supports):
       per token per 128 along K: scale = fp32(amax) / 448 (fp32 division),
       code = e4m3 round-to-nearest-even of fp32(v / scale), saturating at 448;
       an all-zero block gets scale 1.
-  R10 NVFP4 experts (the 4-bit format TensorFold #1247 names for #874, list "What
+  R15 NVFP4 experts (the 4-bit format TensorFold #1247 names for #874, list "What
       it does not cover"; its layout is not on the pages) are FP4 E2M1 codes
       (sign, 2 exponent bits with bias 1, 1 mantissa bit, no inf/NaN), two per byte
       with element 2i in the low nibble, one E4M3 scale per 16 consecutive
@@ -235,7 +235,7 @@ def dequant_blocks(codes, scales, block: int = FP8_BLOCK) -> np.ndarray:
     return vals * sc
 
 
-# --------------------------------------------------------------------------- NVFP4 (R10)
+# --------------------------------------------------------------------------- NVFP4 (R15)
 NVFP4_BLOCK = 16
 
 
@@ -262,7 +262,7 @@ def nvfp4_unpack(packed) -> np.ndarray:
 
 def dequant_nvfp4(packed, block_scales, matrix_scale) -> np.ndarray:
     """[rows, K/2] packed E2M1 codes, [rows, K/16] E4M3 block scales and the fp32 scale
-    of the matrix -> float64 [rows, K] weights (reading R10)."""
+    of the matrix -> float64 [rows, K] weights (reading R15)."""
     vals = e2m1_values()[nvfp4_unpack(packed)]
     sc = np.repeat(e4m3_decode(block_scales), NVFP4_BLOCK, axis=-1)
     return vals * sc * float(matrix_scale)

@@ -1,4 +1,4 @@
-"""Pins of the oracle's NVFP4 decoding (reading R10) against things other than itself:
+"""Pins of the oracle's NVFP4 decoding (reading R15) against things other than itself:
 IEEE-754 bit patterns built independently, a row worked by hand, the optimality of the
 generator's rounding under the oracle's decode, and the dense path with the same
 weights."""
