@@ -190,6 +190,67 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int32_t* __restrict__ blk, i
   }
 }
 
+// Same result as k_perm_scan when every thread's run of blocks fits in registers
+// (ceil(nblk / P) <= RPT, P = 1024 / E' parts per expert, E' = E rounded up to a
+// power of two).  Thread (part gj, expert ge) with the expert index fastest across
+// lanes: its run of histogram entries is loaded once (coalesced over experts),
+// summed, and rewritten as running bases from the same registers; the parts of an
+// expert meet once in LDS, where expert thread e turns them into an exclusive
+// prefix and its total.
+template <int RPT>
+__global__ __launch_bounds__(1024) void k_perm_scan_reg(int32_t* __restrict__ blk, int nblk,
+                                                        int64_t T, int E, int S, int BM,
+                                                        int32_t* __restrict__ offsets,
+                                                        int32_t* __restrict__ active,
+                                                        int32_t* __restrict__ meta,
+                                                        int2* __restrict__ tiles) {
+  __shared__ int tmp[32];
+  __shared__ int offs[1025];
+  __shared__ int psum[1024];                       // [part][E'] sums, then exclusive prefixes
+  int Ep = 1;
+  while (Ep < E) Ep <<= 1;
+  const int P = 1024 / Ep;
+  const int tid = threadIdx.x, ge = tid & (Ep - 1), gj = tid / Ep;
+  const bool mine = ge < E;
+  const int per = (nblk + P - 1) / P;
+  const int b0 = gj * per;
+  int v[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int b = b0 + i;
+    v[i] = (mine && i < per && b < nblk) ? blk[int64_t(b) * E + ge] : 0;
+  }
+  int part = 0;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) part += v[i];
+  psum[tid] = part;
+  __syncthreads();
+  int cnt = 0;
+  if (tid < E) {
+    int run = 0;
+    for (int g = 0; g < P; ++g) {
+      const int x = psum[g * Ep + tid];
+      psum[g * Ep + tid] = run;
+      run += x;
+    }
+    cnt = run;
+  } else if (tid < E + S) {
+    cnt = int(T);
+  }
+  build_schedule(cnt, E + S, BM, offs, active, meta, tiles, tmp);
+  __syncthreads();
+  if (tid <= E + S) offsets[tid] = offs[tid];
+  if (mine) {
+    int r = offs[ge] + psum[tid];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int b = b0 + i;
+      if (i < per && b < nblk) blk[int64_t(b) * E + ge] = r;
+      r += v[i];
+    }
+  }
+}
+
 // Stable scatter, one wave per permutation block of 64 tokens.  The rank of
 // (t, j) among its block's rows of expert e is the number of lower lanes whose
 // token also chose e: a 64-bit lane mask per (wave, expert) built with LDS
@@ -306,8 +367,21 @@ int launch_scan_scatter(const Plan& p, const int32_t* ids, const float* w, int32
                         int32_t* offsets, int32_t* active, int32_t* meta, int2* tiles,
                         int32_t* row_token, int32_t* inv, float* row_w, int BM, hipStream_t st) {
   const unsigned g4 = unsigned((p.T + 255) / 256);
-  hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, st, blk, p.nblk, p.T, p.E, p.S, BM,
-                     offsets, active, meta, tiles);
+  int Ep = 1;
+  while (Ep < p.E) Ep <<= 1;
+  const int per = (p.nblk + 1024 / Ep - 1) / (1024 / Ep);    // histogram blocks per thread
+  if (per <= 8)
+    hipLaunchKernelGGL(k_perm_scan_reg<8>, dim3(1), dim3(1024), 0, st, blk, p.nblk, p.T, p.E, p.S,
+                       BM, offsets, active, meta, tiles);
+  else if (per <= 16)
+    hipLaunchKernelGGL(k_perm_scan_reg<16>, dim3(1), dim3(1024), 0, st, blk, p.nblk, p.T, p.E, p.S,
+                       BM, offsets, active, meta, tiles);
+  else if (per <= 32)
+    hipLaunchKernelGGL(k_perm_scan_reg<32>, dim3(1), dim3(1024), 0, st, blk, p.nblk, p.T, p.E, p.S,
+                       BM, offsets, active, meta, tiles);
+  else
+    hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, st, blk, p.nblk, p.T, p.E, p.S, BM,
+                       offsets, active, meta, tiles);
   hipLaunchKernelGGL(k_perm_scatter, dim3(g4), dim3(256), size_t(4) * p.E * 8, st, ids, w, p.T,
                      p.k, p.E, p.S, blk, row_token, inv, row_w);
   return check_launch();

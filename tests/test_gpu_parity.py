@@ -106,8 +106,12 @@ def test_route_forced_ties(moe):
 
 
 # ----------------------------------------------------------------------------- permutation
+# the last five reach the scan's register paths with 5, 16, 17 and 24 histogram blocks per
+# thread, and its LDS-staged path (E = 1000: one thread per expert, 40 blocks each)
 @pytest.mark.parametrize("T,E,k,S", [(1, 16, 4, 0), (4, 128, 8, 0), (257, 128, 8, 0),
-                                     (1000, 128, 8, 0), (333, 256, 6, 2), (64, 16, 4, 1)])
+                                     (1000, 128, 8, 0), (333, 256, 6, 2), (64, 16, 4, 1),
+                                     (20000, 16, 4, 0), (8192, 128, 8, 0), (4100, 256, 6, 2),
+                                     (3000, 512, 8, 0), (2500, 1000, 8, 0)])
 def test_permute_bit_exact(moe, T, E, k, S):
     _print_case("permute", T, E, k, S)
     rng = np.random.default_rng(T * 7 + E)
