@@ -41,6 +41,13 @@ plainest the rest supports):
       elements along the input dimension and one fp32 scale per expert matrix:
       weight = e2m1(code) * e4m3(block scale) * matrix scale.  Activations stay
       in their own type (no activation quantisation).
+  R16 The decoder-layer step around the MoE block (the config paragraph of
+      TensorFold #1247: 24 layers, a dense layer 0, so 23 MoE layers) is
+      x_out = x + MoE(RMSNorm(x)) with RMSNorm(x) = x / sqrt(mean(x^2) + eps) * gamma
+      over the hidden dimension, eps = 1e-6 (no value on the pages).  The
+      normalised rows are rounded to the activation type before the router and
+      the experts see them, and the sum x + y is rounded to it once; the
+      residual stream between layers is held in the activation type.
 
 Every floating-point step runs in float64 except the FP8 scale/code decisions
 of R9, which are taken in fp32 as the kernels take them.
@@ -266,6 +273,46 @@ def dequant_nvfp4(packed, block_scales, matrix_scale) -> np.ndarray:
     vals = e2m1_values()[nvfp4_unpack(packed)]
     sc = np.repeat(e4m3_decode(block_scales), NVFP4_BLOCK, axis=-1)
     return vals * sc * float(matrix_scale)
+
+
+# --------------------------------------------------------------------------- decoder step (R16)
+RMS_EPS = 1e-6
+
+
+def round_bf16(v) -> np.ndarray:
+    """float64 -> nearest bfloat16 value (ties to even), returned as float64.  A bf16
+    value has 8 significant bits: v = m * 2^e with 0.5 <= |m| < 1, so the result is
+    rint(m * 2^8) * 2^(e - 8) (numpy's rint rounds halves to even).  Normal range only
+    (|v| within bf16's normal exponents), which covers every activation here."""
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)
+    return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+
+
+def round_act(v, act: str) -> np.ndarray:
+    """Round to the activation type the layer stores (bf16 or fp32)."""
+    if act == "bf16":
+        return round_bf16(v)
+    return np.asarray(v, dtype=np.float32).astype(np.float64)
+
+
+def rms_norm(x, gamma, eps: float = RMS_EPS) -> np.ndarray:
+    """x / sqrt(mean over the last axis of x^2 + eps) * gamma, in float64."""
+    x = _f64(x)
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    return x * r * _f64(gamma)
+
+
+def residual_layer(x, gamma, w_router, bias, experts, G: int, Gk: int, k: int,
+                   act: str = "bf16", eps: float = RMS_EPS, ids=None, x_norm=None) -> dict:
+    """One MoE block of the decoder step (R16): x_n = round(RMSNorm(x)); the layer runs on
+    x_n; x_out = round(x + y).  `x_norm`, when given, replaces x_n (a caller that checks
+    the normalisation separately runs the rest of the step on the same rows)."""
+    xn = round_act(rms_norm(x, gamma, eps), act) if x_norm is None else _f64(x_norm)
+    out = forward(xn, w_router, bias, experts, G, Gk, k, ids=ids)
+    out["x_norm"] = xn
+    out["x_out"] = round_act(_f64(x) + out["y"], act)
+    return out
 
 
 # --------------------------------------------------------------------------- experts
