@@ -212,6 +212,27 @@ int moe_forward_timed(const moe_config* cfg, const void* x, const moe_weights* w
                       int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
                       hipStream_t stream, hipEvent_t* kernel_events);
 
+/*
+ * One MoE block of a decoder layer with its neighbours fused: the pre-MoE RMSNorm
+ * and the residual add.  The stack it belongs to is the one TensorFold issue #1247
+ * "Ling-3.0-tiny on a Qualcomm board" describes in jschmied's config paragraph
+ * (24 layers, a dense layer 0, so 23 MoE blocks per decode step); the pages give
+ * no norm epsilon, 1e-6 is the usual choice.
+ *   x_n   = round(x / sqrt(mean over H of x^2 + norm_eps) * norm_weight)
+ *   x_out = round(x + y),  y = the MoE layer of moe_forward applied to x_n
+ * round() is to act_dtype (bf16 round-to-nearest-even, or fp32); the mean, the
+ * reciprocal square root and the sum are fp32.  norm_weight: [H] act_dtype, 16-byte
+ * aligned.  x_out may be x itself (the residual stream updated in place) but must
+ * not overlap it otherwise.  Decode batches (T <= 16) compute the norm inside the
+ * router-logits kernel and add the residual in the down/combine kernel; larger
+ * batches add one norm kernel and add the residual in the combine.  Other
+ * arguments, the workspace and the errors are those of moe_forward; MOE_ERR_ARG
+ * also for a null norm_weight or a negative or NaN norm_eps.
+ */
+int moe_forward_residual(const moe_config* cfg, const void* x, const void* norm_weight,
+                         float norm_eps, const moe_weights* w, void* x_out, int32_t* topk_ids_out,
+                         float* topk_w_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Static description of a status code (for MOE_ERR_HIP: the last HIP error text
    seen by this thread).  Never NULL. */
 const char* moe_strerror(int status);

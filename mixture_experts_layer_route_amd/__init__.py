@@ -38,7 +38,8 @@ class MoeWeights(ctypes.Structure):
 
 
 ENTRY_POINTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn",
-                "moe_combine", "moe_forward", "moe_forward_timed", "moe_strerror")
+                "moe_combine", "moe_forward", "moe_forward_timed", "moe_forward_residual",
+                "moe_strerror")
 TIMED_EVENTS = 4   # MOE_TIMED_EVENTS: start/stop of the gate/up kernel, start/stop of the down kernel
 
 _lib = None
@@ -64,6 +65,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_combine": [cfgp, P, P, P, P, P, P],
         "moe_forward": [cfgp, P, wp, P, P, P, P, SZ, P],
         "moe_forward_timed": [cfgp, P, wp, P, P, P, P, SZ, P, P],
+        "moe_forward_residual": [cfgp, P, P, ctypes.c_float, wp, P, P, P, P, SZ, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -169,6 +171,22 @@ def forward(cfg, x, weights: dict, ws, y: Optional[torch.Tensor] = None,
     _check(load_library().moe_forward(ctypes.byref(cfg), _ptr(x), ctypes.byref(wst), _ptr(y),
                                       _ptr(ids), _ptr(wts), _ptr(ws), ws.numel(), _stream()))
     return y
+
+
+def forward_residual(cfg, x, norm_weight, weights: dict, ws, x_out: Optional[torch.Tensor] = None,
+                     eps: float = 1e-6, ids: Optional[torch.Tensor] = None,
+                     wts: Optional[torch.Tensor] = None, wst: Optional[MoeWeights] = None):
+    """The decoder step around the layer: x_out = x + MoE(RMSNorm(x) * norm_weight).
+    x_out may be x itself.  Returns x_out (and writes ids / wts when given)."""
+    if x_out is None:
+        x_out = torch.empty_like(x)
+    if wst is None:
+        wst = weights_struct(weights)
+    _check(load_library().moe_forward_residual(ctypes.byref(cfg), _ptr(x), _ptr(norm_weight),
+                                               ctypes.c_float(eps), ctypes.byref(wst),
+                                               _ptr(x_out), _ptr(ids), _ptr(wts), _ptr(ws),
+                                               ws.numel(), _stream()))
+    return x_out
 
 
 def forward_timed(cfg, x, wst: MoeWeights, ws, y, events_array) -> None:

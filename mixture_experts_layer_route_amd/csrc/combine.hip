@@ -1,8 +1,9 @@
 // Weighted combine back to token order (the weighted layer of the HelloSun/ling30tiny
 // model card's numeric-check summary 數值檢查摘要; shared-expert sum per the Inkling
 // PR summary of llama.cpp "Add TML Inkling architecture"):
-//   y[t] = sum_j w[t,j] * y_perm[inv[t,j]] + sum_s y_perm[offsets[E+s] + t]
-// in that fixed order, fp32, then stored in the activation type.  No atomics,
+//   y[t] = sum_j w[t,j] * y_perm[inv[t,j]] + sum_s y_perm[offsets[E+s] + t] (+ res[t])
+// in that fixed order, fp32, then stored in the activation type.  `res` is the
+// decoder step's residual input (or null); y may alias it element for element.  No atomics,
 // so the result is bitwise reproducible.
 #include "moe_internal.h"
 
@@ -14,8 +15,8 @@ template <typename TP, typename TY, bool PREWEIGHTED>
 __global__ __launch_bounds__(256) void k_combine(const TP* __restrict__ y_perm,
                                                  const int32_t* __restrict__ offsets,
                                                  const int32_t* __restrict__ inv,
-                                                 const float* __restrict__ w, TY* __restrict__ y,
-                                                 int H, int E, int k, int S) {
+                                                 const float* __restrict__ w, const TY* res,
+                                                 TY* y, int H, int E, int k, int S) {
   const int64_t t = blockIdx.x;
   const int c = (blockIdx.y * 256 + threadIdx.x) * 8;
   if (c >= H) return;
@@ -37,6 +38,12 @@ __global__ __launch_bounds__(256) void k_combine(const TP* __restrict__ y_perm,
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] += v[i];
   }
+  if (res) {
+    float v[8];
+    load8(res + t * H + c, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += v[i];
+  }
   TY* out = y + t * H + c;
   if constexpr (sizeof(TY) == 2) {
     uint4 pk;
@@ -52,23 +59,24 @@ __global__ __launch_bounds__(256) void k_combine(const TP* __restrict__ y_perm,
 }
 
 int launch_combine(const Plan& p, const float* y_perm, const int32_t* offsets, const int32_t* inv,
-                   const float* w, void* y, hipStream_t st) {
+                   const float* w, const void* res, void* y, hipStream_t st) {
   dim3 grid(unsigned(p.T), unsigned((p.H + 2047) / 2048));
   if (p.act == MOE_F32)
     hipLaunchKernelGGL((k_combine<float, float, false>), grid, dim3(256), 0, st, y_perm, offsets,
-                       inv, w, (float*)y, p.H, p.E, p.k, p.S);
+                       inv, w, (const float*)res, (float*)y, p.H, p.E, p.k, p.S);
   else
     hipLaunchKernelGGL((k_combine<float, bf16_t, false>), grid, dim3(256), 0, st, y_perm, offsets,
-                       inv, w, (bf16_t*)y, p.H, p.E, p.k, p.S);
+                       inv, w, (const bf16_t*)res, (bf16_t*)y, p.H, p.E, p.k, p.S);
   return check_launch();
 }
 
 // bf16 rows that already carry their routing weight (the fused down epilogue).
 int launch_combine_preweighted(const Plan& p, const bf16_t* y_perm, const int32_t* offsets,
-                               const int32_t* inv, void* y, hipStream_t st) {
+                               const int32_t* inv, const void* res, void* y, hipStream_t st) {
   dim3 grid(unsigned(p.T), unsigned((p.H + 2047) / 2048));
   hipLaunchKernelGGL((k_combine<bf16_t, bf16_t, true>), grid, dim3(256), 0, st, y_perm, offsets,
-                     inv, (const float*)nullptr, (bf16_t*)y, p.H, p.E, p.k, p.S);
+                     inv, (const float*)nullptr, (const bf16_t*)res, (bf16_t*)y, p.H, p.E, p.k,
+                     p.S);
   return check_launch();
 }
 

@@ -112,6 +112,7 @@ struct DecodeArgs {
   int32_t* inv;        // [T, k]
   float* h;            // [R, I] fp32
   void* y;             // [T, H]
+  const void* res;     // [T, H] residual added to y (the decoder step), or null
   int T, H, I, E, S, G, Gk, k;
 };
 
@@ -495,12 +496,11 @@ __global__ __launch_bounds__(256) void k_decode_down(DecodeArgs a) {
     }
 #pragma unroll
     for (int nn = 0; nn < NR; ++nn) {
-      const float v = wave_sum(acc[nn]);
+      float v = wave_sum(acc[nn]);
       if (lane == nn && n0 + nn < H) {
-        if (sizeof(TA) == 2)
-          static_cast<bf16_t*>(a.y)[int64_t(t) * H + n0 + nn] = f32_to_bf16(v);
-        else
-          static_cast<float*>(a.y)[int64_t(t) * H + n0 + nn] = v;
+        const int64_t o = int64_t(t) * H + n0 + nn;
+        if (a.res) v += to_f32<TA>(static_cast<const TA*>(a.res)[o]);
+        static_cast<TA*>(a.y)[o] = from_f32<TA>(v);
       }
     }
   }
@@ -621,9 +621,11 @@ __global__ __launch_bounds__(256) void k_decode_down_nv(DecodeArgs a) {
     if (threadIdx.x < NRB) {
       const int n = n0 + threadIdx.x;
       if (n < H) {
-        const float v = (part_l[0][threadIdx.x] + part_l[1][threadIdx.x]) +
-                        (part_l[2][threadIdx.x] + part_l[3][threadIdx.x]);
-        static_cast<bf16_t*>(a.y)[int64_t(t) * H + n] = f32_to_bf16(v);
+        float v = (part_l[0][threadIdx.x] + part_l[1][threadIdx.x]) +
+                  (part_l[2][threadIdx.x] + part_l[3][threadIdx.x]);
+        const int64_t o = int64_t(t) * H + n;
+        if (a.res) v += bf16_to_f32(static_cast<const bf16_t*>(a.res)[o]);
+        static_cast<bf16_t*>(a.y)[o] = f32_to_bf16(v);
       }
     }
     __syncthreads();
@@ -703,7 +705,7 @@ static int launch_decode_nv_t(const Plan& p, const DecodeArgs& a, hipStream_t st
 
 int launch_decode_ffn(const Plan& p, const void* x, const float* logits, const moe_weights* w,
                       int32_t* ids, float* wts, int32_t* offsets, int32_t* row_token,
-                      int32_t* inv, float* h, void* y, hipStream_t st) {
+                      int32_t* inv, float* h, const void* res, void* y, hipStream_t st) {
   DecodeArgs a{};
   a.x = x; a.logits = logits;
   a.wg = w->w_gate; a.wu = w->w_up; a.wd = w->w_down;
@@ -713,7 +715,7 @@ int launch_decode_ffn(const Plan& p, const void* x, const float* logits, const m
   a.shbg = w->sh_b_gate; a.shbu = w->sh_b_up; a.shbd = w->sh_b_down;
   a.gg = w->g_gate; a.gu = w->g_up; a.gd = w->g_down;
   a.shgg = w->sh_g_gate; a.shgu = w->sh_g_up; a.shgd = w->sh_g_down;
-  a.h = h; a.y = y;
+  a.h = h; a.y = y; a.res = res;
   a.T = int(p.T); a.H = p.H; a.I = p.I; a.E = p.E; a.S = p.S; a.G = p.G; a.Gk = p.Gk; a.k = p.k;
   const int ns = (p.H + 511) / 512, nsd = (p.I + 511) / 512;
   const bool rows = select_rows_ok(p);

@@ -212,7 +212,7 @@ template <typename TW, typename TY, int NR>
 __global__ __launch_bounds__(256) void k_down_combine_skinny(
     const float* __restrict__ hin, const int32_t* __restrict__ ids, const float* __restrict__ w,
     const int32_t* __restrict__ inv, const TW* __restrict__ wd, const TW* __restrict__ shd,
-    TY* __restrict__ y, int T, int H, int I, int E, int k, int S) {
+    const TY* res, TY* y, int T, int H, int I, int E, int k, int S) {
   constexpr int JB = 8;
   const int lane = threadIdx.x & 63;
   const int n0 = blockIdx.x * NR;
@@ -269,8 +269,12 @@ __global__ __launch_bounds__(256) void k_down_combine_skinny(
   }
 #pragma unroll
   for (int nn = 0; nn < NR; ++nn) {
-    const float v = wave_sum(acc[nn]);
-    if (lane == nn && n0 + nn < H) y[int64_t(t) * H + n0 + nn] = from_f32<TY>(v);
+    float v = wave_sum(acc[nn]);
+    if (lane == nn && n0 + nn < H) {
+      const int64_t o = int64_t(t) * H + n0 + nn;
+      if (res) v += to_f32<TY>(res[o]);
+      y[o] = from_f32<TY>(v);
+    }
   }
 }
 
@@ -314,19 +318,19 @@ int launch_down_skinny(const Plan& p, const float* h, const int32_t* offsets,
 }
 
 int launch_down_combine_skinny(const Plan& p, const float* h, const int32_t* ids, const float* wts,
-                               const int32_t* inv, const moe_weights* w, void* y,
+                               const int32_t* inv, const moe_weights* w, const void* res, void* y,
                                hipStream_t st) {
   constexpr int NR = 4;
   dim3 grid(unsigned((p.H + NR - 1) / NR), unsigned((p.T + 3) / 4));
   const int T = int(p.T);
   if (p.wt == MOE_F32)
     launch_kernel(p, kTimeDown, k_down_combine_skinny<float, float, NR>, grid, dim3(256), 0, st, h, ids,
-                       wts, inv, (const float*)w->w_down, (const float*)w->sh_down, (float*)y, T,
+                       wts, inv, (const float*)w->w_down, (const float*)w->sh_down, (const float*)res, (float*)y, T,
                        p.H, p.I, p.E, p.k, p.S);
   else
     launch_kernel(p, kTimeDown, k_down_combine_skinny<bf16_t, bf16_t, NR>, grid, dim3(256), 0, st, h,
                        ids, wts, inv, (const bf16_t*)w->w_down, (const bf16_t*)w->sh_down,
-                       (bf16_t*)y, T, p.H, p.I, p.E, p.k, p.S);
+                       (const bf16_t*)res, (bf16_t*)y, T, p.H, p.I, p.E, p.k, p.S);
   return check_launch();
 }
 

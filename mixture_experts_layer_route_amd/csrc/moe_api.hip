@@ -84,6 +84,7 @@ int make_plan(const moe_config* c, Plan* p) {
   q.o_sx = take(fp8 ? size_t(T) * (H / 128) * 4 : 0);
   q.o_hq = take(fp8 ? size_t(q.R) * I : 0);
   q.o_shq = take(fp8 ? size_t(q.R) * (I / 128) * 4 : 0);
+  q.o_xn = take(size_t(T) * H * (act == MOE_F32 ? 4 : 2));   // normalised rows (decoder step)
   q.total = o;
   *p = q;
   return MOE_OK;
@@ -203,12 +204,15 @@ int moe_combine(const moe_config* cfg, const float* y_perm, const int32_t* exper
   Plan p;
   MOE_TRY(make_plan(cfg, &p));
   if (!y_perm || !expert_offsets || !inv_rows || !topk_w || !y) return MOE_ERR_ARG;
-  return launch_combine(p, y_perm, expert_offsets, inv_rows, topk_w, y, stream);
+  return launch_combine(p, y_perm, expert_offsets, inv_rows, topk_w, nullptr, y, stream);
 }
 
+// The layer on x, or (gamma != null) the decoder step around it: x_n = RMSNorm(x) feeds
+// the router and the experts and x (`res`) is added to the combined output.
 static int forward_impl(const moe_config* cfg, const void* x, const moe_weights* w, void* y,
                         int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
-                        hipStream_t stream, hipEvent_t* ev) {
+                        hipStream_t stream, hipEvent_t* ev, const void* gamma = nullptr,
+                        float eps = 0.f) {
   Plan p;
   MOE_TRY(make_plan(cfg, &p));
   if (ev)
@@ -216,6 +220,8 @@ static int forward_impl(const moe_config* cfg, const void* x, const moe_weights*
   if (!x || !y || !w || !w->w_router) return MOE_ERR_ARG;
   MOE_TRY(check_experts(p, w));
   MOE_TRY(check_ws(p, ws, ws_bytes));
+  const void* res = gamma ? x : nullptr;
+  void* xn = at<void>(ws, p.o_xn);
   int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, p.o_ids);
   float* wts = topk_w_out ? topk_w_out : at<float>(ws, p.o_w);
   float* logits = at<float>(ws, p.o_logits);
@@ -229,10 +235,20 @@ static int forward_impl(const moe_config* cfg, const void* x, const moe_weights*
 
   int32_t* blk = at<int32_t>(ws, p.o_blk);
   if (p.fused_down && decode_ffn_ok(p)) {
-    // decode: the logits, then gate/up (routing in every block) and down + combine
-    MOE_TRY(launch_logits(p, x, w->w_router, w->router_bias, logits, stream));
-    return launch_decode_ffn(p, x, logits, w, ids, wts, off, rowtok, inv, at<float>(ws, p.o_h), y,
-                             stream);
+    // decode: the logits (with the norm in front for the decoder step), then gate/up
+    // (routing in every block) and down + combine (+ residual)
+    if (gamma) {
+      MOE_TRY(launch_logits_norm(p, x, gamma, eps, w->w_router, w->router_bias, logits, xn, stream));
+      x = xn;
+    } else {
+      MOE_TRY(launch_logits(p, x, w->w_router, w->router_bias, logits, stream));
+    }
+    return launch_decode_ffn(p, x, logits, w, ids, wts, off, rowtok, inv, at<float>(ws, p.o_h),
+                             res, y, stream);
+  }
+  if (gamma) {
+    MOE_TRY(launch_rmsnorm(p, x, gamma, eps, xn, stream));
+    x = xn;
   }
   if (p.small_route) {
     MOE_TRY(launch_logits(p, x, w->w_router, w->router_bias, logits, stream));
@@ -247,10 +263,10 @@ static int forward_impl(const moe_config* cfg, const void* x, const moe_weights*
   if (p.skinny) {
     float* h = at<float>(ws, p.o_h);
     MOE_TRY(launch_gateup_skinny(p, x, rowtok, off, active, meta, w, h, stream));
-    if (p.fused_down) return launch_down_combine_skinny(p, h, ids, wts, inv, w, y, stream);
+    if (p.fused_down) return launch_down_combine_skinny(p, h, ids, wts, inv, w, res, y, stream);
     float* yp = at<float>(ws, p.o_yp32);
     MOE_TRY(launch_down_skinny(p, h, off, active, meta, w, yp, stream));
-    return launch_combine(p, yp, off, inv, wts, y, stream);
+    return launch_combine(p, yp, off, inv, wts, res, y, stream);
   }
   bf16_t* ypw = at<bf16_t>(ws, p.o_ypw);
   if (p.wt == MOE_BF16) {
@@ -268,7 +284,7 @@ static int forward_impl(const moe_config* cfg, const void* x, const moe_weights*
     MOE_TRY(launch_gateup_mfma(p, x, rowtok, off, tiles, meta, w, h, xq, sx, hq, shq, stream));
     MOE_TRY(launch_down_mfma(p, hq, off, tiles, meta, w, row_w, nullptr, ypw, shq, stream));
   }
-  return launch_combine_preweighted(p, ypw, off, inv, y, stream);
+  return launch_combine_preweighted(p, ypw, off, inv, res, y, stream);
 }
 
 int moe_forward(const moe_config* cfg, const void* x, const moe_weights* w, void* y,
@@ -284,6 +300,14 @@ int moe_forward_timed(const moe_config* cfg, const void* x, const moe_weights* w
   for (int i = 0; i < MOE_TIMED_EVENTS; ++i)
     if (!kernel_events[i]) return MOE_ERR_ARG;
   return forward_impl(cfg, x, w, y, topk_ids_out, topk_w_out, ws, ws_bytes, stream, kernel_events);
+}
+
+int moe_forward_residual(const moe_config* cfg, const void* x, const void* norm_weight,
+                         float norm_eps, const moe_weights* w, void* x_out, int32_t* topk_ids_out,
+                         float* topk_w_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!norm_weight || !(norm_eps >= 0.f)) return MOE_ERR_ARG;
+  return forward_impl(cfg, x, w, x_out, topk_ids_out, topk_w_out, ws, ws_bytes, stream, nullptr,
+                      norm_weight, norm_eps);
 }
 
 const char* moe_strerror(int status) {

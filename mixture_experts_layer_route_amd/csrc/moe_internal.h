@@ -28,7 +28,7 @@ struct Plan {
   int64_t max_tiles;    // upper bound on M tiles
   // workspace carve (byte offsets)
   size_t o_logits, o_ids, o_w, o_blk, o_off, o_meta, o_active, o_tiles, o_rowtok, o_inv, o_roww,
-      o_h, o_ypw, o_yp32, o_xq, o_sx, o_hq, o_shq, total;
+      o_h, o_ypw, o_yp32, o_xq, o_sx, o_hq, o_shq, o_xn, total;
   // optional timing events bound to kernel dispatches: [0],[1] start/stop of the
   // gate/up expert kernel, [2],[3] of the down kernel (all null when not timed)
   hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
@@ -60,6 +60,11 @@ int record_hip_error(hipError_t err);
 
 int launch_logits(const Plan& p, const void* x, const void* wr, const float* bias, float* logits,
                   hipStream_t st);
+// decoder step: RMSNorm of the rows (batch), or fused in front of the few-token router
+int launch_rmsnorm(const Plan& p, const void* x, const void* gamma, float eps, void* xn,
+                   hipStream_t st);
+int launch_logits_norm(const Plan& p, const void* x, const void* gamma, float eps, const void* wr,
+                       const float* bias, float* logits, void* xn, hipStream_t st);
 int launch_select(const Plan& p, const float* logits, int32_t* ids, float* w, int32_t* blk,
                   hipStream_t st);
 int launch_scan_scatter(const Plan& p, const int32_t* ids, const float* w, int32_t* blk,
@@ -82,7 +87,7 @@ int gemm_tile_rows(const Plan& p);
 // Decode path: gate/up (with in-kernel routing) then down + combine.
 int launch_decode_ffn(const Plan& p, const void* x, const float* logits, const moe_weights* w,
                       int32_t* ids, float* wts, int32_t* offsets, int32_t* row_token,
-                      int32_t* inv, float* h, void* y, hipStream_t st);
+                      int32_t* inv, float* h, const void* res, void* y, hipStream_t st);
 int launch_gateup_skinny(const Plan& p, const void* x, const int32_t* row_token,
                          const int32_t* offsets, const int32_t* active, const int32_t* meta,
                          const moe_weights* w, float* h, hipStream_t st);
@@ -90,7 +95,8 @@ int launch_down_skinny(const Plan& p, const float* h, const int32_t* offsets,
                        const int32_t* active, const int32_t* meta, const moe_weights* w,
                        float* y_perm, hipStream_t st);
 int launch_down_combine_skinny(const Plan& p, const float* h, const int32_t* ids, const float* wts,
-                               const int32_t* inv, const moe_weights* w, void* y, hipStream_t st);
+                               const int32_t* inv, const moe_weights* w, const void* res, void* y,
+                               hipStream_t st);
 int launch_gateup_mfma(const Plan& p, const void* x, const int32_t* row_token,
                        const int32_t* offsets, const int2* tiles, const int32_t* meta,
                        const moe_weights* w, void* h, const uint8_t* xq, const float* sx,
@@ -100,9 +106,10 @@ int launch_down_mfma(const Plan& p, const void* h, const int32_t* offsets, const
                      bf16_t* out16, const float* sh_scale, hipStream_t st);
 int launch_quant(const Plan& p, const void* in, bool in_bf16, int64_t rows, int K, uint8_t* codes,
                  float* scales, hipStream_t st);
+// `res`: residual added to y (decoder step), or null
 int launch_combine(const Plan& p, const float* y_perm, const int32_t* offsets, const int32_t* inv,
-                   const float* w, void* y, hipStream_t st);
+                   const float* w, const void* res, void* y, hipStream_t st);
 int launch_combine_preweighted(const Plan& p, const bf16_t* y_perm, const int32_t* offsets,
-                               const int32_t* inv, void* y, hipStream_t st);
+                               const int32_t* inv, const void* res, void* y, hipStream_t st);
 
 }  // namespace moe

@@ -150,6 +150,161 @@ __global__ __launch_bounds__(256) void k_logits_few(const TA* __restrict__ x,
   }
 }
 
+// Router logits of a handful of tokens with the pre-layer RMSNorm fused in front:
+// x_n = round(x / sqrt(mean(x^2) + eps) * gamma) per token, l = x_n W_r^T (+ bias).
+// Every wave first computes the T inverse RMS values itself (the token rows are
+// small and cached), so no block waits on another; wave 0 of block 0 also stores
+// x_n, which the expert kernels read, so router and experts see the same rows.
+// grid = ceil(E/4), block = 256 (one wave per expert).
+template <typename TA>
+__global__ __launch_bounds__(256) void k_logits_few_norm(const TA* __restrict__ x,
+                                                         const TA* __restrict__ gamma, float eps,
+                                                         const TA* __restrict__ wr,
+                                                         const float* __restrict__ bias,
+                                                         float* __restrict__ logits,
+                                                         TA* __restrict__ xn_out, int T, int H,
+                                                         int E) {
+  constexpr int SMAX = 4;
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= E) return;                    // uniform over the wave; e = 0 is the writer
+  const bool writer = e == 0;
+  const TA* wrow = wr + int64_t(e) * H;
+  // the first slab of the router row and of gamma travel with the pre-pass loads
+  Chunk8<TA> wc0[SMAX], gc0[SMAX];
+#pragma unroll
+  for (int s = 0; s < SMAX; ++s) {
+    const int h = s * 512 + lane * 8;
+    if (h < H) {
+      wc0[s].load(wrow + h);
+      gc0[s].load(gamma + h);
+    }
+  }
+  float ss[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) ss[q] = 0.f;
+  for (int hb = 0; hb < H; hb += 512 * SMAX) {
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s) {
+      const int h = hb + s * 512 + lane * 8;
+      if (h < H) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          if (q < T) {
+            float v[8];
+            load8(x + int64_t(q) * H + h, v);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ss[q] = fmaf(v[i], v[i], ss[q]);
+          }
+        }
+      }
+    }
+  }
+  float rinv[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q)
+    rinv[q] = q < T ? 1.0f / sqrtf(wave_sum(ss[q]) / float(H) + eps) : 0.f;
+  float acc[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+  for (int hb = 0; hb < H; hb += 512 * SMAX) {
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s) {
+      const int h = hb + s * 512 + lane * 8;
+      if (h < H) {
+        float wv[8], gv[8];
+        if (hb == 0) {
+          wc0[s].get(wv);
+          gc0[s].get(gv);
+        } else {
+          load8(wrow + h, wv);
+          load8(gamma + h, gv);
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          if (q < T) {
+            float v[8];
+            load8(x + int64_t(q) * H + h, v);
+            TA nb[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              nb[i] = from_f32<TA>(v[i] * rinv[q] * gv[i]);
+              acc[q] = fmaf(to_f32<TA>(nb[i]), wv[i], acc[q]);
+            }
+            if (writer) {
+              TA* o = xn_out + int64_t(q) * H + h;
+#pragma unroll
+              for (int i = 0; i < 8; ++i) o[i] = nb[i];
+            }
+          }
+        }
+      }
+    }
+  }
+  const float b = bias ? bias[e] : 0.f;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    if (q < T) {
+      const float v = wave_sum(acc[q]);
+      if (lane == 0) logits[int64_t(q) * E + e] = v + b;
+    }
+  }
+}
+
+// RMSNorm of a batch (one wave per token): x_n = round(x / sqrt(mean(x^2) + eps) * gamma).
+// grid = ceil(T/4), block = 256.
+template <typename TA>
+__global__ __launch_bounds__(256) void k_rmsnorm(const TA* __restrict__ x,
+                                                 const TA* __restrict__ gamma, float eps,
+                                                 TA* __restrict__ xn, int64_t T, int H) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const TA* xr = x + t * H;
+  float ss = 0.f;
+  for (int h = lane * 8; h < H; h += 512) {
+    float v[8];
+    load8(xr + h, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss = fmaf(v[i], v[i], ss);
+  }
+  const float rinv = 1.0f / sqrtf(wave_sum(ss) / float(H) + eps);
+  for (int h = lane * 8; h < H; h += 512) {
+    float v[8], gv[8];
+    load8(xr + h, v);
+    load8(gamma + h, gv);
+    TA* o = xn + t * H + h;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = from_f32<TA>(v[i] * rinv * gv[i]);
+  }
+}
+
+int launch_rmsnorm(const Plan& p, const void* x, const void* gamma, float eps, void* xn,
+                   hipStream_t st) {
+  const dim3 grid(unsigned((p.T + 3) / 4));
+  if (p.act == MOE_F32)
+    hipLaunchKernelGGL(k_rmsnorm<float>, grid, dim3(256), 0, st, (const float*)x,
+                       (const float*)gamma, eps, (float*)xn, p.T, p.H);
+  else
+    hipLaunchKernelGGL(k_rmsnorm<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)x,
+                       (const bf16_t*)gamma, eps, (bf16_t*)xn, p.T, p.H);
+  return check_launch();
+}
+
+int launch_logits_norm(const Plan& p, const void* x, const void* gamma, float eps, const void* wr,
+                       const float* bias, float* logits, void* xn, hipStream_t st) {
+  const dim3 grid(unsigned((p.E + 3) / 4));
+  if (p.act == MOE_F32)
+    hipLaunchKernelGGL(k_logits_few_norm<float>, grid, dim3(256), 0, st, (const float*)x,
+                       (const float*)gamma, eps, (const float*)wr, bias, logits, (float*)xn,
+                       int(p.T), p.H, p.E);
+  else
+    hipLaunchKernelGGL(k_logits_few_norm<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)x,
+                       (const bf16_t*)gamma, eps, (const bf16_t*)wr, bias, logits, (bf16_t*)xn,
+                       int(p.T), p.H, p.E);
+  return check_launch();
+}
+
 // ---------------------------------------------------------------------------
 // Matrix-core router logits for bf16 batches: l = X W_r^T (+ bias), fp32 [T, E].
 // One workgroup of 4 waves (2 x 2, each 32 tokens x 32 experts, one 32x32 MFMA

@@ -153,6 +153,14 @@ def _encode_nvfp4(w: np.ndarray):
     return torch.from_numpy(packed), bcode.view(torch.uint8), torch.from_numpy(g)
 
 
+def make_norm_weight(H: int, act: str, seed: int) -> torch.Tensor:
+    """Pre-MoE RMSNorm weight [H] for the decoder step: 1 + 0.1 * N(0, 1) drawn in float32
+    from ``default_rng(seed)`` (its own stream, so the layer draws above are unchanged),
+    stored in the activation type."""
+    rng = np.random.default_rng(seed)
+    return _store(np.float32(1.0) + np.float32(0.1) * rng.standard_normal(H, dtype=np.float32), act)
+
+
 def make_layer(shape: LayerShape) -> dict:
     """Draw one layer's inputs.  Returns CPU tensors keyed by argument name.
 

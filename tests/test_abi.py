@@ -89,6 +89,25 @@ def test_calls_reject_null_and_small_workspace(lib):
                               1 << 40, None) == -2        # NVFP4: the forward's decode path only
 
 
+def test_forward_residual_rejects_bad_norm_arguments(lib):
+    cfg = _cfg()
+    fake = ctypes.c_void_p(1 << 40)
+    w = moe.MoeWeights()
+    w.w_router = w.w_gate = w.w_up = w.w_down = 1 << 40
+    f = lib.moe_forward_residual
+    assert f(ctypes.byref(cfg), fake, None, ctypes.c_float(1e-6), ctypes.byref(w), fake, None, None,
+             fake, 1 << 40, None) == -1                                   # no norm weight
+    for eps in (-1.0, float("nan")):
+        assert f(ctypes.byref(cfg), fake, fake, ctypes.c_float(eps), ctypes.byref(w), fake, None,
+                 None, fake, 1 << 40, None) == -1
+    assert f(ctypes.byref(cfg), None, fake, ctypes.c_float(1e-6), ctypes.byref(w), fake, None,
+             None, fake, 1 << 40, None) == -1                             # no x
+    n = ctypes.c_size_t(0)
+    lib.moe_workspace_size(ctypes.byref(cfg), ctypes.byref(n))
+    assert f(ctypes.byref(cfg), fake, fake, ctypes.c_float(1e-6), ctypes.byref(w), fake, None,
+             None, fake, n.value - 256, None) == -3
+
+
 def test_nvfp4_supported_shapes(lib):
     n = ctypes.c_size_t(0)
     ok = [dict(wt="nvfp4"), dict(wt="nvfp4", T=1), dict(wt="nvfp4", T=16),

@@ -1,0 +1,194 @@
+"""GPU parity of the decoder step around the layer (moe_forward_residual:
+x_out = x + MoE(RMSNorm(x) * gamma)) against the oracle's residual_layer, on every
+expert path (decode kernels with the norm fused into the router, 4-bit decode, the
+skinny fused down, the skinny and matrix-core batch paths with the norm kernel, FP8,
+shared experts, fp32), in place, and as a three-layer stack captured in one HIP graph.
+
+bf16 x_out: the error of y = x_out - x beyond the final store's rounding meets the
+layer's rel L2 bound, and where y stays fp32 up to that store (the decode kernels) every
+element lands within one bf16 step of round(x + y_oracle); a wrong norm, a wrong gamma
+or a missing residual breaks both by far.  The fp32 layer checks y = x_out - x against
+the oracle's y directly.  The GPU's normalised rows are checked against the oracle's
+RMSNorm first, and the rest of the step is compared on those rows.  Routing is checked on the normalised rows with
+the near-tie rule."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import moe_oracle as mo
+from tests.helpers import TOL, TOL_F32_INTERNAL, check_routing, config_for, np_exact, oracle_experts, \
+    to_device
+
+pytestmark = pytest.mark.gpu
+S_ = synth.LayerShape
+EPS = 1e-6
+
+
+@pytest.fixture(scope="module")
+def moe():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mixture_experts_layer_route_amd as m
+    m.load_library()
+    return m
+
+
+def _bf16_step(v):
+    a = np.abs(v)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, 2.0 ** (e - 7), 2.0 ** -133)
+
+
+def _xn_from_ws(moe, cfg, ws, shape):
+    """The step's normalised rows, left in the workspace's last slot (256-byte aligned,
+    T*H elements of the activation type)."""
+    esz = 4 if shape.act == "f32" else 2
+    n = shape.T * shape.H * esz
+    o = moe.workspace_size(cfg) - ((n + 255) // 256) * 256
+    raw = ws[o:o + n].cpu()
+    return raw.view(torch.float32 if esz == 4 else torch.bfloat16).reshape(shape.T, shape.H)
+
+
+def _check_step(shape, cpu, gamma, x_in, x_out, g_ids, g_w, g_xn, fp32_y=False):
+    """The GPU's normalised rows against the oracle's RMSNorm (fp32 on the GPU, float64
+    in the oracle: a row element may land one step away where the exact value sits next
+    to a rounding boundary), then routing, weights and x_out from the oracle run on the
+    GPU's own rows."""
+    x64 = np_exact(x_in)
+    act = shape.act
+    xn_o = mo.round_act(mo.rms_norm(x64, np_exact(gamma), EPS), act)
+    xn = np_exact(g_xn)
+    if act == "bf16":
+        d = np.abs(xn - xn_o) / _bf16_step(xn_o)
+        assert d.max() <= 1.0 and np.mean(d > 0) < 1e-3, (d.max(), np.mean(d > 0))
+    else:
+        np.testing.assert_allclose(xn, xn_o, rtol=1e-6, atol=0)
+    l64 = mo.router_logits(xn, np_exact(cpu["w_router"]), np_exact(cpu["router_bias"]))
+    near, o_ids = check_routing(g_ids, g_w, l64, shape)
+    use_ids = np.where(near[:, None], g_ids, o_ids)
+    ref = mo.residual_layer(x64, np_exact(gamma), np_exact(cpu["w_router"]),
+                            np_exact(cpu["router_bias"]), oracle_experts(cpu), shape.G, shape.Gk,
+                            shape.k, act=act, eps=EPS, ids=use_ids, x_norm=xn)
+    got = np_exact(x_out)
+    if act == "bf16":
+        # beyond the final store's rounding (half a step of x_out), the error of y must meet
+        # the layer's bound; paths that keep y in fp32 up to that store (the decode kernels)
+        # must land within one step of round(x + y_oracle) everywhere
+        e = np.abs((got - x64) - ref["y"])
+        excess = np.maximum(e - 0.5 * _bf16_step(ref["x_out"]), 0.0)
+        err = float(np.linalg.norm(excess) / np.linalg.norm(ref["y"]))
+        steps = np.abs(got - ref["x_out"]) / _bf16_step(ref["x_out"])
+        print(f"{shape.name} T={shape.T}: y error beyond the store rounding {err:.3e}; "
+              f"max {steps.max():.0f} bf16 steps, {np.mean(steps > 0):.3%} elements off, "
+              f"near-ties {int(near.sum())}")
+        assert err <= TOL[shape.wt]
+        if fp32_y:
+            assert steps.max() <= 1.0
+    else:
+        err = mo.rel_l2(got - x64, ref["y"])
+        print(f"{shape.name} T={shape.T}: rel_l2(y) {err:.3e}")
+        assert err <= TOL_F32_INTERNAL
+
+
+def _run(moe, shape, inplace=False, scale=1.0):
+    cpu = synth.make_layer(shape)
+    if scale != 1.0:
+        cpu["x"] = (cpu["x"].float() * scale).to(cpu["x"].dtype)
+    gamma = synth.make_norm_weight(shape.H, shape.act, shape.seed + 1000)
+    dev = to_device(cpu)
+    g = gamma.cuda()
+    cfg = config_for(shape)
+    ws = moe.alloc_workspace(cfg)
+    ids = torch.empty((shape.T, shape.k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((shape.T, shape.k), dtype=torch.float32, device="cuda")
+    x = dev["x"].clone()
+    out = moe.forward_residual(cfg, x, g, dev, ws, x_out=x if inplace else None, eps=EPS,
+                               ids=ids, wts=wts)
+    torch.cuda.synchronize()
+    _check_step(shape, cpu, gamma, cpu["x"], out.cpu(), ids.cpu().numpy(), wts.cpu().numpy(),
+                _xn_from_ws(moe, cfg, ws, shape), fp32_y=shape.T <= 16 and shape.H <= 2048)
+
+
+CASES = [
+    # workload or explicit shape, T override
+    ("decode", None), ("decode", 1), ("decode", 16), ("decode_nvfp4", None), ("prefill", 300),
+    ("tiny", None), ("tiny", 300), ("fp8", 130), ("inkling", 100),
+]
+
+
+@pytest.mark.parametrize("name,T", CASES)
+def test_residual_step(moe, name, T):
+    print("case: residual", name, T, flush=True)
+    base = synth.WORKLOADS[name]
+    shape = base if T is None else base.with_tokens(T, 500 + T)
+    _run(moe, shape, scale=3.0 if shape.x_dist == "rms" else 1.0)
+
+
+def test_residual_step_skinny_fused_down(moe):
+    """T <= 16 with H beyond the decode kernels' range: skinny gate/up and the fused
+    skinny down + combine carry the residual."""
+    print("case: residual skinny fused", flush=True)
+    _run(moe, S_("wide", 4, 2560, 256, 16, 4, 2, 4, 0, "bf16", "bf16", "normal", 0.0, 61))
+
+
+@pytest.mark.parametrize("name,T", [("decode", None), ("prefill", 200)])
+def test_residual_step_in_place(moe, name, T):
+    print("case: residual in place", name, T, flush=True)
+    base = synth.WORKLOADS[name]
+    shape = base if T is None else base.with_tokens(T, 700)
+    _run(moe, shape, inplace=True)
+
+
+def test_three_layer_stack_in_one_graph(moe):
+    """Three decode blocks with their own weights, chained x0 -> x1 -> x2 -> x3 and
+    captured in one HIP graph; every replay equals the eager chain bit for bit, and each
+    block matches the oracle on the input the GPU gave it."""
+    print("case: residual stack graph", flush=True)
+    base = synth.WORKLOADS["decode"]
+    layers = []
+    for l in range(3):
+        shape = base.with_tokens(base.T, 800 + l)
+        cpu = synth.make_layer(shape)
+        gamma = synth.make_norm_weight(shape.H, shape.act, 900 + l)
+        dev = to_device(cpu)
+        layers.append((shape, cpu, gamma, dev, gamma.cuda(), moe.weights_struct(dev)))
+    shape0 = layers[0][0]
+    cfg = config_for(shape0)
+    ws = moe.alloc_workspace(cfg)
+    xs = [layers[0][3]["x"].clone()] + [torch.empty_like(layers[0][3]["x"]) for _ in range(3)]
+    ids = [torch.empty((shape0.T, shape0.k), dtype=torch.int32, device="cuda") for _ in range(3)]
+    wts = [torch.empty((shape0.T, shape0.k), dtype=torch.float32, device="cuda") for _ in range(3)]
+
+    def chain():
+        for l, (shape, cpu, gamma, dev, g, wst) in enumerate(layers):
+            moe.forward_residual(cfg, xs[l], g, dev, ws, x_out=xs[l + 1], eps=EPS, ids=ids[l],
+                                 wts=wts[l], wst=wst)
+
+    eager = []
+    for l, (shape, cpu, gamma, dev, g, wst) in enumerate(layers):   # one block at a time
+        moe.forward_residual(cfg, xs[l], g, dev, ws, x_out=xs[l + 1], eps=EPS, ids=ids[l],
+                             wts=wts[l], wst=wst)
+        torch.cuda.synchronize()
+        _check_step(shape, cpu, gamma, xs[l].cpu(), xs[l + 1].cpu(), ids[l].cpu().numpy(),
+                    wts[l].cpu().numpy(), _xn_from_ws(moe, cfg, ws, shape), fp32_y=True)
+    eager = [x.clone() for x in xs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        chain()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        chain()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for x in xs[1:]:
+            x.fill_(0)
+        graph.replay()
+        torch.cuda.synchronize()
+        for l in range(1, 4):
+            assert torch.equal(xs[l], eager[l]), (rep, l)
+        chain()                                   # eager work on the same workspace in between
+        torch.cuda.synchronize()
