@@ -34,7 +34,8 @@ WEIGHT_KEYS = ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down", "sh_gate"
 NV_KEYS = ("b_gate", "b_up", "b_down", "g_gate", "g_up", "g_down")
 # weight copies rotated per step so that the weight stream comes from HBM, not from
 # the 256 MB last-level cache (one NVFP4 copy of the decode layer is ~170 MB)
-DEFAULT_SETS = {"tiny": 1, "decode": 8, "prefill": 2, "fp8": 4, "inkling": 1, "decode_nvfp4": 16}
+DEFAULT_SETS = {"tiny": 1, "decode": 8, "prefill": 2, "fp8": 4, "inkling": 1, "decode_nvfp4": 16,
+                "decode_stack": 1}
 
 
 def log(*a):
@@ -47,7 +48,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode",
-                    choices=["tiny", "decode", "prefill", "fp8", "inkling", "decode_nvfp4"])
+                    choices=["tiny", "decode", "prefill", "fp8", "inkling", "decode_nvfp4",
+                             "decode_stack"])
     ap.add_argument("--sets", type=int, default=0, help="weight copies rotated per step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="host time budget for the oracle baseline (0 = skip)")
@@ -137,14 +139,19 @@ def oracle_experts(mo, cpu, f):
     return mo.Experts(*(f(cpu[n]) for n in WEIGHT_KEYS), nv=nv, sh_nv=sh_nv)
 
 
+def blas_threads():
+    """Threads numpy's BLAS runs the oracle with."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        return os.cpu_count()
+
+
 def cpu_baseline(shape, cpu, budget_s):
     """The float64 oracle, as it stands, on a bounded sample of the same workload."""
     from oracle import moe_oracle as mo
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count()
+    threads = blas_threads()
     f = lambda t: None if t is None else (t.numpy() if t.dtype.itemsize == 1 else t.float().numpy())
     ex = oracle_experts(mo, cpu, f)
     x, wr, b = f(cpu["x"]), f(cpu["w_router"]), f(cpu["router_bias"])
@@ -164,6 +171,129 @@ def cpu_baseline(shape, cpu, budget_s):
                       f"(full routing + experts + combine, float64 numpy), {el:.1f} s"}
 
 
+def run_stack(args):
+    """The decoder step's 23 MoE blocks (x_{l+1} = x_l + MoE_l(RMSNorm_l(x_l))) for a
+    decode batch, captured in one HIP graph and replayed; the same chain launched eagerly
+    beside it.  Each block streams its own copy of the experts from HBM."""
+    import torch
+    import mixture_experts_layer_route_amd as moe
+    import synth
+    from oracle import moe_oracle as mo
+
+    shape = synth.WORKLOADS["decode_stack"]
+    L = synth.STACK_BLOCKS
+    eps = 1e-6
+    log(f"workload {shape}; {L} blocks")
+    cpu = synth.make_layer(shape)
+    base = {k: (None if v is None else v.cuda()) for k, v in cpu.items()}
+    blocks = []
+    for l in range(L):
+        d = {k: (v.clone() if k in WEIGHT_KEYS and v is not None else v) for k, v in base.items()}
+        router = synth.make_router(shape.E, shape.H, shape.act, 10_000 + l)
+        gamma = synth.make_norm_weight(shape.H, shape.act, 20_000 + l)
+        d["w_router"] = router.cuda()
+        blocks.append((d, moe.weights_struct(d), gamma.cuda(), router, gamma))
+    cfg = moe.make_config(shape.T, shape.H, shape.I, shape.E, shape.G, shape.Gk, shape.k,
+                          shape.S, shape.act, shape.wt)
+    ws = moe.alloc_workspace(cfg)
+    xs = [base["x"].clone()] + [torch.empty_like(base["x"]) for _ in range(L)]
+    ids = [torch.empty((shape.T, shape.k), dtype=torch.int32, device="cuda") for _ in range(L)]
+
+    def chain():
+        for l, (d, wst, g, _, _) in enumerate(blocks):
+            moe.forward_residual(cfg, xs[l], g, d, ws, x_out=xs[l + 1], eps=eps, ids=ids[l],
+                                 wst=wst)
+
+    chain()
+    torch.cuda.synchronize()
+    # parity per block on the GPU's own trajectory (oracle forced onto the GPU's ids)
+    f = lambda t: t.float().cpu().numpy()
+    ex = oracle_experts(mo, cpu, lambda t: None if t is None else
+                        (t.numpy() if t.dtype.itemsize == 1 else t.float().numpy()))
+    worst, U_tot = 0.0, 0
+    for l, (_, _, _, router, gamma) in enumerate(blocks):
+        g_ids = ids[l].cpu().numpy()
+        U_tot += int(np.unique(g_ids).size)
+        ref = mo.residual_layer(f(xs[l]), gamma.float().numpy(), router.float().numpy(), None, ex,
+                                shape.G, shape.Gk, shape.k, eps=eps, ids=g_ids)
+        e = np.abs(f(xs[l + 1]).astype(np.float64) - f(xs[l]) - ref["y"])
+        a = np.abs(ref["x_out"])
+        half_step = 0.5 * 2.0 ** (np.floor(np.log2(np.where(a > 0, a, 1.0))) - 7)
+        worst = max(worst, float(np.linalg.norm(np.maximum(e - half_step, 0.0))
+                                 / np.linalg.norm(ref["y"])))
+    log(f"parity over {L} blocks: worst rel_l2 of y beyond the bf16 store's rounding "
+        f"{worst:.3e}; touched experts {U_tot}")
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        chain()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        chain()
+    torch.cuda.synchronize()
+    K, W = args.steps, args.warmup
+    for _ in range(W):
+        graph.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(K):
+        graph.replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms_graph = start.elapsed_time(end) / K
+    start.record()
+    for _ in range(K):
+        chain()
+    end.record()
+    torch.cuda.synchronize()
+    ms_eager = start.elapsed_time(end) / K
+    log(f"stack step {ms_graph * 1e3:.1f} us in one graph ({ms_graph * 1e3 / L:.2f} us per "
+        f"block); eager launches {ms_eager * 1e3:.1f} us")
+    per_expert = 3 * shape.I * shape.H * 2
+    abytes = U_tot * per_expert + L * (shape.E * shape.H * 2 + shape.H * 2 + 2 * shape.T * shape.H * 2)
+    achieved = abytes / (ms_graph * 1e-3) / 1e9
+    res = {
+        "metric": METRIC, "value": round(shape.T / (ms_graph * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms_graph, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode_stack", "blocks": L, "T": shape.T, "H": shape.H,
+                   "I": shape.I, "E": shape.E, "G": shape.G, "Gk": shape.Gk, "k": shape.k,
+                   "touched_experts": U_tot},
+        "us_per_block": round(ms_graph * 1e3 / L, 2),
+        "ms_per_step_eager_launches": round(ms_eager, 5),
+        "parity_rel_l2_worst_block": float(f"{worst:.3e}"),   # beyond the bf16 store rounding
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": f"whole step: {L} blocks x (norm+logits, gate/up, down+combine+"
+                               "residual) in one graph",
+                     "per_launch": f"{abytes} B = {U_tot} touched experts x {per_expert} B + "
+                                   "router, norm weight and rows per block"},
+    }
+    if args.cpu_seconds > 0:
+        t0 = time.perf_counter()
+        reps = 0
+        xin = f(xs[0])
+        while True:
+            xc = xin
+            for l, (_, _, _, router, gamma) in enumerate(blocks):
+                xc = mo.residual_layer(xc, gamma.float().numpy(), router.float().numpy(), None,
+                                       ex, shape.G, shape.Gk, shape.k, eps=eps)["x_out"]
+            reps += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        el = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(reps * shape.T / el, 3), "unit": "tokens/s",
+                               "cores": blas_threads(), "kind": "oracle",
+                               "sample": f"{reps} x the oracle's {L}-block step on the same "
+                                         f"{shape.T} tokens (float64 numpy), {el:.1f} s"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -172,6 +302,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.workload == "decode_stack":
+        run_stack(args)
         return
     import torch
     import mixture_experts_layer_route_amd as moe

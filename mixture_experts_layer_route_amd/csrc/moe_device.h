@@ -107,6 +107,16 @@ template <typename TW> struct Chunk8;
 template <> struct Chunk8<bf16_t> {
   uint4 v;
   __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void store(bf16_t* p) const { *reinterpret_cast<uint4*>(p) = v; }
+  // element i = round(a[i] * r * g[i]) (fp32 products, then round to nearest even)
+  __device__ __forceinline__ void set(const float (&a)[8], float r, const float (&g)[8]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = uint32_t(f32_to_bf16(a[2 * i] * r * g[2 * i])) |
+             (uint32_t(f32_to_bf16(a[2 * i + 1] * r * g[2 * i + 1])) << 16);
+    v = make_uint4(w[0], w[1], w[2], w[3]);
+  }
   __device__ __forceinline__ void get(float (&o)[8]) const {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -121,6 +131,14 @@ template <> struct Chunk8<float> {
   __device__ __forceinline__ void load(const float* p) {
     a = *reinterpret_cast<const float4*>(p);
     b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ void store(float* p) const {
+    *reinterpret_cast<float4*>(p) = a;
+    *reinterpret_cast<float4*>(p + 4) = b;
+  }
+  __device__ __forceinline__ void set(const float (&x)[8], float r, const float (&g)[8]) {
+    a = make_float4(x[0] * r * g[0], x[1] * r * g[1], x[2] * r * g[2], x[3] * r * g[3]);
+    b = make_float4(x[4] * r * g[4], x[5] * r * g[5], x[6] * r * g[6], x[7] * r * g[7]);
   }
   __device__ __forceinline__ void get(float (&o)[8]) const {
     o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;

@@ -152,10 +152,13 @@ __global__ __launch_bounds__(256) void k_logits_few(const TA* __restrict__ x,
 
 // Router logits of a handful of tokens with the pre-layer RMSNorm fused in front:
 // x_n = round(x / sqrt(mean(x^2) + eps) * gamma) per token, l = x_n W_r^T (+ bias).
-// Every wave first computes the T inverse RMS values itself (the token rows are
-// small and cached), so no block waits on another; wave 0 of block 0 also stores
-// x_n, which the expert kernels read, so router and experts see the same rows.
-// grid = ceil(E/4), block = 256 (one wave per expert).
+// Each block normalises the T rows once into LDS (wave w takes tokens w, w+4, ...;
+// the same lane order and reduction as k_rmsnorm, so both paths produce the same
+// rows), then its four waves form one expert's dot products each from LDS.
+// T <= 16, H <= 2048 (the decode kernels' range).  Block 0
+// also stores x_n, which the expert kernels read, so router and experts see the same
+// rows.  The expert's router row is in flight during the normalisation.
+// grid = ceil(E/4), block = 256, dynamic LDS = T*H elements.
 template <typename TA>
 __global__ __launch_bounds__(256) void k_logits_few_norm(const TA* __restrict__ x,
                                                          const TA* __restrict__ gamma, float eps,
@@ -165,45 +168,56 @@ __global__ __launch_bounds__(256) void k_logits_few_norm(const TA* __restrict__ 
                                                          TA* __restrict__ xn_out, int T, int H,
                                                          int E) {
   constexpr int SMAX = 4;
-  const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (e >= E) return;                    // uniform over the wave; e = 0 is the writer
-  const bool writer = e == 0;
-  const TA* wrow = wr + int64_t(e) * H;
-  // the first slab of the router row and of gamma travel with the pre-pass loads
-  Chunk8<TA> wc0[SMAX], gc0[SMAX];
+  extern __shared__ __align__(16) unsigned char xn_raw[];
+  TA* xn_l = reinterpret_cast<TA*>(xn_raw);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int e = blockIdx.x * 4 + wv;
+  const TA* wrow = wr + int64_t(min(e, E - 1)) * H;
+  // one memory round trip: the router row, gamma and this wave's token rows (H <= 2048,
+  // T <= 16: at most four tokens of four 512-wide slabs per wave) load together
+  Chunk8<TA> wc0[SMAX], gc[SMAX], xc[4][SMAX];
 #pragma unroll
   for (int s = 0; s < SMAX; ++s) {
     const int h = s * 512 + lane * 8;
     if (h < H) {
       wc0[s].load(wrow + h);
-      gc0[s].load(gamma + h);
+      gc[s].load(gamma + h);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (wv + 4 * j < T) xc[j][s].load(x + int64_t(wv + 4 * j) * H + h);
     }
   }
-  float ss[16];
 #pragma unroll
-  for (int q = 0; q < 16; ++q) ss[q] = 0.f;
-  for (int hb = 0; hb < H; hb += 512 * SMAX) {
+  for (int j = 0; j < 4; ++j) {
+    const int q = wv + 4 * j;
+    if (q >= T) break;                   // uniform over the wave
+    float ss = 0.f;
 #pragma unroll
     for (int s = 0; s < SMAX; ++s) {
-      const int h = hb + s * 512 + lane * 8;
+      if (s * 512 + lane * 8 < H) {
+        float v[8];
+        xc[j][s].get(v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss = fmaf(v[i], v[i], ss);
+      }
+    }
+    const float rinv = 1.0f / sqrtf(wave_sum(ss) / float(H) + eps);
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s) {
+      const int h = s * 512 + lane * 8;
       if (h < H) {
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          if (q < T) {
-            float v[8];
-            load8(x + int64_t(q) * H + h, v);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) ss[q] = fmaf(v[i], v[i], ss[q]);
-          }
-        }
+        float v[8], gv[8];
+        xc[j][s].get(v);
+        gc[s].get(gv);
+        Chunk8<TA> o;
+        o.set(v, rinv, gv);
+        o.store(xn_l + q * H + h);
+        if (blockIdx.x == 0) o.store(xn_out + int64_t(q) * H + h);
       }
     }
   }
-  float rinv[16];
-#pragma unroll
-  for (int q = 0; q < 16; ++q)
-    rinv[q] = q < T ? 1.0f / sqrtf(wave_sum(ss[q]) / float(H) + eps) : 0.f;
+  __syncthreads();
+  if (e >= E) return;                    // uniform over the wave
   float acc[16];
 #pragma unroll
   for (int q = 0; q < 16; ++q) acc[q] = 0.f;
@@ -212,30 +226,14 @@ __global__ __launch_bounds__(256) void k_logits_few_norm(const TA* __restrict__ 
     for (int s = 0; s < SMAX; ++s) {
       const int h = hb + s * 512 + lane * 8;
       if (h < H) {
-        float wv[8], gv[8];
-        if (hb == 0) {
-          wc0[s].get(wv);
-          gc0[s].get(gv);
-        } else {
-          load8(wrow + h, wv);
-          load8(gamma + h, gv);
-        }
+        float wv8[8];
+        if (hb == 0) wc0[s].get(wv8); else load8(wrow + h, wv8);
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
           if (q < T) {
             float v[8];
-            load8(x + int64_t(q) * H + h, v);
-            TA nb[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              nb[i] = from_f32<TA>(v[i] * rinv[q] * gv[i]);
-              acc[q] = fmaf(to_f32<TA>(nb[i]), wv[i], acc[q]);
-            }
-            if (writer) {
-              TA* o = xn_out + int64_t(q) * H + h;
-#pragma unroll
-              for (int i = 0; i < 8; ++i) o[i] = nb[i];
-            }
+            load8(xn_l + q * H + h, v);
+            acc[q] = dot8(v, wv8, acc[q]);
           }
         }
       }
@@ -273,9 +271,9 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const TA* __restrict__ x,
     float v[8], gv[8];
     load8(xr + h, v);
     load8(gamma + h, gv);
-    TA* o = xn + t * H + h;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = from_f32<TA>(v[i] * rinv * gv[i]);
+    Chunk8<TA> o;
+    o.set(v, rinv, gv);
+    o.store(xn + t * H + h);
   }
 }
 
@@ -293,13 +291,15 @@ int launch_rmsnorm(const Plan& p, const void* x, const void* gamma, float eps, v
 
 int launch_logits_norm(const Plan& p, const void* x, const void* gamma, float eps, const void* wr,
                        const float* bias, float* logits, void* xn, hipStream_t st) {
+  if (p.T > 16 || p.H > 2048) return MOE_ERR_UNSUPPORTED;   // the decode path's range only
   const dim3 grid(unsigned((p.E + 3) / 4));
+  const size_t lds = size_t(p.T) * p.H * (p.act == MOE_F32 ? 4 : 2);
   if (p.act == MOE_F32)
-    hipLaunchKernelGGL(k_logits_few_norm<float>, grid, dim3(256), 0, st, (const float*)x,
+    hipLaunchKernelGGL(k_logits_few_norm<float>, grid, dim3(256), lds, st, (const float*)x,
                        (const float*)gamma, eps, (const float*)wr, bias, logits, (float*)xn,
                        int(p.T), p.H, p.E);
   else
-    hipLaunchKernelGGL(k_logits_few_norm<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)x,
+    hipLaunchKernelGGL(k_logits_few_norm<bf16_t>, grid, dim3(256), lds, st, (const bf16_t*)x,
                        (const bf16_t*)gamma, eps, (const bf16_t*)wr, bias, logits, (bf16_t*)xn,
                        int(p.T), p.H, p.E);
   return check_launch();

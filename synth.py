@@ -16,6 +16,9 @@ Shapes and value distributions follow the five workloads of the layer:
   inkling   T=4096, H=2048, I=512, E=256 ungrouped, k=6, 2 shared experts
   decode_nvfp4  the decode layer with NVFP4 experts (4-bit E2M1 codes, an E4M3
             scale per 16 inputs, an fp32 scale per expert matrix)
+  decode_stack  23 decode MoE blocks of a decoder step (x + MoE(RMSNorm(x)) each): the
+            decode layer's experts copied per block, a router and a norm weight
+            drawn per block (make_router, make_norm_weight)
 
 The Ling-3.0-tiny layer shape (128 routed experts split into 8 groups of 16,
 of which 4 groups survive per token; hidden size 1536; SwiGLU experts) comes
@@ -79,7 +82,10 @@ WORKLOADS = {
                           act=BF16, wt=BF16, x_dist="normal", bias_std=0.0, seed=4),
     "decode_nvfp4": LayerShape("decode_nvfp4", T=4, H=1536, I=512, E=128, G=8, Gk=4, k=8,
                                S=0, act=BF16, wt=NVFP4, x_dist="rms", bias_std=0.0, seed=5),
+    "decode_stack": LayerShape("decode_stack", T=4, H=1536, I=512, E=128, G=8, Gk=4, k=8,
+                               S=0, act=BF16, wt=BF16, x_dist="normal", bias_std=0.0, seed=6),
 }
+STACK_BLOCKS = 23      # MoE blocks of the 24-layer stack (layer 0 is dense)
 
 FP8_BLOCK = 128
 E4M3_MAX = 448.0
@@ -159,6 +165,13 @@ def make_norm_weight(H: int, act: str, seed: int) -> torch.Tensor:
     stored in the activation type."""
     rng = np.random.default_rng(seed)
     return _store(np.float32(1.0) + np.float32(0.1) * rng.standard_normal(H, dtype=np.float32), act)
+
+
+def make_router(E: int, H: int, act: str, seed: int, std: float = 0.05) -> torch.Tensor:
+    """Router weight [E, H] ~ N(0, std) drawn in float32 from ``default_rng(seed)``, stored
+    in the activation type (the decoder stack draws one per block)."""
+    rng = np.random.default_rng(seed)
+    return _store(rng.standard_normal((E, H), dtype=np.float32) * np.float32(std), act)
 
 
 def make_layer(shape: LayerShape) -> dict:
