@@ -79,9 +79,7 @@ typedef enum {
  *   (MOE_F32, MOE_F32), (MOE_BF16, MOE_BF16), (MOE_BF16, MOE_E4M3_B128),
  *   (MOE_BF16, MOE_NVFP4).
  * Constraints: T >= 1; H, I >= 1 and multiples of 8 (of 128 for e4m3 experts, of
- * 32 for NVFP4 experts); NVFP4 experts serve decode batches only: T <= 16,
- * H <= 2048, I <= 1024, k + S <= 32, moe_forward only (moe_expert_ffn returns
- * MOE_ERR_UNSUPPORTED for them);
+ * 32 for NVFP4 experts, which also need H <= 2048, I <= 1024 and k + S <= 32);
  * E >= 1; G >= 1 with E % G == 0; 1 <= Gk <= G; 1 <= k <= Gk * E / G;
  * k <= 16; E + S <= 1024; T * (k + S) < 2^31.
  */

@@ -172,7 +172,7 @@ __device__ __forceinline__ void decode_gateup_nv(const DecodeArgs& a, const bf16
       e4m3_pair(b.su[s], su0[s], su1[s]);
     }
     for (int r = off_l[e]; r < off_l[e + 1]; ++r) {
-      const bf16_t* xr = xs + rt_l[r] * H;
+      const bf16_t* xr = xs + int64_t(rt_l[r]) * H;
       float ag = 0.f, au = 0.f;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
@@ -633,6 +633,242 @@ __global__ __launch_bounds__(256) void k_decode_down_nv(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// NVFP4 experts for batches beyond the decode kernels (the permutation comes from
+// global memory: offsets, the active-expert list and meta[0] = its length).
+//
+// Dot of 16 bf16 pairs held as dwords with 16 bf16 activation pairs (two chains).
+__device__ __forceinline__ float dot8_bf16x2(const uint32_t* w, const uint32_t* x) {
+  float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+  for (int p = 0; p < 8; p += 2) {
+    d0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[p]),
+                                         __builtin_bit_cast(bf16x2_t, x[p]), d0, false);
+    d1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[p + 1]),
+                                         __builtin_bit_cast(bf16x2_t, x[p + 1]), d1, false);
+  }
+  return d0 + d1;
+}
+
+// 16 bytes of E2M1 codes -> 16 bf16 pairs (exact: every E2M1 value is a bf16 value).
+__device__ __forceinline__ void fp4x32_to_bf16(const uint4& c, uint32_t (&o)[16]) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[4 * i + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], 1.0f, 0));
+    o[4 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], 1.0f, 1));
+    o[4 * i + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], 1.0f, 2));
+    o[4 * i + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], 1.0f, 3));
+  }
+}
+
+// Gate/up: item = (active expert, 4 consecutive rows of I), one 16-lane DPP row per
+// weight row as in the decode kernel.  The item's codes are converted once to bf16
+// pairs in registers; the expert's token rows then stream through with the next row's
+// activations in flight while the current one is multiplied.
+template <int NS>
+__global__ __launch_bounds__(256) void k_nv_gateup_batch(DecodeArgs a,
+                                                         const int32_t* __restrict__ active,
+                                                         const int32_t* __restrict__ meta) {
+  const int H = a.H, I = a.I, E = a.E;
+  const int H2 = H / 2, H16 = H / 16, HC = H / 32;
+  const int lane = threadIdx.x & 63, q = lane >> 4, cc = lane & 15;
+  const int ipe = I / 4;
+  const int total = meta[0] * ipe;
+  const int64_t cstr = int64_t(I) * H2, bstr = int64_t(I) * H16;
+  const bf16_t* x = static_cast<const bf16_t*>(a.x);
+  const uint8_t* wgp = static_cast<const uint8_t*>(a.wg);
+  const uint8_t* wup = static_cast<const uint8_t*>(a.wu);
+  const uint8_t* shg = static_cast<const uint8_t*>(a.shg);
+  const uint8_t* shu = static_cast<const uint8_t*>(a.shu);
+  for (int item = blockIdx.x * 4 + (threadIdx.x >> 6); item < total; item += gridDim.x * 4) {
+    const int u = item / ipe, i0 = (item - u * ipe) * 4, row = i0 + q;
+    const int e = active[u];
+    uint32_t wg[NS][16], wu[NS][16];
+    float sg[NS][2], su[NS][2];
+    {
+      const uint8_t* gp = nv_expert(wgp, shg, e, E, cstr) + int64_t(row) * H2;
+      const uint8_t* up = nv_expert(wup, shu, e, E, cstr) + int64_t(row) * H2;
+      const uint8_t* gs = nv_expert(a.bg, a.shbg, e, E, bstr) + int64_t(row) * H16;
+      const uint8_t* us = nv_expert(a.bu, a.shbu, e, E, bstr) + int64_t(row) * H16;
+      uint4 cg[NS], cu[NS];
+      uint32_t bg2[NS], bu2[NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int c = cc + 16 * s;
+        cg[s] = cu[s] = make_uint4(0u, 0u, 0u, 0u);
+        bg2[s] = bu2[s] = 0u;
+        if (c < HC) {
+          cg[s] = *reinterpret_cast<const uint4*>(gp + c * 16);
+          cu[s] = *reinterpret_cast<const uint4*>(up + c * 16);
+          bg2[s] = *reinterpret_cast<const uint16_t*>(gs + c * 2);
+          bu2[s] = *reinterpret_cast<const uint16_t*>(us + c * 2);
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        fp4x32_to_bf16(cg[s], wg[s]);
+        fp4x32_to_bf16(cu[s], wu[s]);
+        e4m3_pair(bg2[s], sg[s][0], sg[s][1]);
+        e4m3_pair(bu2[s], su[s][0], su[s][1]);
+      }
+    }
+    const float ggs = e < E ? a.gg[e] : a.shgg[e - E];
+    const float gus = e < E ? a.gu[e] : a.shgu[e - E];
+    const int r0 = a.offsets[e], r1 = a.offsets[e + 1];
+    auto loadx = [&](int r, uint4 (&xv)[NS][4]) {
+      const bf16_t* xr = x + int64_t(a.row_token[r]) * H;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int c = cc + 16 * s;
+        if (c < HC) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) xv[s][v] = *reinterpret_cast<const uint4*>(xr + c * 32 + v * 8);
+        }
+      }
+    };
+    auto dot = [&](int r, const uint4 (&xv)[NS][4]) {
+      float ag = 0.f, au = 0.f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        if (cc + 16 * s < HC) {
+          uint32_t xw[16];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            xw[4 * v] = xv[s][v].x; xw[4 * v + 1] = xv[s][v].y;
+            xw[4 * v + 2] = xv[s][v].z; xw[4 * v + 3] = xv[s][v].w;
+          }
+          ag = fmaf(dot8_bf16x2(wg[s], xw), sg[s][0], ag);
+          au = fmaf(dot8_bf16x2(wu[s], xw), su[s][0], au);
+          ag = fmaf(dot8_bf16x2(wg[s] + 8, xw + 8), sg[s][1], ag);
+          au = fmaf(dot8_bf16x2(wu[s] + 8, xw + 8), su[s][1], au);
+        }
+      }
+      ag = row_sum(ag) * ggs;
+      au = row_sum(au) * gus;
+      if (cc == 0) a.h[int64_t(r) * I + i0 + q] = silu(ag) * au;
+    };
+    uint4 xa[NS][4], xb[NS][4];
+    if (r0 < r1) loadx(r0, xa);
+    for (int r = r0; r < r1; r += 2) {
+      if (r + 1 < r1) loadx(r + 1, xb);
+      dot(r, xa);
+      if (r + 1 >= r1) break;
+      if (r + 2 < r1) loadx(r + 2, xa);
+      dot(r + 1, xb);
+    }
+  }
+}
+
+// Down: item = (active expert, 4*RG output columns), expert-major into unweighted
+// fp32 rows y_perm[r, n] = h[r] . Wd[e][n].  The item's codes become fp32 weights
+// once (E2M1 value times its e4m3 block scale, exact in fp32; the matrix scale
+// multiplies the reduced sum), then the expert's h rows stream through with the next
+// row in flight.
+template <int NSD, int RG>
+__global__ __launch_bounds__(256) void k_nv_down_batch(DecodeArgs a,
+                                                       const int32_t* __restrict__ active,
+                                                       const int32_t* __restrict__ meta,
+                                                       float* __restrict__ y_perm) {
+  constexpr int NRB = 4 * RG;
+  const int H = a.H, I = a.I, E = a.E;
+  const int I2 = I / 2, I16 = I / 16, IC = I / 32;
+  const int lane = threadIdx.x & 63, q = lane >> 4, cc = lane & 15;
+  const int nb = (H + NRB - 1) / NRB;
+  const int total = meta[0] * nb;
+  const int64_t cstr = int64_t(H) * I2, bstr = int64_t(H) * I16;
+  const uint8_t* wdp = static_cast<const uint8_t*>(a.wd);
+  const uint8_t* shd = static_cast<const uint8_t*>(a.shd);
+  for (int item = blockIdx.x * 4 + (threadIdx.x >> 6); item < total; item += gridDim.x * 4) {
+    const int u = item / nb, n0 = (item - u * nb) * NRB;
+    const int e = active[u];
+    float wf[RG][NSD][32];
+    {
+      const uint8_t* cp = nv_expert(wdp, shd, e, E, cstr);
+      const uint8_t* bp = nv_expert(a.bd, a.shbd, e, E, bstr);
+      uint4 wc[RG][NSD];
+      uint32_t ws2[RG][NSD];
+#pragma unroll
+      for (int g = 0; g < RG; ++g) {
+        const int n = n0 + 4 * g + q;
+#pragma unroll
+        for (int s = 0; s < NSD; ++s) {
+          const int c = cc + 16 * s;
+          wc[g][s] = make_uint4(0u, 0u, 0u, 0u);
+          ws2[g][s] = 0u;
+          if (n < H && c < IC) {
+            wc[g][s] = *reinterpret_cast<const uint4*>(cp + int64_t(n) * I2 + c * 16);
+            ws2[g][s] = *reinterpret_cast<const uint16_t*>(bp + int64_t(n) * I16 + c * 2);
+          }
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < RG; ++g)
+#pragma unroll
+        for (int s = 0; s < NSD; ++s) {
+          float s0, s1;
+          e4m3_pair(ws2[g][s], s0, s1);
+          const uint32_t w[4] = {wc[g][s].x, wc[g][s].y, wc[g][s].z, wc[g][s].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float sc = i < 2 ? s0 : s1;
+            const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], 1.0f, 0);
+            const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], 1.0f, 1);
+            const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], 1.0f, 2);
+            const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], 1.0f, 3);
+            wf[g][s][8 * i + 0] = p0[0] * sc; wf[g][s][8 * i + 1] = p0[1] * sc;
+            wf[g][s][8 * i + 2] = p1[0] * sc; wf[g][s][8 * i + 3] = p1[1] * sc;
+            wf[g][s][8 * i + 4] = p2[0] * sc; wf[g][s][8 * i + 5] = p2[1] * sc;
+            wf[g][s][8 * i + 6] = p3[0] * sc; wf[g][s][8 * i + 7] = p3[1] * sc;
+          }
+        }
+    }
+    const float gd = e < E ? a.gd[e] : a.shgd[e - E];
+    const int r0 = a.offsets[e], r1 = a.offsets[e + 1];
+    auto loadh = [&](int r, float4 (&hv)[NSD][8]) {
+#pragma unroll
+      for (int s = 0; s < NSD; ++s) {
+        const int c = cc + 16 * s;
+        if (c < IC) {
+          const float4* hp = reinterpret_cast<const float4*>(a.h + int64_t(r) * I + c * 32);
+#pragma unroll
+          for (int v = 0; v < 8; ++v) hv[s][v] = hp[v];
+        }
+      }
+    };
+    auto dot = [&](int r, const float4 (&hv)[NSD][8]) {
+#pragma unroll
+      for (int g = 0; g < RG; ++g) {
+        float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+        for (int s = 0; s < NSD; ++s) {
+          if (cc + 16 * s < IC) {
+#pragma unroll
+            for (int v = 0; v < 8; ++v) {
+              d0 = fmaf(wf[g][s][4 * v + 0], hv[s][v].x, d0);
+              d1 = fmaf(wf[g][s][4 * v + 1], hv[s][v].y, d1);
+              d0 = fmaf(wf[g][s][4 * v + 2], hv[s][v].z, d0);
+              d1 = fmaf(wf[g][s][4 * v + 3], hv[s][v].w, d1);
+            }
+          }
+        }
+        const float d = row_sum(d0 + d1) * gd;
+        const int n = n0 + 4 * g + q;
+        if (cc == 0 && n < H) y_perm[int64_t(r) * H + n] = d;
+      }
+    };
+    float4 ha[NSD][8], hb[NSD][8];
+    if (r0 < r1) loadh(r0, ha);
+    for (int r = r0; r < r1; r += 2) {
+      if (r + 1 < r1) loadh(r + 1, hb);
+      dot(r, ha);
+      if (r + 1 >= r1) break;
+      if (r + 2 < r1) loadh(r + 2, ha);
+      dot(r + 1, hb);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 static size_t decode_lds(const Plan& p) {
   const size_t tsize = p.act == MOE_F32 ? 4 : 2;
   return ((size_t(p.T) * p.H * tsize + 15) & ~size_t(15)) +
@@ -701,6 +937,58 @@ static int launch_decode_nv_t(const Plan& p, const DecodeArgs& a, hipStream_t st
     launch_kernel(p, kTimeDown, k2, dim3(int(std::min<int64_t>(b2, items(1)))), dim3(256), 0, st, a);
   }
   return check_launch();
+}
+
+static DecodeArgs nv_batch_args(const Plan& p, const void* x, const int32_t* row_token,
+                                const int32_t* offsets, const moe_weights* w, float* h) {
+  DecodeArgs a{};
+  a.x = x;
+  a.wg = w->w_gate; a.wu = w->w_up; a.wd = w->w_down;
+  a.shg = w->sh_gate; a.shu = w->sh_up; a.shd = w->sh_down;
+  a.bg = w->b_gate; a.bu = w->b_up; a.bd = w->b_down;
+  a.shbg = w->sh_b_gate; a.shbu = w->sh_b_up; a.shbd = w->sh_b_down;
+  a.gg = w->g_gate; a.gu = w->g_up; a.gd = w->g_down;
+  a.shgg = w->sh_g_gate; a.shgu = w->sh_g_up; a.shgd = w->sh_g_down;
+  a.offsets = const_cast<int32_t*>(offsets);
+  a.row_token = const_cast<int32_t*>(row_token);
+  a.h = h;
+  a.T = int(std::min<int64_t>(p.T, INT32_MAX)); a.H = p.H; a.I = p.I; a.E = p.E; a.S = p.S;
+  return a;
+}
+
+int launch_nv_gateup_batch(const Plan& p, const void* x, const int32_t* row_token,
+                           const int32_t* offsets, const int32_t* active, const int32_t* meta,
+                           const moe_weights* w, float* h, hipStream_t st) {
+  const DecodeArgs a = nv_batch_args(p, x, row_token, offsets, w, h);
+  const int ns = (p.H + 511) / 512;
+  const int64_t items = p.max_active * (p.I / 4);
+  auto go = [&](auto kern) {
+    int b = 0;
+    MOE_TRY(persistent_blocks(reinterpret_cast<const void*>(kern), 0, &b));
+    const int grid = int(std::max<int64_t>(1, std::min<int64_t>(b, (items + 3) / 4)));
+    launch_kernel(p, kTimeGateUp, kern, dim3(grid), dim3(256), 0, st, a, active, meta);
+    return check_launch();
+  };
+  if (ns <= 1) return go(k_nv_gateup_batch<1>);
+  if (ns == 2) return go(k_nv_gateup_batch<2>);
+  if (ns == 3) return go(k_nv_gateup_batch<3>);
+  return go(k_nv_gateup_batch<4>);
+}
+
+int launch_nv_down_batch(const Plan& p, const float* h, const int32_t* offsets,
+                         const int32_t* active, const int32_t* meta, const moe_weights* w,
+                         float* y_perm, hipStream_t st) {
+  const DecodeArgs a = nv_batch_args(p, nullptr, nullptr, offsets, w, const_cast<float*>(h));
+  auto go = [&](auto kern, int rg) {
+    int b = 0;
+    MOE_TRY(persistent_blocks(reinterpret_cast<const void*>(kern), 0, &b));
+    const int64_t items = p.max_active * ((p.H + 4 * rg - 1) / (4 * rg));
+    const int grid = int(std::max<int64_t>(1, std::min<int64_t>(b, (items + 3) / 4)));
+    launch_kernel(p, kTimeDown, kern, dim3(grid), dim3(256), 0, st, a, active, meta, y_perm);
+    return check_launch();
+  };
+  if (p.I <= 512) return go(k_nv_down_batch<1, 2>, 2);
+  return go(k_nv_down_batch<2, 1>, 1);
 }
 
 int launch_decode_ffn(const Plan& p, const void* x, const float* logits, const moe_weights* w,

@@ -294,6 +294,8 @@ static void gateup(const Plan& p, const void* x, const int32_t* rt, const int32_
 int launch_gateup_skinny(const Plan& p, const void* x, const int32_t* row_token,
                          const int32_t* offsets, const int32_t* active, const int32_t* meta,
                          const moe_weights* w, float* h, hipStream_t st) {
+  if (p.wt == MOE_NVFP4)
+    return launch_nv_gateup_batch(p, x, row_token, offsets, active, meta, w, h, st);
   if (p.wt == MOE_F32)
     gateup<float, float>(p, x, row_token, offsets, active, meta, w, h, st);
   else
@@ -304,6 +306,7 @@ int launch_gateup_skinny(const Plan& p, const void* x, const int32_t* row_token,
 int launch_down_skinny(const Plan& p, const float* h, const int32_t* offsets,
                        const int32_t* active, const int32_t* meta, const moe_weights* w,
                        float* y_perm, hipStream_t st) {
+  if (p.wt == MOE_NVFP4) return launch_nv_down_batch(p, h, offsets, active, meta, w, y_perm, st);
   constexpr int NR = 2, RC = 4;
   dim3 grid(unsigned(p.max_active), unsigned((p.H + 4 * NR - 1) / (4 * NR)));
   if (p.wt == MOE_F32)

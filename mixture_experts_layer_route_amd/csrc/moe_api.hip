@@ -40,9 +40,8 @@ int make_plan(const moe_config* c, Plan* p) {
   if (!(dense32 || dense16 || fp8 || nv4)) return MOE_ERR_UNSUPPORTED;
   if (H % 8 || I % 8) return MOE_ERR_UNSUPPORTED;
   if (fp8 && (H % 128 || I % 128)) return MOE_ERR_UNSUPPORTED;
-  // NVFP4 experts: the decode kernels only (a handful of tokens)
-  if (nv4 && (H % 32 || I % 32 || T > 16 || H > 2048 || I > 1024 || k + S > 32))
-    return MOE_ERR_UNSUPPORTED;
+  // NVFP4 experts: the decode kernels (a handful of tokens) or the expert-major ones
+  if (nv4 && (H % 32 || I % 32 || H > 2048 || I > 1024 || k + S > 32)) return MOE_ERR_UNSUPPORTED;
   if (E % G || G > 64 || Gk > G) return MOE_ERR_UNSUPPORTED;
   if (int64_t(k) > int64_t(Gk) * (E / G) || k > 16) return MOE_ERR_UNSUPPORTED;
   if (E + S > 1024) return MOE_ERR_UNSUPPORTED;
@@ -59,9 +58,10 @@ int make_plan(const moe_config* c, Plan* p) {
   q.skinny = dense32 || nv4 || (dense16 && (q.Rk <= 8 * int64_t(E) || !mfma_shape));
   q.small_route = T <= 64 && T * k <= 256;
   q.fused_down = q.skinny && T <= 16;
+  // NVFP4 batches the decode kernels do not take run the expert-major kernels + combine
+  if (nv4 && q.fused_down && !decode_ffn_ok(q)) q.fused_down = false;
   q.max_active = std::min<int64_t>(E, q.Rk) + S;
   q.bm = gemm_tile_rows(q);
-  if (nv4 && !(q.fused_down && decode_ffn_ok(q))) return MOE_ERR_UNSUPPORTED;
   q.max_tiles = q.Rk / q.bm + std::min<int64_t>(E, q.Rk) + int64_t(S) * ((T + q.bm - 1) / q.bm);
 
   size_t o = 0;
@@ -190,7 +190,6 @@ int moe_expert_ffn(const moe_config* cfg, const void* x, const int32_t* expert_o
                    size_t ws_bytes, hipStream_t stream) {
   Plan p;
   MOE_TRY(make_plan(cfg, &p));
-  if (p.wt == MOE_NVFP4) return MOE_ERR_UNSUPPORTED;   // NVFP4 experts: moe_forward only
   if (!x || !expert_offsets || !row_token || !y_perm) return MOE_ERR_ARG;
   MOE_TRY(check_experts(p, w));
   MOE_TRY(check_ws(p, ws, ws_bytes));

@@ -88,6 +88,14 @@ int gemm_tile_rows(const Plan& p);
 int launch_decode_ffn(const Plan& p, const void* x, const float* logits, const moe_weights* w,
                       int32_t* ids, float* wts, int32_t* offsets, int32_t* row_token,
                       int32_t* inv, float* h, const void* res, void* y, hipStream_t st);
+// NVFP4 experts beyond the decode kernels: expert-major gate/up (h fp32) and down
+// (unweighted fp32 rows), reading the permutation from global memory
+int launch_nv_gateup_batch(const Plan& p, const void* x, const int32_t* row_token,
+                           const int32_t* offsets, const int32_t* active, const int32_t* meta,
+                           const moe_weights* w, float* h, hipStream_t st);
+int launch_nv_down_batch(const Plan& p, const float* h, const int32_t* offsets,
+                         const int32_t* active, const int32_t* meta, const moe_weights* w,
+                         float* y_perm, hipStream_t st);
 int launch_gateup_skinny(const Plan& p, const void* x, const int32_t* row_token,
                          const int32_t* offsets, const int32_t* active, const int32_t* meta,
                          const moe_weights* w, float* h, hipStream_t st);

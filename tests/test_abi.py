@@ -86,7 +86,7 @@ def test_calls_reject_null_and_small_workspace(lib):
     assert lib.moe_forward(ctypes.byref(cfg4), fake, ctypes.byref(w), fake, None, None, fake,
                            1 << 40, None) == -1
     assert lib.moe_expert_ffn(ctypes.byref(cfg4), fake, fake, fake, ctypes.byref(w), fake, fake,
-                              1 << 40, None) == -2        # NVFP4: the forward's decode path only
+                              1 << 40, None) == -1        # and so does the expert FFN entry
 
 
 def test_forward_residual_rejects_bad_norm_arguments(lib):
@@ -115,12 +115,12 @@ def test_nvfp4_supported_shapes(lib):
           dict(wt="nvfp4", T=8, H=1024, I=256, E=256, G=1, Gk=1, k=6, S=2),
           dict(wt="nvfp4", H=512, I=1024, E=32, G=1, Gk=1, k=4, S=1),
           dict(wt="nvfp4", T=3, H=512, I=256, E=256, G=64, Gk=8, k=16),
-          dict(wt="nvfp4", T=12, H=2048, I=256, E=16, G=4, Gk=2, k=4)]
+          dict(wt="nvfp4", T=12, H=2048, I=256, E=16, G=4, Gk=2, k=4),
+          dict(wt="nvfp4", T=17), dict(wt="nvfp4", T=8192), dict(wt="nvfp4", T=16, H=2048)]
     for kw in ok:
         assert lib.moe_workspace_size(ctypes.byref(_cfg(**kw)), ctypes.byref(n)) == 0, kw
-    bad = [dict(wt="nvfp4", T=17), dict(wt="nvfp4", H=1520), dict(wt="nvfp4", I=496),
-           dict(wt="nvfp4", act="f32"), dict(wt="nvfp4", H=4096), dict(wt="nvfp4", I=2048),
-           dict(wt="nvfp4", T=16, H=2048)]              # token rows beyond the LDS budget
+    bad = [dict(wt="nvfp4", H=1520), dict(wt="nvfp4", I=496), dict(wt="nvfp4", act="f32"),
+           dict(wt="nvfp4", H=4096), dict(wt="nvfp4", I=2048), dict(wt="nvfp4", k=8, S=25)]
     for kw in bad:
         assert lib.moe_workspace_size(ctypes.byref(_cfg(**kw)), ctypes.byref(n)) == -2, kw
 

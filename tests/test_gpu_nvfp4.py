@@ -1,15 +1,17 @@
-"""GPU parity of the decode path with NVFP4 experts (4-bit E2M1 codes, an e4m3 scale per
+"""GPU parity of the layer with NVFP4 experts (4-bit E2M1 codes, an e4m3 scale per
 16 inputs, an fp32 scale per expert matrix) against the float64 oracle on the same
 stored codes, on the decode workload, its token-count edges, shared experts, the
 Inkling-shaped router, hidden/intermediate sizes that leave lanes of the 16-lane
-rows idle, and a skewed router.  Same bar as the other layers: exact ids where the
+rows idle, and a skewed router; then batches beyond the decode kernels (the
+expert-major kernels, on both permutation paths) and the expert-FFN entry point.  Same bar as the other layers: exact ids where the
 logit margin is clear, rel L2 of y within the bf16 bound."""
 import numpy as np
 import pytest
 import torch
 
 import synth
-from tests.helpers import config_for, to_device
+from oracle import moe_oracle as mo
+from tests.helpers import config_for, np_exact, oracle_experts, to_device
 from tests.test_gpu_parity import _forward_check
 
 pytestmark = pytest.mark.gpu
@@ -116,3 +118,49 @@ def test_nvfp4_deterministic_and_graph(moe):
     torch.cuda.synchronize()
     assert torch.equal(y, ref2)
     assert not torch.equal(ref2, y1)
+
+
+@pytest.mark.parametrize("T", [17, 40, 64, 300, 1200])
+def test_forward_nvfp4_batch(moe, T):
+    """Beyond 16 tokens: selection + permutation (one block up to 64 tokens, the scan
+    beyond), the expert-major 4-bit kernels and the combine."""
+    print("case: nvfp4 batch", T, flush=True)
+    shape, cpu, dev = _decode_layer(T, 600 + T)
+    _forward_check(moe, shape, cpu, dev)
+
+
+BATCH_CASES = [
+    ("nvb_ling_sh", 100, 1536, 512, 128, 8, 4, 8, 2, "bf16", "nvfp4", "rms", 0.0, 71),
+    ("nvb_ragged", 200, 640, 384, 64, 4, 2, 4, 0, "bf16", "nvfp4", "rms", 0.3, 72),
+    ("nvb_i1024", 150, 512, 1024, 32, 1, 1, 4, 1, "bf16", "nvfp4", "normal", 0.0, 73),
+    ("nvb_h2048_t16", 16, 2048, 256, 16, 4, 2, 4, 0, "bf16", "nvfp4", "rms", 0.0, 74),
+]
+
+
+@pytest.mark.parametrize("case", BATCH_CASES, ids=[c[0] for c in BATCH_CASES])
+def test_forward_nvfp4_batch_edge(moe, case):
+    print("case: nvfp4 batch edge", case[0], flush=True)
+    shape = S_(*case)
+    cpu = synth.make_layer(shape)
+    _forward_check(moe, shape, cpu, to_device(cpu))
+
+
+def test_expert_ffn_nvfp4(moe):
+    """moe_expert_ffn on the oracle's own permutation: unweighted fp32 rows."""
+    print("case: nvfp4 expert_ffn", flush=True)
+    shape = S_("nvb_ffn", 130, 1536, 512, 128, 8, 4, 8, 1, "bf16", "nvfp4", "rms", 0.0, 75)
+    cpu = synth.make_layer(shape)
+    dev = to_device(cpu)
+    ex = oracle_experts(cpu)
+    x64 = np_exact(cpu["x"])
+    ids, _, _ = mo.route(x64, np_exact(cpu["w_router"]), None, shape.G, shape.Gk, shape.k)
+    off, rt, _ = mo.permute(ids, shape.E, shape.S)
+    cfg = config_for(shape)
+    ws = moe.alloc_workspace(cfg)
+    yp = moe.expert_ffn(cfg, dev["x"], torch.from_numpy(off.astype(np.int32)).cuda(),
+                        torch.from_numpy(rt.astype(np.int32)).cuda(), dev, ws)
+    torch.cuda.synchronize()
+    ref = mo.expert_ffn(x64, off, rt, ex)
+    err = mo.rel_l2(yp.cpu().numpy(), ref)
+    print(f"nvfp4 expert_ffn rel_l2 {err:.3e}")
+    assert err <= 1e-4          # fp32 rows, no output rounding
