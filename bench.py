@@ -35,7 +35,7 @@ NV_KEYS = ("b_gate", "b_up", "b_down", "g_gate", "g_up", "g_down")
 # weight copies rotated per step so that the weight stream comes from HBM, not from
 # the 256 MB last-level cache (one NVFP4 copy of the decode layer is ~170 MB)
 DEFAULT_SETS = {"tiny": 1, "decode": 8, "prefill": 2, "fp8": 4, "inkling": 1, "decode_nvfp4": 16,
-                "decode_stack": 1}
+                "prefill_nvfp4": 4, "decode_stack": 1}
 
 
 def log(*a):
@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode",
                     choices=["tiny", "decode", "prefill", "fp8", "inkling", "decode_nvfp4",
-                             "decode_stack"])
+                             "prefill_nvfp4", "decode_stack"])
     ap.add_argument("--sets", type=int, default=0, help="weight copies rotated per step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="host time budget for the oracle baseline (0 = skip)")
@@ -104,7 +104,7 @@ def kernel_roofline(shape, which, ms, U):
     mats = 2 if which == "gateup" else 1          # gate+up, or down
     name = ("gate/up expert kernel (SwiGLU fused)" if which == "gateup"
             else "down expert kernel (routing weight applied)")
-    if shape.name == "prefill":
+    if shape.name in ("prefill", "prefill_nvfp4"):
         flops = 2.0 * R * H * I * mats
         achieved = flops / (ms * 1e-3) / 1e12
         return {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,

@@ -43,13 +43,6 @@ __device__ __forceinline__ const TB* nv_expert(const TB* routed, const TB* share
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
-// Two e4m3 codes (low byte first) -> two floats.
-__device__ __forceinline__ void e4m3_pair(uint32_t two, float& s0, float& s1) {
-  const auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(two, 1.0f, false);
-  s0 = f[0];
-  s1 = f[1];
-}
-
 // Dot of 16 consecutive E2M1 weights (two dwords of codes, element 2i in the low
 // nibble of byte i) with 16 bf16 activations (eight dwords of bf16 pairs).  Each
 // code byte becomes a bf16 pair exactly (every E2M1 value is a bf16 value), and

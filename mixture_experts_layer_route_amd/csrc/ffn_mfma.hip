@@ -437,6 +437,260 @@ void k_gemm_bf16_v2(GemmBf16Args p) {
   }
 }
 
+// ===========================================================================
+// NVFP4 weights on the bf16 matrix cores (tile, waves and activation ring of the
+// pipelined bf16 kernel).  The weight slab of a 64-deep K step arrives as E2M1 codes
+// (32 bytes per weight row) and e4m3 block scales (4 per row) in registers: thread t
+// owns half row t / 2 of the slab (32 codes, two scale blocks).  One step ahead, and
+// interleaved with the current step's MFMAs, it writes them as bf16 into the tile's
+// swizzled LDS layout: an E2M1 value times an e4m3 scale has at most 6 significant
+// bits, so the bf16 is exact and is the high half of the fp32 product.  A three-slot
+// ring of converted slabs keeps one barrier per step.  The per-expert matrix scales
+// multiply the accumulators in the epilogue.
+struct GemmNv4Args {
+  const bf16_t* a;            // gate/up: x [T, H] (gathered); down: h [R, I]
+  const int32_t* row_token;
+  const int32_t* offsets;
+  const int2* tiles;
+  const int32_t* meta;
+  const uint8_t *w0, *w1, *sh0, *sh1;   // packed codes (gate/up: gate, up; down: down)
+  const uint8_t *b0, *b1, *shb0, *shb1; // e4m3 block scales
+  const float *g0, *g1, *shg0, *shg1;   // fp32 matrix scales
+  const float* row_w;
+  bf16_t* out16;
+  float* out32;
+  int K, N, E;
+};
+
+__device__ __forceinline__ uint32_t bf16_pair_hi(float lo, float hi) {
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+}
+
+template <bool GATEUP>
+__global__ __launch_bounds__(BfCfg::NT) __attribute__((amdgpu_waves_per_eu(BfCfg::WPE)))
+void k_gemm_nv4(GemmNv4Args p) {
+  using C = BfCfg;
+  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, WM = C::WM, WN = C::WN, W = C::W;
+  constexpr int MI = C::MI, NI = C::NI, CH = C::CH, RPD = C::RPD, AJ = C::AJ, NT = C::NT;
+  static_assert(BK == 64 && BN * 2 == NT, "one thread per half row of a 64-deep weight slab");
+  constexpr int A_U4 = BM * CH, B_U4 = BN * CH;
+  constexpr int RING_U4 = 3 * A_U4 + 3 * B_U4;
+  constexpr int STG_U4 = BM * C::LSD * 2 / 16;
+  __shared__ uint4 smem[RING_U4 > STG_U4 ? RING_U4 : STG_U4];
+  const int ncol = GATEUP ? p.N / (BN / 2) : p.N / BN;
+  int tile, ct;
+  if (!xcd_item(p.meta[1], ncol, tile, ct)) return;
+  const int2 te = p.tiles[tile];
+  const int e = te.x, m0 = te.y;
+  const int base = p.offsets[e];
+  const int cnt = p.offsets[e + 1] - base;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wm = wv / WN, wn = wv % WN;
+  const int64_t K = p.K;
+
+  const bf16_t* ag[AJ];
+#pragma unroll
+  for (int i = 0; i < AJ; ++i) {
+    const int r = RPD * (wv + W * i) + lane / CH;
+    const int m = min(m0 + r, cnt - 1);
+    ag[i] = (GATEUP ? p.a + int64_t(p.row_token[base + m]) * K : p.a + int64_t(base + m) * K) +
+            C::dma_chunk(lane, wv + W * i) * 8;
+  }
+  // this thread's weight half row: slab row wr, K half hh
+  const int wr = tid >> 1, hh = tid & 1;
+  const uint8_t* wc;
+  const uint8_t* wsc;
+  float gsc0, gsc1 = 0.f;
+  {
+    const int64_t cst = int64_t(p.N) * (K / 2), sst = int64_t(p.N) * (K / 16);
+    int64_t row;
+    bool second = false;
+    if (GATEUP) {
+      second = wr >= BN / 2;
+      row = int64_t(ct) * (BN / 2) + (second ? wr - BN / 2 : wr);
+    } else {
+      row = int64_t(ct) * BN + wr;
+    }
+    wc = expert_mat(second ? p.w1 : p.w0, second ? p.sh1 : p.sh0, e, p.E, cst) + row * (K / 2) + hh * 16;
+    wsc = expert_mat(second ? p.b1 : p.b0, second ? p.shb1 : p.shb0, e, p.E, sst) + row * (K / 16) + hh * 2;
+    gsc0 = e < p.E ? p.g0[e] : p.shg0[e - p.E];
+    if (GATEUP) gsc1 = e < p.E ? p.g1[e] : p.shg1[e - p.E];
+  }
+  auto issue_a = [&](int kt, int slot) {
+    const int64_t ko = int64_t(kt) * BK;
+    uint4* sa = smem + slot * A_U4;
+#pragma unroll
+    for (int i = 0; i < AJ; ++i) dma16(ag[i] + ko, sa + (wv + W * i) * 64);
+  };
+  auto fetch_b = [&](int kt, uint4& c, uint32_t& sc) {
+    c = *reinterpret_cast<const uint4*>(wc + int64_t(kt) * 32);
+    sc = *reinterpret_cast<const uint16_t*>(wsc + int64_t(kt) * 4);
+  };
+  // chunk j (8 values) of this thread's 32 codes -> bf16 in slot `slot`
+  auto convert_chunk = [&](const uint4& c, float s0, float s1, int slot, int j) {
+    const uint32_t w = j == 0 ? c.x : j == 1 ? c.y : j == 2 ? c.z : c.w;
+    const float sc = j < 2 ? s0 : s1;
+    const auto f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    const auto f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    const auto f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    const auto f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    smem[3 * A_U4 + slot * B_U4 + C::pos(wr, hh * 4 + j)] =
+        make_uint4(bf16_pair_hi(f0[0] * sc, f0[1] * sc), bf16_pair_hi(f1[0] * sc, f1[1] * sc),
+                   bf16_pair_hi(f2[0] * sc, f2[1] * sc), bf16_pair_hi(f3[0] * sc, f3[1] * sc));
+  };
+
+  f32x16 acc[MI][NI];
+#pragma unroll
+  for (int a = 0; a < MI; ++a)
+#pragma unroll
+    for (int b = 0; b < NI; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+  float roww[GATEUP ? 1 : MI][GATEUP ? 1 : 16];
+  if (!GATEUP) {
+#pragma unroll
+    for (int a = 0; a < (GATEUP ? 1 : MI); ++a)
+#pragma unroll
+      for (int r = 0; r < (GATEUP ? 1 : 16); ++r) {
+        const int row = wm * (BM / WM) + a * 32 + acc_row(r, lane);
+        roww[a][r] = (p.out32 || m0 + row >= cnt) ? 0.f : p.row_w[base + m0 + row];
+      }
+  }
+  auto load_frags = [&](const uint4* sa, const uint4* sb, int ks, bf16x8 (&af)[MI], bf16x8 (&bfr)[NI]) {
+    const int chunk = ks * 2 + (lane >> 5);
+#pragma unroll
+    for (int a = 0; a < MI; ++a)
+      af[a] = __builtin_bit_cast(bf16x8, sa[C::pos(wm * (BM / WM) + a * 32 + (lane & 31), chunk)]);
+#pragma unroll
+    for (int b = 0; b < NI; ++b) {
+      const int row = GATEUP ? ((b < NI / 2 ? 0 : BN / 2) + wn * (BN / 2 / WN) + (b % (NI / 2)) * 32 + (lane & 31))
+                             : (wn * (BN / WN) + b * 32 + (lane & 31));
+      bfr[b] = __builtin_bit_cast(bf16x8, sb[C::pos(row, chunk)]);
+    }
+  };
+  // MFMAs on slab `slot`; the next slab's conversion (chunk ks after sub-step ks) and
+  // the refill loads run between them
+  auto compute = [&](int slot, bool conv, const uint4& c, uint32_t sc2, int cslot, auto&& between) {
+    const uint4* sa = smem + slot * A_U4;
+    const uint4* sb = smem + 3 * A_U4 + slot * B_U4;
+    float s0 = 0.f, s1 = 0.f;
+    if (conv) e4m3_pair(sc2, s0, s1);
+    bf16x8 af[2][MI], bfr[2][NI];
+    load_frags(sa, sb, 0, af[0], bfr[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    between();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks + 1 < 4) load_frags(sa, sb, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int a = 0; a < MI; ++a)
+#pragma unroll
+        for (int b = 0; b < NI; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][a], bfr[ks & 1][b], acc[a][b], 0, 0, 0);
+      if (conv) convert_chunk(c, s0, s1, cslot, ks);
+    }
+  };
+
+  const int nk = int(K / BK);
+  // prologue: A0, B0, B1, A1 (weight registers before the activation DMAs, so that
+  // waiting for slab kt's activations and slab kt+1's weights leaves only A(kt+1) out)
+  uint4 cA, cB;
+  uint32_t sA = 0u, sB = 0u;
+  issue_a(0, 0);
+  fetch_b(0, cA, sA);
+  if (nk > 1) {
+    fetch_b(1, cB, sB);
+    issue_a(1, 1);
+    wait_vm_lgkm0<AJ + 2>();
+  } else {
+    wait_vm_lgkm0<0>();
+  }
+  {
+    float s0, s1;
+    e4m3_pair(sA, s0, s1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) convert_chunk(cA, s0, s1, 0, j);
+  }
+  // step kt: wait for A(kt) and B(kt+1); barrier; fetch B(kt+2) into the register
+  // slot B(kt) used, DMA A(kt+2); multiply slab kt while converting B(kt+1)
+#define MOE_NV_STEP(KT, SLOT, NSLOT, CNEXT, SNEXT, CFREE, SFREE)                             \
+  {                                                                                          \
+    if ((KT) + 1 < nk) wait_vm_lgkm0<AJ>(); else wait_vm_lgkm0<0>();                         \
+    block_sync_nowait();                                                                     \
+    compute(SLOT, (KT) + 1 < nk, CNEXT, SNEXT, NSLOT, [&] {                                  \
+      if ((KT) + 2 < nk) {                                                                   \
+        fetch_b((KT) + 2, CFREE, SFREE);                                                     \
+        issue_a((KT) + 2, ((KT) + 2) % 3);                                                   \
+      }                                                                                      \
+    });                                                                                      \
+  }
+  // weight register slots alternate: slab kt+1 sits in cB (kt even) or cA (kt odd)
+  for (int kt = 0; kt < nk; kt += 6) {
+    MOE_NV_STEP(kt, 0, 1, cB, sB, cA, sA)
+    if (kt + 1 < nk) MOE_NV_STEP(kt + 1, 1, 2, cA, sA, cB, sB)
+    if (kt + 2 < nk) MOE_NV_STEP(kt + 2, 2, 0, cB, sB, cA, sA)
+    if (kt + 3 < nk) MOE_NV_STEP(kt + 3, 0, 1, cA, sA, cB, sB)
+    if (kt + 4 < nk) MOE_NV_STEP(kt + 4, 1, 2, cB, sB, cA, sA)
+    if (kt + 5 < nk) MOE_NV_STEP(kt + 5, 2, 0, cA, sA, cB, sB)
+  }
+#undef MOE_NV_STEP
+
+  if (GATEUP || !p.out32) {
+    constexpr int OC = GATEUP ? BN / 2 : BN;
+    constexpr int LS = GATEUP ? C::LSG : C::LSD;
+    bf16_t* stg = reinterpret_cast<bf16_t*>(smem);
+    __syncthreads();
+#pragma unroll
+    for (int a = 0; a < MI; ++a) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * (BM / WM) + a * 32 + acc_row(r, lane);
+        if (GATEUP) {
+#pragma unroll
+          for (int b = 0; b < NI / 2; ++b) {
+            const float g = acc[a][b][r] * gsc0, u = acc[a][b + NI / 2][r] * gsc1;
+            stg[row * LS + wn * (BN / 2 / WN) + b * 32 + (lane & 31)] = f32_to_bf16(silu(g) * u);
+          }
+        } else {
+          const float wr2 = roww[GATEUP ? 0 : a][GATEUP ? 0 : r] * gsc0;
+#pragma unroll
+          for (int b = 0; b < NI; ++b)
+            stg[row * LS + wn * (BN / WN) + b * 32 + (lane & 31)] = f32_to_bf16(acc[a][b][r] * wr2);
+        }
+      }
+    }
+    __syncthreads();
+    constexpr int CPR = OC / 8;
+    const int rows = min(BM, cnt - m0);
+    const int col0 = ct * OC;
+    for (int i = tid; i < rows * CPR; i += NT) {
+      const int row = i / CPR, c = i - row * CPR;
+      const uint4 v = *reinterpret_cast<const uint4*>(stg + row * LS + c * 8);
+      *reinterpret_cast<uint4*>(p.out16 + int64_t(base + m0 + row) * p.N + col0 + c * 8) = v;
+    }
+    return;
+  }
+#pragma unroll
+  for (int a = 0; a < MI; ++a) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = wm * (BM / WM) + a * 32 + acc_row(r, lane);
+      if (m0 + row >= cnt) continue;
+      const int64_t grow = int64_t(base + m0 + row);
+#pragma unroll
+      for (int b = 0; b < NI; ++b)
+        p.out32[grow * p.N + ct * BN + wn * (BN / WN) + b * 32 + (lane & 31)] = acc[a][b][r] * gsc0;
+    }
+  }
+}
+
+// shapes the NVFP4 matrix-core kernels cover
+bool nv4_mfma_ok(const Plan& p) {
+  return p.wt == MOE_NVFP4 && p.I % (BfCfg::BN / 2) == 0 && p.H % BfCfg::BN == 0 &&
+         p.H % BfCfg::BK == 0 && p.I % BfCfg::BK == 0;
+}
+
 // shapes the pipelined bf16 kernel covers (else the register-staged one runs)
 static bool bf_pipelined_ok(const Plan& p) {
   return p.wt == MOE_BF16 && p.I % (BfCfg::BN / 2) == 0 && p.H % BfCfg::BN == 0 &&
@@ -983,6 +1237,17 @@ int launch_gateup_mfma(const Plan& p, const void* x, const int32_t* row_token,
                     dim3(xcd_grid(p.max_tiles * (p.I / (BfCfg::BN / 2)))), dim3(BfCfg::NT), 0, st, a);
     else
       launch_kernel(p, kTimeGateUp, k_gemm_bf16<true>, dim3(grid), dim3(256), 0, st, a);
+  } else if (p.wt == MOE_NVFP4) {
+    GemmNv4Args a{};
+    a.a = (const bf16_t*)x; a.row_token = row_token; a.offsets = offsets; a.tiles = tiles;
+    a.meta = meta;
+    a.w0 = (const uint8_t*)w->w_gate; a.w1 = (const uint8_t*)w->w_up;
+    a.sh0 = (const uint8_t*)w->sh_gate; a.sh1 = (const uint8_t*)w->sh_up;
+    a.b0 = w->b_gate; a.b1 = w->b_up; a.shb0 = w->sh_b_gate; a.shb1 = w->sh_b_up;
+    a.g0 = w->g_gate; a.g1 = w->g_up; a.shg0 = w->sh_g_gate; a.shg1 = w->sh_g_up;
+    a.out16 = (bf16_t*)h; a.K = p.H; a.N = p.I; a.E = p.E;
+    launch_kernel(p, kTimeGateUp, k_gemm_nv4<true>,
+                  dim3(xcd_grid(p.max_tiles * (p.I / (BfCfg::BN / 2)))), dim3(BfCfg::NT), 0, st, a);
   } else {
     GemmFp8Args a{};
     a.a = xq; a.a_scale = sx; a.row_token = row_token; a.offsets = offsets; a.tiles = tiles;
@@ -1016,6 +1281,14 @@ int launch_down_mfma(const Plan& p, const void* h, const int32_t* offsets, const
                     dim3(xcd_grid(p.max_tiles * (p.H / BfCfg::BN))), dim3(BfCfg::NT), 0, st, a);
     else
       launch_kernel(p, kTimeDown, k_gemm_bf16<false>, dim3(grid), dim3(256), 0, st, a);
+  } else if (p.wt == MOE_NVFP4) {
+    GemmNv4Args a{};
+    a.a = (const bf16_t*)h; a.offsets = offsets; a.tiles = tiles; a.meta = meta;
+    a.w0 = (const uint8_t*)w->w_down; a.sh0 = (const uint8_t*)w->sh_down;
+    a.b0 = w->b_down; a.shb0 = w->sh_b_down; a.g0 = w->g_down; a.shg0 = w->sh_g_down;
+    a.row_w = row_w; a.out16 = out16; a.out32 = out32; a.K = p.I; a.N = p.H; a.E = p.E;
+    launch_kernel(p, kTimeDown, k_gemm_nv4<false>,
+                  dim3(xcd_grid(p.max_tiles * (p.H / BfCfg::BN))), dim3(BfCfg::NT), 0, st, a);
   } else {
     GemmFp8Args a{};
     a.a = (const uint8_t*)h; a.a_scale = sh_scale; a.offsets = offsets; a.tiles = tiles;

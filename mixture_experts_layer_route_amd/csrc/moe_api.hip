@@ -55,7 +55,8 @@ int make_plan(const moe_config* c, Plan* p) {
   q.nblk = int((T + 63) / 64);
   const bool mfma_shape = H % 128 == 0 && I % 64 == 0;
   // Few rows per expert on average: the weight stream dominates, skinny kernels.
-  q.skinny = dense32 || nv4 || (dense16 && (q.Rk <= 8 * int64_t(E) || !mfma_shape));
+  q.skinny = dense32 || (dense16 && (q.Rk <= 8 * int64_t(E) || !mfma_shape));
+  if (nv4) q.skinny = q.Rk <= 8 * int64_t(E) || !nv4_mfma_ok(q);
   q.small_route = T <= 64 && T * k <= 256;
   q.fused_down = q.skinny && T <= 16;
   // NVFP4 batches the decode kernels do not take run the expert-major kernels + combine
@@ -131,7 +132,7 @@ static int run_experts(const Plan& p, const void* x, const int32_t* off, const i
     MOE_TRY(launch_gateup_skinny(p, x, rowtok, off, active, meta, w, h, st));
     return launch_down_skinny(p, h, off, active, meta, w, y_perm32, st);
   }
-  if (p.wt == MOE_BF16) {
+  if (p.wt == MOE_BF16 || p.wt == MOE_NVFP4) {
     bf16_t* h = at<bf16_t>(ws, p.o_h);
     MOE_TRY(launch_gateup_mfma(p, x, rowtok, off, tiles, meta, w, h, nullptr, nullptr, nullptr,
                                nullptr, st));
@@ -268,7 +269,7 @@ static int forward_impl(const moe_config* cfg, const void* x, const moe_weights*
     return launch_combine(p, yp, off, inv, wts, res, y, stream);
   }
   bf16_t* ypw = at<bf16_t>(ws, p.o_ypw);
-  if (p.wt == MOE_BF16) {
+  if (p.wt == MOE_BF16 || p.wt == MOE_NVFP4) {
     bf16_t* h = at<bf16_t>(ws, p.o_h);
     MOE_TRY(launch_gateup_mfma(p, x, rowtok, off, tiles, meta, w, h, nullptr, nullptr, nullptr,
                                nullptr, stream));

@@ -250,6 +250,14 @@ __device__ __forceinline__ uint64_t rank_key(float s, int idx) {
 __device__ __forceinline__ int key_index(uint64_t k) { return int(0xFFFFFFFFu - uint32_t(k)); }
 
 
+// Two OCP e4m3 codes (low byte first) -> two floats (the gfx950 packed conversion
+// with a unit scale decodes all 256 codes exactly, subnormals included).
+__device__ __forceinline__ void e4m3_pair(uint32_t two, float& s0, float& s1) {
+  const auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(two, 1.0f, false);
+  s0 = f[0];
+  s1 = f[1];
+}
+
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
 }  // namespace moe

@@ -84,6 +84,8 @@ bool decode_ffn_ok(const Plan& p);
 bool select_rows_ok(const Plan& p);
 // M rows per tile the matrix-core expert kernels use for this plan
 int gemm_tile_rows(const Plan& p);
+// the NVFP4 matrix-core kernels cover this shape
+bool nv4_mfma_ok(const Plan& p);
 // Decode path: gate/up (with in-kernel routing) then down + combine.
 int launch_decode_ffn(const Plan& p, const void* x, const float* logits, const moe_weights* w,
                       int32_t* ids, float* wts, int32_t* offsets, int32_t* row_token,

@@ -16,6 +16,7 @@ Shapes and value distributions follow the five workloads of the layer:
   inkling   T=4096, H=2048, I=512, E=256 ungrouped, k=6, 2 shared experts
   decode_nvfp4  the decode layer with NVFP4 experts (4-bit E2M1 codes, an E4M3
             scale per 16 inputs, an fp32 scale per expert matrix)
+  prefill_nvfp4 the prefill layer (router bias included) with NVFP4 experts
   decode_stack  23 decode MoE blocks of a decoder step (x + MoE(RMSNorm(x)) each): the
             decode layer's experts copied per block, a router and a norm weight
             drawn per block (make_router, make_norm_weight)
@@ -82,6 +83,8 @@ WORKLOADS = {
                           act=BF16, wt=BF16, x_dist="normal", bias_std=0.0, seed=4),
     "decode_nvfp4": LayerShape("decode_nvfp4", T=4, H=1536, I=512, E=128, G=8, Gk=4, k=8,
                                S=0, act=BF16, wt=NVFP4, x_dist="rms", bias_std=0.0, seed=5),
+    "prefill_nvfp4": LayerShape("prefill_nvfp4", T=8192, H=1536, I=512, E=128, G=8, Gk=4, k=8,
+                                S=0, act=BF16, wt=NVFP4, x_dist="rms", bias_std=0.5, seed=7),
     "decode_stack": LayerShape("decode_stack", T=4, H=1536, I=512, E=128, G=8, Gk=4, k=8,
                                S=0, act=BF16, wt=BF16, x_dist="normal", bias_std=0.0, seed=6),
 }
