@@ -134,3 +134,15 @@ def test_weights_struct_matches_header():
     cbody = txt[txt.index("typedef struct {"):txt.index("} moe_config;")]
     cnames = re.findall(r"^\s*int\d+_t\s+(\w+);", cbody, re.M)
     assert cnames == [n for n, _ in moe.MoeConfig._fields_]
+
+
+def test_forward_timed_rejects_missing_events(lib):
+    cfg = _cfg()
+    fake = ctypes.c_void_p(1 << 40)
+    w = moe.MoeWeights()
+    w.w_router = w.w_gate = w.w_up = w.w_down = 1 << 40
+    assert lib.moe_forward_timed(ctypes.byref(cfg), fake, ctypes.byref(w), fake, None, None, fake,
+                                 1 << 40, None, None) == -1
+    ev = (ctypes.c_void_p * moe.TIMED_EVENTS)(*([1 << 40] * (moe.TIMED_EVENTS - 1) + [None]))
+    assert lib.moe_forward_timed(ctypes.byref(cfg), fake, ctypes.byref(w), fake, None, None, fake,
+                                 1 << 40, None, ev) == -1
