@@ -129,6 +129,33 @@ def kernel_roofline(shape, which, ms, U):
             "per_launch": f"{abytes} B = {U} touched experts x {per_expert} B of weights"}
 
 
+def step_roofline(shape, ms, U):
+    """The whole step against the same peak (the way the scope table prices a config):
+    prefill-sized bf16 work by all expert and router flops, everything else by the
+    bytes the method must move (each touched expert's weights once, the router, x, y)."""
+    T, H, I, E, k, S = shape.T, shape.H, shape.I, shape.E, shape.k, shape.S
+    act = 4 if shape.act == "f32" else 2
+    if shape.name in ("prefill", "prefill_nvfp4"):
+        flops = 2.0 * T * (k + S) * H * I * 3 + 2.0 * T * E * H
+        achieved = flops / (ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                "per_step": f"{flops / 1e9:.2f} GFLOP (experts 2*R*H*I*3 + router 2*T*E*H)"}
+    wbytes = {"e4m3": 1, "f32": 4, "bf16": 2, "nvfp4": 0.5}[shape.wt]
+    if shape.wt == "e4m3":
+        scales = 3 * (I // 128) * (H // 128) * 4
+    elif shape.wt == "nvfp4":
+        scales = 3 * (I * H // 16 + 4)
+    else:
+        scales = 0
+    per_expert = int(3 * I * H * wbytes) + scales
+    nbytes = U * per_expert + E * H * act + 2 * T * H * act
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "per_step": f"{nbytes} B = {U} touched experts x {per_expert} B + router, x and y"}
+
+
 def oracle_experts(mo, cpu, f):
     """The oracle's expert set over the synthetic layer's stored weights."""
     nv = sh_nv = None
@@ -406,6 +433,7 @@ def main():
         "ms_per_step_without_kernel_events": round(ms_plain, 5),
         "parity_rel_l2": float(f"{err:.3e}"),
         "roofline": roof,
+        "step_roofline": step_roofline(shape, ms_per_step, U),
     }
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(shape, cpu, args.cpu_seconds)
