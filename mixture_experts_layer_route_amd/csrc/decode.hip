@@ -21,6 +21,13 @@
 #include <type_traits>
 
 #include "moe_internal.h"
+
+#ifndef MOE_DEC_PF
+#define MOE_DEC_PF 8   // prefetch loads (1 KB each) per prefetching wave, 0 = none
+#endif
+#ifndef MOE_DEC_PF_TOPM
+#define MOE_DEC_PF_TOPM 2   // experts per token the prefetch covers (certain while <= Gk)
+#endif
 #include "route_select.h"
 
 namespace moe {
@@ -274,7 +281,68 @@ __global__ __launch_bounds__(256) void k_decode_gateup(DecodeArgs a) {
     for (int t = wv; t < T; t += 4)
       select_token_wave<SEL>(a.logits + int64_t(t) * E, E, a.G, a.Gk, k, ids_l + t * k, w_l + t * k);
   }
-  wait_vm_lgkm0<0>();
+  // Weight prefetch while the routing is still being decided.  A token's j highest raw
+  // logits for j <= Gk are always selected (the j-th lies in a group of rank <= j, so
+  // its group is kept, and it outranks everything else in the kept groups), so waves
+  // with no selection work read the logits of tokens 0..3, find their top experts and
+  // pull slices of those experts' gate/up rows through the caches with direct-to-LDS
+  // loads into a scratch area that is never read (MOE_DEC_PF loads of 1 KB per wave;
+  // they retire after everything the prologue waits for, so the wait below leaves
+  // exactly them in flight).
+  bool prefetcher = false;
+#if MOE_DEC_PF > 0
+  if constexpr (SEL < 0) {
+    constexpr int V = -SEL;
+    const int ngrp = (T + 3) / 4;
+    if (wv >= ngrp) {                                  // uniform over the wave
+      prefetcher = true;
+      const int r16 = lane & 15, q = lane >> 4, Tq = min(T, 4);
+      const float* l = a.logits + int64_t(min(q, Tq - 1)) * E + V * r16;
+      // top-MOE_DEC_PF_TOPM experts of each row's token (all certain while <= Gk)
+      uint64_t key[V];
+#pragma unroll
+      for (int i = 0; i < V; ++i) key[i] = rank_key(l[i], V * r16 + i);
+      int ex[4 * MOE_DEC_PF_TOPM];
+#pragma unroll
+      for (int m = 0; m < MOE_DEC_PF_TOPM; ++m) {
+        uint64_t best = 0ull;
+#pragma unroll
+        for (int i = 0; i < V; ++i) best = key[i] > best ? key[i] : best;
+        const uint64_t win = row_max_u64(best);
+#pragma unroll
+        for (int i = 0; i < V; ++i) key[i] = key[i] == win ? 0ull : key[i];
+        const int id = key_index(win);
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) ex[qq * MOE_DEC_PF_TOPM + m] = __builtin_amdgcn_readlane(id, 16 * qq);
+      }
+      const int topm = min(MOE_DEC_PF_TOPM, min(a.Gk, k));
+      constexpr bool NV = std::is_same<TW, nvfp4_t>::value;
+      const int64_t mb = NV ? int64_t(I) * H / 2 : int64_t(I) * H * int64_t(sizeof(TW));
+      const int64_t span = int64_t(Tq) * topm * 2 * mb;   // bytes of the prefetch set
+      const int npw = 4 - ngrp;                         // prefetching waves per block
+      const int pw = wv - ngrp;
+      const unsigned char* gb = static_cast<const unsigned char*>(a.wg);
+      const unsigned char* ub = static_cast<const unsigned char*>(a.wu);
+      unsigned char* scratch = reinterpret_cast<unsigned char*>(
+          (reinterpret_cast<uintptr_t>(bits_l + 4 * E) + 15) & ~uintptr_t(15)) + pw * 1024;
+#pragma unroll
+      for (int j = 0; j < MOE_DEC_PF; ++j) {
+        int64_t o = ((int64_t(blockIdx.x) * npw + pw) * MOE_DEC_PF + j) * 1024 + lane * 16;
+        o %= span;
+        const int slot = int(o / (2 * mb));              // token tq's m-th expert: tq*topm + m
+        const int64_t rem = o - int64_t(slot) * 2 * mb;
+        const int tq = slot / topm, m = slot - tq * topm;
+        int e = ex[0];
+#pragma unroll
+        for (int c = 1; c < 4 * MOE_DEC_PF_TOPM; ++c)
+          if (c == tq * MOE_DEC_PF_TOPM + m) e = ex[c];
+        const unsigned char* src = (rem < mb ? gb + rem : ub + (rem - mb)) + int64_t(e) * mb;
+        dma16(src, scratch);
+      }
+    }
+  }
+#endif
+  if (prefetcher) wait_vm_lgkm0<MOE_DEC_PF>(); else wait_vm_lgkm0<0>();
   __syncthreads();
   if (threadIdx.x < nslot) atomicOr(&bits_l[wv * E + ids_l[threadIdx.x]], 1ull << lane);
   __syncthreads();
@@ -397,6 +465,7 @@ __global__ __launch_bounds__(256) void k_decode_gateup(DecodeArgs a) {
     }
   }
   }
+  wait_vm_lgkm0<0>();   // no direct-to-LDS load may land after the workgroup's LDS is released
 }
 
 template <typename TA, typename TW, int NSD>
@@ -865,7 +934,8 @@ __global__ __launch_bounds__(256) void k_nv_down_batch(DecodeArgs a,
 static size_t decode_lds(const Plan& p) {
   const size_t tsize = p.act == MOE_F32 ? 4 : 2;
   return ((size_t(p.T) * p.H * tsize + 15) & ~size_t(15)) +
-         size_t(2 * (p.E + p.S) + 1 + p.R + 3 * p.T * p.k + 1) * 4 + size_t(4) * p.E * 8 + 8;
+         size_t(2 * (p.E + p.S) + 1 + p.R + 3 * p.T * p.k + 1) * 4 + size_t(4) * p.E * 8 + 8 +
+         (MOE_DEC_PF > 0 ? 4096 + 16 : 0);   // prefetch scratch, 1 KB per wave, 16-byte aligned
 }
 
 bool decode_ffn_ok(const Plan& p) {
