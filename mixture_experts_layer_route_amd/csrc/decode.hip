@@ -291,7 +291,8 @@ __global__ __launch_bounds__(256) void k_decode_gateup(DecodeArgs a) {
   // exactly them in flight).
   bool prefetcher = false;
 #if MOE_DEC_PF > 0
-  if constexpr (SEL < 0) {
+  // (not for 4-bit weights: their stream is short and arithmetic-bound, measured neutral)
+  if constexpr (SEL < 0 && !std::is_same<TW, nvfp4_t>::value) {
     constexpr int V = -SEL;
     const int ngrp = (T + 3) / 4;
     if (wv >= ngrp) {                                  // uniform over the wave
