@@ -6,10 +6,11 @@
 // not cover": each expert runs on just the rows that picked it), so both kernels
 // are organised around that stream:
 //   gate/up: every block first routes the T tokens itself from the logits into
-//     LDS (one wave per token selects; thread e places the rows of expert e in
-//     ascending (token, slot) order; block 0 publishes the routing), then each
-//     wave walks work items (active expert, NI weight rows) round-robin over the
-//     grid with the next item's loads in flight while the current one is
+//     LDS (sixteen lanes or a wave per token select; the rows of each expert are
+//     placed in ascending (token, slot) order; block 0 publishes the routing),
+//     while idle waves prefetch the experts the routing is certain to choose; then
+//     each wave walks work items (active expert, NI weight rows) round-robin over
+//     the grid with the next item's loads in flight while the current one is
 //     multiplied; h (fp32) goes to the workspace;
 //   down + combine: item = (token t, NR output columns),
 //     y[t,n] = sum_j w[t,j] (h[row(t,j)] . Wd[id(t,j)][n]) + sum_s (h[shared row] . Wd_s[n]),
@@ -18,6 +19,9 @@
 // A single kernel with a device-wide barrier between the two halves measured
 // slower on MI355X than the launch it saves (the cross-XCD arrival counting and
 // cache write-back cost tens of microseconds), so the halves are two launches.
+// NVFP4 experts have their own item loops here (decode, and the expert-major ones
+// for batches the decode kernels do not take); the decoder step adds the residual
+// in the down kernels.
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -228,8 +232,9 @@ __global__ __launch_bounds__(256) void k_decode_gateup(DecodeArgs a) {
   float* w_l = reinterpret_cast<float*>(inv_l + nslot);
   __shared__ int tmp[8];
   __shared__ int n_act_l;
-  unsigned long long* bits_l = reinterpret_cast<unsigned long long*>(
-      (reinterpret_cast<uintptr_t>(w_l + nslot) + 7) & ~uintptr_t(7));                       // [4][E]
+  // byte offsets from lds_raw keep the LDS address space visible to the compiler
+  const size_t bits_off = (size_t(reinterpret_cast<unsigned char*>(w_l + nslot) - lds_raw) + 7) & ~size_t(7);
+  unsigned long long* bits_l = reinterpret_cast<unsigned long long*>(lds_raw + bits_off);   // [4][E]
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const TA* x = static_cast<const TA*>(a.x);
   const TW* wg = static_cast<const TW*>(a.wg);
@@ -324,8 +329,7 @@ __global__ __launch_bounds__(256) void k_decode_gateup(DecodeArgs a) {
       const int pw = wv - ngrp;
       const unsigned char* gb = static_cast<const unsigned char*>(a.wg);
       const unsigned char* ub = static_cast<const unsigned char*>(a.wu);
-      unsigned char* scratch = reinterpret_cast<unsigned char*>(
-          (reinterpret_cast<uintptr_t>(bits_l + 4 * E) + 15) & ~uintptr_t(15)) + pw * 1024;
+      unsigned char* scratch = lds_raw + ((bits_off + size_t(4) * E * 8 + 15) & ~size_t(15)) + pw * 1024;
 #pragma unroll
       for (int j = 0; j < MOE_DEC_PF; ++j) {
         int64_t o = ((int64_t(blockIdx.x) * npw + pw) * MOE_DEC_PF + j) * 1024 + lane * 16;

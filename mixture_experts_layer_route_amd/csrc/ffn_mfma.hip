@@ -1,4 +1,4 @@
-// Grouped SwiGLU expert GEMMs on CDNA4 matrix cores (bf16 and block-FP8).
+// Grouped SwiGLU expert GEMMs on CDNA4 matrix cores (bf16, block-FP8, NVFP4).
 //
 // The pages say the bf16 experts have no grouped kernel and that a port would
 // want a real one (TensorFold issue #1247 "Ling-3.0-tiny on a Qualcomm board",
@@ -8,13 +8,17 @@
 // offset) from the device tile table the permutation built, so the host never
 // learns the per-expert row counts.  Workgroups beyond the live tile count exit.
 //
-// Tiles: 128 x 128 outputs per workgroup of 4 waves (2 x 2, 64 x 64 per wave,
-// 2 x 2 MFMA 32x32 blocks), K staged through LDS in double-buffered slabs with
-// the 16-byte chunks of each row XOR-swizzled by (row & 7) to spread LDS banks.
-// The gate/up kernel gathers activation rows through row_token while loading
-// (the permuted activations are never materialised) and applies SwiGLU in
-// registers: each wave owns 32 gate and the matching 32 up columns, so g and u
-// of one (row, i) sit in the same lane and register.
+// The pipelined kernels (k_gemm_bf16_v2, k_gemm_nv4, k_gemm_fp8_v2) take 128-row
+// tiles of 256 weight rows per workgroup of 8 waves, K moving global -> LDS by
+// direct-to-LDS loads through a three-slot ring, the 16-byte chunks of each tile row
+// XOR-swizzled so that a ds_read_b128 of 16 lanes hits distinct banks; work items
+// are laid out XCD by XCD so the workgroups sharing weight slabs share an L2.  The
+// register-staged kernels (k_gemm_bf16, k_gemm_fp8: 128 x 128 tiles of 4 waves,
+// double-buffered) cover the shapes the pipelined tiles do not divide.  The gate/up
+// kernels gather activation rows through row_token while loading (the permuted
+// activations are never materialised) and apply SwiGLU in registers: a wave holds
+// gate columns and the matching up columns, so g and u of one (row, i) sit in the
+// same lane and register.
 #include "moe_internal.h"
 
 namespace moe {

@@ -70,7 +70,7 @@ int make_plan(const moe_config* c, Plan* p) {
   q.o_logits = take(size_t(T) * E * 4);
   q.o_ids = take(size_t(q.Rk) * 4);
   q.o_w = take(size_t(q.Rk) * 4);
-  q.o_blk = take(size_t(q.nblk) * E * 4);
+  q.o_blk = take(size_t(2) * q.nblk * E * 4);   // [2][nblk][E]: the row selection counts half blocks
   q.o_off = take(size_t(E + S + 1) * 4);
   q.o_meta = take(16);
   q.o_active = take(size_t(E + S) * 4);
@@ -257,8 +257,9 @@ static int forward_impl(const moe_config* cfg, const void* x, const moe_weights*
   } else {
     MOE_TRY(launch_logits(p, x, w->w_router, w->router_bias, logits, stream));
     MOE_TRY(launch_select(p, logits, ids, wts, blk, stream));
-    MOE_TRY(launch_scan_scatter(p, ids, wts, blk, off, active, meta, tiles, rowtok, inv, row_w,
-                                p.bm, stream));
+    const int32_t* blk2 = select_rows_ok(p) ? blk + size_t(p.nblk) * p.E : nullptr;
+    MOE_TRY(launch_scan_scatter(p, ids, wts, blk, blk2, off, active, meta, tiles, rowtok, inv,
+                                row_w, p.bm, stream));
   }
   if (p.skinny) {
     float* h = at<float>(ws, p.o_h);

@@ -68,8 +68,9 @@ int launch_logits_norm(const Plan& p, const void* x, const void* gamma, float ep
 int launch_select(const Plan& p, const float* logits, int32_t* ids, float* w, int32_t* blk,
                   hipStream_t st);
 int launch_scan_scatter(const Plan& p, const int32_t* ids, const float* w, int32_t* blk,
-                        int32_t* offsets, int32_t* active, int32_t* meta, int2* tiles,
-                        int32_t* row_token, int32_t* inv, float* row_w, int BM, hipStream_t st);
+                        const int32_t* blk2, int32_t* offsets, int32_t* active, int32_t* meta,
+                        int2* tiles, int32_t* row_token, int32_t* inv, float* row_w, int BM,
+                        hipStream_t st);
 int launch_permute(const Plan& p, const int32_t* ids, const float* w, int32_t* blk,
                    int32_t* offsets, int32_t* active, int32_t* meta, int2* tiles,
                    int32_t* row_token, int32_t* inv, float* row_w, int BM, hipStream_t st);

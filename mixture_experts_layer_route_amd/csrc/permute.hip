@@ -88,12 +88,14 @@ __global__ __launch_bounds__(256) void k_perm_count(const int32_t* __restrict__ 
 }
 
 // Totals, offsets, per-block bases (in place over the histogram) and schedule.
-// One block of 1024 threads.  The [nblk][E] histogram is staged through LDS in
+// The histogram is blk [nblk][E], plus blk2 [nblk][E] when the counts of each
+// block come in two halves (the bases are written over blk).  One block of 1024 threads.  The [nblk][E] histogram is staged through LDS in
 // chunks with coalesced loads; each expert gets P = 1024 / E' threads (E' = E
 // rounded up to a power of two, P <= 64) that own contiguous runs of blocks, so
 // the per-expert sums and running bases are short per thread and combine by
 // segmented shuffles over the P lanes of the expert.
-__global__ __launch_bounds__(1024) void k_perm_scan(int32_t* __restrict__ blk, int nblk, int64_t T,
+__global__ __launch_bounds__(1024) void k_perm_scan(int32_t* __restrict__ blk,
+                                                    const int32_t* __restrict__ blk2, int nblk, int64_t T,
                                                     int E, int S, int BM,
                                                     int32_t* __restrict__ offsets,
                                                     int32_t* __restrict__ active,
@@ -129,6 +131,16 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int32_t* __restrict__ blk, i
     for (int u = 0; u < PER; ++u) {
       const int i = tid + u * 1024;
       v[u] = i < n ? blk[int64_t(b0) * E + i] : 0;
+    }
+    if (blk2) {
+      int v2[PER];
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int i = tid + u * 1024;
+        v2[u] = i < n ? blk2[int64_t(b0) * E + i] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < PER; ++u) v[u] += v2[u];
     }
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
@@ -198,7 +210,8 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int32_t* __restrict__ blk, i
 // expert meet once in LDS, where expert thread e turns them into an exclusive
 // prefix and its total.
 template <int RPT>
-__global__ __launch_bounds__(1024) void k_perm_scan_reg(int32_t* __restrict__ blk, int nblk,
+__global__ __launch_bounds__(1024) void k_perm_scan_reg(int32_t* __restrict__ blk,
+                                                        const int32_t* __restrict__ blk2, int nblk,
                                                         int64_t T, int E, int S, int BM,
                                                         int32_t* __restrict__ offsets,
                                                         int32_t* __restrict__ active,
@@ -219,6 +232,16 @@ __global__ __launch_bounds__(1024) void k_perm_scan_reg(int32_t* __restrict__ bl
   for (int i = 0; i < RPT; ++i) {
     const int b = b0 + i;
     v[i] = (mine && i < per && b < nblk) ? blk[int64_t(b) * E + ge] : 0;
+  }
+  if (blk2) {                                      // uniform: every load issued before any add
+    int v2[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int b = b0 + i;
+      v2[i] = (mine && i < per && b < nblk) ? blk2[int64_t(b) * E + ge] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) v[i] += v2[i];
   }
   int part = 0;
 #pragma unroll
@@ -251,48 +274,49 @@ __global__ __launch_bounds__(1024) void k_perm_scan_reg(int32_t* __restrict__ bl
   }
 }
 
-// Stable scatter, one wave per permutation block of 64 tokens.  The rank of
-// (t, j) among its block's rows of expert e is the number of lower lanes whose
-// token also chose e: a 64-bit lane mask per (wave, expert) built with LDS
-// atomic ORs.  grid = ceil(T/256), block = 256, dynamic LDS = 4*E*8 bytes.
+// Stable scatter, one block of four waves per permutation block of 64 tokens:
+// lane = token of the block, wave w takes the slots j = w, w + 4, ...  The rank of
+// (t, j) among the block's rows of expert e is the number of lower tokens of the
+// block that also chose e (a token chooses an expert at most once): a 64-bit token
+// mask per expert built with LDS atomic ORs.  grid = nblk, block = 256, dynamic
+// LDS = E*8 bytes.
 __global__ __launch_bounds__(256) void k_perm_scatter(
     const int32_t* __restrict__ ids, const float* __restrict__ w, int64_t T, int k, int E, int S,
     const int32_t* __restrict__ blk_base, int32_t* __restrict__ row_token,
     int32_t* __restrict__ inv, float* __restrict__ row_w) {
-  extern __shared__ unsigned long long bits[];  // [4][E]
+  extern __shared__ unsigned long long bits[];  // [E]
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  for (int i = threadIdx.x; i < 4 * E; i += 256) bits[i] = 0ull;
+  for (int i = threadIdx.x; i < E; i += 256) bits[i] = 0ull;
   __syncthreads();
-  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t t = int64_t(blockIdx.x) * 64 + lane;
   const bool valid = t < T;
-  // the token's k <= 16 ids and weights, all loads issued before any is used
-  int id[16];
-  float wt[16];
+  // this wave's slots of the token (k <= 16: at most four), all loads issued first
+  int id[4];
+  float wt[4];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    id[j] = (valid && j < k) ? ids[t * k + j] : 0;
-    wt[j] = (valid && j < k && row_w) ? w[t * k + j] : 0.f;
+  for (int q = 0; q < 4; ++q) {
+    const int j = wv + 4 * q;
+    id[q] = (valid && j < k) ? ids[t * k + j] : 0;
+    wt[q] = (valid && j < k && row_w) ? w[t * k + j] : 0.f;
   }
 #pragma unroll
-  for (int j = 0; j < 16; ++j)
-    if (valid && j < k) atomicOr(&bits[wv * E + id[j]], 1ull << lane);
+  for (int q = 0; q < 4; ++q)
+    if (valid && wv + 4 * q < k) atomicOr(&bits[id[q]], 1ull << lane);
   __syncthreads();
   if (!valid) return;
   const unsigned long long lower = (1ull << lane) - 1ull;
-  const int32_t* base = blk_base + (int64_t(blockIdx.x) * 4 + wv) * E;
-  int bs[16];
+  const int32_t* base = blk_base + int64_t(blockIdx.x) * E;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) bs[j] = j < k ? base[id[j]] : 0;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int q = 0; q < 4; ++q) {
+    const int j = wv + 4 * q;
     if (j >= k) break;
-    const int e = id[j];
-    const int r = bs[j] + __popcll(bits[wv * E + e] & lower);
+    const int e = id[q];
+    const int r = base[e] + __popcll(bits[e] & lower);
     row_token[r] = int32_t(t);
     inv[t * k + j] = r;
-    if (row_w) row_w[r] = wt[j];
+    if (row_w) row_w[r] = wt[q];
   }
-  for (int s = 0; s < S; ++s) {
+  for (int s = wv; s < S; s += 4) {
     const int64_t r = T * k + int64_t(s) * T + t;
     row_token[r] = int32_t(t);
     if (row_w) row_w[r] = 1.0f;
@@ -364,26 +388,26 @@ __global__ __launch_bounds__(1024) void k_route_permute_small(
 
 // ---------------------------------------------------------------------------
 int launch_scan_scatter(const Plan& p, const int32_t* ids, const float* w, int32_t* blk,
-                        int32_t* offsets, int32_t* active, int32_t* meta, int2* tiles,
-                        int32_t* row_token, int32_t* inv, float* row_w, int BM, hipStream_t st) {
-  const unsigned g4 = unsigned((p.T + 255) / 256);
+                        const int32_t* blk2, int32_t* offsets, int32_t* active, int32_t* meta,
+                        int2* tiles, int32_t* row_token, int32_t* inv, float* row_w, int BM,
+                        hipStream_t st) {
   int Ep = 1;
   while (Ep < p.E) Ep <<= 1;
   const int per = (p.nblk + 1024 / Ep - 1) / (1024 / Ep);    // histogram blocks per thread
   if (per <= 8)
-    hipLaunchKernelGGL(k_perm_scan_reg<8>, dim3(1), dim3(1024), 0, st, blk, p.nblk, p.T, p.E, p.S,
+    hipLaunchKernelGGL(k_perm_scan_reg<8>, dim3(1), dim3(1024), 0, st, blk, blk2, p.nblk, p.T, p.E, p.S,
                        BM, offsets, active, meta, tiles);
   else if (per <= 16)
-    hipLaunchKernelGGL(k_perm_scan_reg<16>, dim3(1), dim3(1024), 0, st, blk, p.nblk, p.T, p.E, p.S,
+    hipLaunchKernelGGL(k_perm_scan_reg<16>, dim3(1), dim3(1024), 0, st, blk, blk2, p.nblk, p.T, p.E, p.S,
                        BM, offsets, active, meta, tiles);
   else if (per <= 32)
-    hipLaunchKernelGGL(k_perm_scan_reg<32>, dim3(1), dim3(1024), 0, st, blk, p.nblk, p.T, p.E, p.S,
+    hipLaunchKernelGGL(k_perm_scan_reg<32>, dim3(1), dim3(1024), 0, st, blk, blk2, p.nblk, p.T, p.E, p.S,
                        BM, offsets, active, meta, tiles);
   else
-    hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, st, blk, p.nblk, p.T, p.E, p.S, BM,
+    hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, st, blk, blk2, p.nblk, p.T, p.E, p.S, BM,
                        offsets, active, meta, tiles);
-  hipLaunchKernelGGL(k_perm_scatter, dim3(g4), dim3(256), size_t(4) * p.E * 8, st, ids, w, p.T,
-                     p.k, p.E, p.S, blk, row_token, inv, row_w);
+  hipLaunchKernelGGL(k_perm_scatter, dim3(unsigned(p.nblk)), dim3(256), size_t(p.E) * 8, st, ids,
+                     w, p.T, p.k, p.E, p.S, blk, row_token, inv, row_w);
   return check_launch();
 }
 
@@ -393,7 +417,7 @@ int launch_permute(const Plan& p, const int32_t* ids, const float* w, int32_t* b
   const unsigned g4 = unsigned((p.T + 255) / 256);
   hipLaunchKernelGGL(k_perm_count, dim3(g4), dim3(256), size_t(4) * p.E * sizeof(int), st, ids,
                      p.T, p.k, p.E, blk);
-  return launch_scan_scatter(p, ids, w, blk, offsets, active, meta, tiles, row_token, inv, row_w,
+  return launch_scan_scatter(p, ids, w, blk, nullptr, offsets, active, meta, tiles, row_token, inv, row_w,
                              BM, st);
 }
 

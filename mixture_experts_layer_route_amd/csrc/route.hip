@@ -307,67 +307,80 @@ int launch_logits_norm(const Plan& p, const void* x, const void* gamma, float ep
 
 // ---------------------------------------------------------------------------
 // Matrix-core router logits for bf16 batches: l = X W_r^T (+ bias), fp32 [T, E].
-// One workgroup of 4 waves (2 x 2, each 32 tokens x 32 experts, one 32x32 MFMA
-// block) per 64-token x 64-expert tile, so a batch spreads over many CUs.  H moves
-// global -> LDS in slabs of 64 through a 3-stage ring of direct-to-LDS loads; the
-// rows are swizzled as swz16 reads them.  grid = (ceil(T/64), E/64), block = 256.
-__global__ __launch_bounds__(256) void k_logits_mfma(const bf16_t* __restrict__ x,
+// One workgroup per 64-token x 64-expert tile, so a batch spreads over many CUs:
+// eight waves, four tile positions (2 x 2, each 32 tokens x 32 experts, one 32x32
+// MFMA block) times two halves of every 64-deep K slab; the halves meet through
+// LDS at the end.  H moves global -> LDS in slabs of 64 through a ring of NSTG
+// stages of direct-to-LDS loads, one 1 KB load per wave per operand and slab (the
+// K loop is bound by how fast the loads are issued and land, not by the matrix
+// cores, so every wave issues them); the rows are swizzled as swz16 reads them.
+// grid = (ceil(T/64), E/64), block = 512.
+__global__ __launch_bounds__(512) void k_logits_mfma(const bf16_t* __restrict__ x,
                                                      const bf16_t* __restrict__ wr,
                                                      const float* __restrict__ bias, int64_t T,
                                                      int H, int E, float* __restrict__ logits) {
   constexpr int BT = 64, BE = 64, XU4 = BT * 8, STU4 = XU4 + BE * 8;   // uint4 per stage
-  constexpr int L = 4;                                                  // loads per lane per slab
-  __shared__ uint4 ring[3 * STU4];
+  constexpr int L = 2;                                                  // loads per lane per slab
+#ifndef MOE_LOGITS_NSTG
+#define MOE_LOGITS_NSTG 6
+#endif
+  constexpr int NSTG = MOE_LOGITS_NSTG;
+  __shared__ uint4 ring[NSTG * STU4];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int wm = wv >> 1, wn = wv & 1;
+  const int wt = wv & 3, kh = wv >> 2;             // tile position, K half
+  const int wm = wt >> 1, wn = wt & 1;
   const int64_t t0 = int64_t(blockIdx.x) * BT;
   const int e0 = blockIdx.y * BE;
-  const bf16_t* xg[2];
-  const bf16_t* wg[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = 8 * (wv + 4 * i) + (lane >> 3);
-    const int c = dma_chunk(lane, wv + 4 * i) * 8;
-    xg[i] = x + min<int64_t>(t0 + r, T - 1) * H + c;
-    wg[i] = wr + int64_t(e0 + r) * H + c;
-  }
+  // wave wv loads rows 8 wv .. 8 wv + 7 of both operands (8 lanes of 16 bytes per row)
+  const int r = 8 * wv + (lane >> 3);
+  const int c = dma_chunk(lane, wv) * 8;
+  const bf16_t* xg = x + min<int64_t>(t0 + r, T - 1) * H + c;
+  const bf16_t* wg = wr + int64_t(e0 + r) * H + c;
   auto issue = [&](int kt, int stage) {
     uint4* st = ring + stage * STU4;
     const int ko = kt * 64;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(xg[i] + ko, st + (wv + 4 * i) * 64);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(wg[i] + ko, st + XU4 + (wv + 4 * i) * 64);
+    dma16(xg + ko, st + wv * 64);
+    dma16(wg + ko, st + XU4 + wv * 64);
   };
   f32x16 acc;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
   auto compute = [&](int stage) {
     const uint4* xc = ring + stage * STU4;
     const uint4* wc = xc + XU4;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int chunk = ks * 2 + (lane >> 5);
+    for (int kq = 0; kq < 2; ++kq) {
+      const int chunk = (kh * 2 + kq) * 2 + (lane >> 5);
       const bf16x8 af = __builtin_bit_cast(bf16x8, xc[swz16(wm * 32 + (lane & 31), chunk)]);
       const bf16x8 bfr = __builtin_bit_cast(bf16x8, wc[swz16(wn * 32 + (lane & 31), chunk)]);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr, acc, 0, 0, 0);
     }
   };
   const int nk = H / 64;
-  issue(0, 0);
-  if (nk > 1) issue(1, 1);
+  for (int s = 0; s < NSTG - 1 && s < nk; ++s) issue(s, s);
+  // step kt: wait for slab kt (NSTG - 2 later slabs may stay in flight while none has
+  // been held back at the tail), barrier, refill the stage slab kt-1 used, multiply kt
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) wait_vm_lgkm0<L>(); else wait_vm_lgkm0<0>();
+    if (kt + NSTG - 1 <= nk) wait_vm_lgkm0<(NSTG - 2) * L>(); else wait_vm_lgkm0<0>();
     block_sync_nowait();
-    if (kt + 2 < nk) issue(kt + 2, (kt + 2) % 3);
-    compute(kt % 3);
+    if (kt + NSTG - 1 < nk) issue(kt + NSTG - 1, (kt + NSTG - 1) % NSTG);
+    compute(kt % NSTG);
   }
+  // the second K half's partial sums join the first's through the (drained) ring
+  float* red = reinterpret_cast<float*>(ring);
+  __syncthreads();
+  if (kh == 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) red[(wt * 16 + i) * 64 + lane] = acc[i];
+  }
+  __syncthreads();
+  if (kh == 1) return;
   const int e = e0 + wn * 32 + (lane & 31);
   const float b = bias ? bias[e] : 0.f;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int64_t t = t0 + wm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-    if (t < T) logits[t * E + e] = acc[r] + b;
+  for (int i = 0; i < 16; ++i) {
+    const int64_t t = t0 + wm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+    if (t < T) logits[t * E + e] = (acc[i] + red[(wt * 16 + i) * 64 + lane]) + b;
   }
 }
 
@@ -398,18 +411,21 @@ __global__ __launch_bounds__(1024) void k_select_wave(const float* __restrict__ 
 
 // ---------------------------------------------------------------------------
 // Same selection with sixteen lanes per token (select_token_row), four tokens per
-// wave, 64 tokens per block of 16 waves.  grid = ceil(T/64), block = 1024.
+// wave, 32 tokens per block of 8 waves, so that a batch of a few thousand tokens
+// covers every CU.  Block 2b + h handles half h of permutation block b (64 tokens)
+// and writes its per-expert row counts to blk[h][b] ([2][nblk][E]; the scan adds
+// the halves).  grid = 2 * nblk, block = 512.
 template <int V>
-__global__ __launch_bounds__(1024) void k_select_rows(const float* __restrict__ logits, int64_t T,
-                                                      int E, int G, int Gk, int k,
-                                                      int32_t* __restrict__ ids,
-                                                      float* __restrict__ w,
-                                                      int32_t* __restrict__ blk) {
+__global__ __launch_bounds__(512) void k_select_rows(const float* __restrict__ logits, int64_t T,
+                                                     int E, int G, int Gk, int k,
+                                                     int32_t* __restrict__ ids,
+                                                     float* __restrict__ w,
+                                                     int32_t* __restrict__ blk, int nblk) {
   __shared__ int cnt[256];
-  for (int i = threadIdx.x; i < E; i += 1024) cnt[i] = 0;
+  for (int i = threadIdx.x; i < E; i += 512) cnt[i] = 0;
   __syncthreads();
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, r16 = lane & 15;
-  const int64_t t = int64_t(blockIdx.x) * 64 + wv * 4 + (lane >> 4);
+  const int64_t t = int64_t(blockIdx.x) * 32 + wv * 4 + (lane >> 4);
   const bool live = t < T;
   const float* l = logits + (live ? t : T - 1) * E + V * r16;
   float lv[V];
@@ -432,8 +448,10 @@ __global__ __launch_bounds__(1024) void k_select_rows(const float* __restrict__ 
     atomicAdd(&cnt[id], 1);
   }
   __syncthreads();
-  if (blk)
-    for (int i = threadIdx.x; i < E; i += 1024) blk[int64_t(blockIdx.x) * E + i] = cnt[i];
+  if (blk) {
+    int32_t* dst = blk + (int64_t(blockIdx.x & 1) * nblk + (blockIdx.x >> 1)) * E;
+    for (int i = threadIdx.x; i < E; i += 512) dst[i] = cnt[i];
+  }
 }
 
 // the row selection covers E = 16 V (V <= 16) with groups spanning a power-of-two
@@ -468,7 +486,7 @@ int launch_logits(const Plan& p, const void* x, const void* wr, const float* bia
   }
   if (logits_mfma_ok(p)) {
     const dim3 grid(unsigned((p.T + 63) / 64), unsigned(p.E / 64));
-    hipLaunchKernelGGL(k_logits_mfma, grid, dim3(256), 0, st, (const bf16_t*)x, (const bf16_t*)wr,
+    hipLaunchKernelGGL(k_logits_mfma, grid, dim3(512), 0, st, (const bf16_t*)x, (const bf16_t*)wr,
                        bias, p.T, p.H, p.E, logits);
     return check_launch();
   }
@@ -492,9 +510,10 @@ int launch_select(const Plan& p, const float* logits, int32_t* ids, float* w, in
   const dim3 grid(unsigned((p.T + 63) / 64));
   if (select_rows_ok(p)) {
     const int V = p.E / 16;
+    const dim3 grid2(unsigned(2 * p.nblk));
 #define MOE_SR(VV)                                                                              \
-  hipLaunchKernelGGL(k_select_rows<VV>, grid, dim3(1024), 0, st, logits, p.T, p.E, p.G, p.Gk, \
-                     p.k, ids, w, blk)
+  hipLaunchKernelGGL(k_select_rows<VV>, grid2, dim3(512), 0, st, logits, p.T, p.E, p.G, p.Gk, \
+                     p.k, ids, w, blk, p.nblk)
     if (V == 1) MOE_SR(1);
     else if (V == 2) MOE_SR(2);
     else if (V == 4) MOE_SR(4);
