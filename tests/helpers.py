@@ -60,7 +60,15 @@ def check_routing(gpu_ids, gpu_w, logits64, shape, w_atol=2e-6):
     clear = ~near
     assert np.array_equal(np.sort(gpu_ids[clear], axis=1), np.sort(o_ids[clear], axis=1)), \
         "expert ids differ on tokens with a clear margin"
-    assert np.array_equal(gpu_ids[clear], o_ids[clear]), "id order differs"
+    # slot order = descending logit: exact where consecutive chosen logits differ by more
+    # than the near-tie margin; where two are closer, either order is a valid ranking
+    o_l = np.take_along_axis(np.asarray(logits64, dtype=np.float64), o_ids, axis=1)
+    order_tie = (o_l[:, :-1] - o_l[:, 1:] <= NEAR_TIE).any(axis=1)
+    strict = clear & ~order_tie
+    assert np.array_equal(gpu_ids[strict], o_ids[strict]), "id order differs"
+    loose = clear & order_tie
+    g_l = np.take_along_axis(np.asarray(logits64, dtype=np.float64)[loose], gpu_ids[loose], axis=1)
+    assert (g_l[:, 1:] - g_l[:, :-1] <= NEAR_TIE).all(), "slots not in descending logit order"
     n = shape.E // shape.G
     for t in np.nonzero(near)[0]:
         ids_t = gpu_ids[t]
