@@ -261,6 +261,8 @@ struct BfTile {
 #define MOE_BF_WN 4
 #endif
 using BfCfg = BfTile<MOE_BF_BM, MOE_BF_BN, MOE_BF_BK, MOE_BF_WM, MOE_BF_WN>;
+// the NVFP4 kernel's tile (its per-thread conversion layout is built for this shape)
+using Nv4Cfg = BfTile<128, 256, 64, 2, 4>;
 
 template <bool GATEUP, class C>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
@@ -471,9 +473,9 @@ __device__ __forceinline__ uint32_t bf16_pair_hi(float lo, float hi) {
 }
 
 template <bool GATEUP>
-__global__ __launch_bounds__(BfCfg::NT) __attribute__((amdgpu_waves_per_eu(BfCfg::WPE)))
+__global__ __launch_bounds__(Nv4Cfg::NT) __attribute__((amdgpu_waves_per_eu(Nv4Cfg::WPE)))
 void k_gemm_nv4(GemmNv4Args p) {
-  using C = BfCfg;
+  using C = Nv4Cfg;
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, WM = C::WM, WN = C::WN, W = C::W;
   constexpr int MI = C::MI, NI = C::NI, CH = C::CH, RPD = C::RPD, AJ = C::AJ, NT = C::NT;
   static_assert(BK == 64 && BN * 2 == NT, "one thread per half row of a 64-deep weight slab");
@@ -691,8 +693,8 @@ void k_gemm_nv4(GemmNv4Args p) {
 
 // shapes the NVFP4 matrix-core kernels cover
 bool nv4_mfma_ok(const Plan& p) {
-  return p.wt == MOE_NVFP4 && p.I % (BfCfg::BN / 2) == 0 && p.H % BfCfg::BN == 0 &&
-         p.H % BfCfg::BK == 0 && p.I % BfCfg::BK == 0;
+  return p.wt == MOE_NVFP4 && p.I % (Nv4Cfg::BN / 2) == 0 && p.H % Nv4Cfg::BN == 0 &&
+         p.H % Nv4Cfg::BK == 0 && p.I % Nv4Cfg::BK == 0;
 }
 
 // shapes the pipelined bf16 kernel covers (else the register-staged one runs)
@@ -701,7 +703,9 @@ static bool bf_pipelined_ok(const Plan& p) {
          p.H % BfCfg::BK == 0 && p.I % BfCfg::BK == 0;
 }
 
-int gemm_tile_rows(const Plan& p) { return bf_pipelined_ok(p) ? BfCfg::BM : TM; }
+int gemm_tile_rows(const Plan& p) {
+  return bf_pipelined_ok(p) ? BfCfg::BM : nv4_mfma_ok(p) ? Nv4Cfg::BM : TM;
+}
 
 // ===========================================================================
 // Block FP8.  Weights e4m3 with one fp32 scale per 128x128 block; activations
@@ -1251,7 +1255,7 @@ int launch_gateup_mfma(const Plan& p, const void* x, const int32_t* row_token,
     a.g0 = w->g_gate; a.g1 = w->g_up; a.shg0 = w->sh_g_gate; a.shg1 = w->sh_g_up;
     a.out16 = (bf16_t*)h; a.K = p.H; a.N = p.I; a.E = p.E;
     launch_kernel(p, kTimeGateUp, k_gemm_nv4<true>,
-                  dim3(xcd_grid(p.max_tiles * (p.I / (BfCfg::BN / 2)))), dim3(BfCfg::NT), 0, st, a);
+                  dim3(xcd_grid(p.max_tiles * (p.I / (Nv4Cfg::BN / 2)))), dim3(Nv4Cfg::NT), 0, st, a);
   } else {
     GemmFp8Args a{};
     a.a = xq; a.a_scale = sx; a.row_token = row_token; a.offsets = offsets; a.tiles = tiles;
@@ -1292,7 +1296,7 @@ int launch_down_mfma(const Plan& p, const void* h, const int32_t* offsets, const
     a.b0 = w->b_down; a.shb0 = w->sh_b_down; a.g0 = w->g_down; a.shg0 = w->sh_g_down;
     a.row_w = row_w; a.out16 = out16; a.out32 = out32; a.K = p.I; a.N = p.H; a.E = p.E;
     launch_kernel(p, kTimeDown, k_gemm_nv4<false>,
-                  dim3(xcd_grid(p.max_tiles * (p.H / BfCfg::BN))), dim3(BfCfg::NT), 0, st, a);
+                  dim3(xcd_grid(p.max_tiles * (p.H / Nv4Cfg::BN))), dim3(Nv4Cfg::NT), 0, st, a);
   } else {
     GemmFp8Args a{};
     a.a = (const uint8_t*)h; a.a_scale = sh_scale; a.offsets = offsets; a.tiles = tiles;
