@@ -1209,23 +1209,41 @@ static bool fp8_pipelined_ok(const Plan& p) {
          p.H / 128 <= Fp8Tile::SMAX && p.I / 128 <= Fp8Tile::SMAX;
 }
 
+// Block-FP8 activations: per row and 128-wide block, scale = amax / 448 (1 for an
+// all-zero block) and codes = e4m3(v / scale), rounded to nearest even and saturated.
 template <typename TI>
 __global__ __launch_bounds__(256) void k_quant_e4m3(const TI* __restrict__ in, int64_t rows, int K,
                                                     uint8_t* __restrict__ codes,
                                                     float* __restrict__ scales) {
-  const int lane = threadIdx.x & 63;
+  // one 128-wide block per DPP row of 16 lanes (8 consecutive values per lane, one
+  // 16-byte load of bf16), four blocks per wave; rows past the end load a clamped
+  // block and store nothing
+  const int lane = threadIdx.x & 63, r16 = lane & 15;
   const int nkb = K / 128;
-  const int64_t idx = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (idx >= rows * nkb) return;
-  const int64_t row = idx / nkb;
-  const int kb = int(idx - row * nkb);
-  const int64_t off = row * K + kb * 128 + lane * 2;
-  const float v0 = to_f32(in[off]), v1 = to_f32(in[off + 1]);
-  const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
-  const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
-  const uint32_t c0 = f32_to_e4m3(v0 / scale), c1 = f32_to_e4m3(v1 / scale);
-  *reinterpret_cast<uint16_t*>(codes + off) = uint16_t(c0 | (c1 << 8));
-  if (lane == 0) scales[row * nkb + kb] = scale;
+  const int64_t nblk = rows * nkb;
+  const int64_t idx = (int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);
+  const bool live = idx < nblk;
+  const int64_t id = live ? idx : nblk - 1;
+  const int64_t row = id / nkb;
+  const int kb = int(id - row * nkb);
+  const int64_t off = row * K + kb * 128 + r16 * 8;
+  float v[8];
+  load8(in + off, v);
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+  m = fmaxf(m, dppf<0xB1>(m));    // quad_perm [1,0,3,2]
+  m = fmaxf(m, dppf<0x4E>(m));    // quad_perm [2,3,0,1]
+  m = fmaxf(m, dppf<0x141>(m));   // row_half_mirror
+  m = fmaxf(m, dppf<0x140>(m));   // row_mirror
+  const float scale = m > 0.f ? m / 448.0f : 1.0f;
+  uint32_t c[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i >> 2] |= f32_to_e4m3(v[i] / scale) << (8 * (i & 3));
+  if (live) {
+    *reinterpret_cast<uint2*>(codes + off) = make_uint2(c[0], c[1]);
+    if (r16 == 0) scales[row * nkb + kb] = scale;
+  }
 }
 
 // ===========================================================================
@@ -1315,7 +1333,8 @@ int launch_down_mfma(const Plan& p, const void* h, const int32_t* offsets, const
 int launch_quant(const Plan& p, const void* in, bool in_bf16, int64_t rows, int K, uint8_t* codes,
                  float* scales, hipStream_t st) {
   const int64_t n = rows * (K / 128);
-  const unsigned grid = unsigned((n + 3) / 4);
+  if (n == 0) return MOE_OK;
+  const unsigned grid = unsigned((n + 15) / 16);   // 16 blocks of 128 per workgroup
   if (in_bf16)
     hipLaunchKernelGGL(k_quant_e4m3<bf16_t>, dim3(grid), dim3(256), 0, st, (const bf16_t*)in, rows,
                        K, codes, scales);

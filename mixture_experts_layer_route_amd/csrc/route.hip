@@ -88,15 +88,15 @@ __global__ __launch_bounds__(256) void k_router_logits_fma(
 // ---------------------------------------------------------------------------
 // Logits for a few tokens (T <= 16): one wave per expert, every load of the
 // expert's row chunks and of the token rows issued from global memory before
-// any is used (one memory round trip per 4 tokens and 2048 hidden units), then a
-// DPP reduction per token.  grid = ceil(E/4), block = 256.
-template <typename TA>
+// any is used (one memory round trip per TQ tokens and SMAX 512-wide chunks of
+// the hidden units: 16 x 1, 8 x 2 or 4 x 4 by H), then a DPP reduction per token.
+// grid = ceil(E/4), block = 256.
+template <typename TA, int TQ, int SMAX>
 __global__ __launch_bounds__(256) void k_logits_few(const TA* __restrict__ x,
                                                     const TA* __restrict__ wr,
                                                     const float* __restrict__ bias,
                                                     float* __restrict__ logits, int T, int H,
                                                     int E) {
-  constexpr int SMAX = 4, TQ = 4;        // 512-wide chunks per pass, tokens per round trip
   const int lane = threadIdx.x & 63;
   const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (e >= E) return;                    // uniform over the wave
@@ -476,12 +476,19 @@ int launch_logits(const Plan& p, const void* x, const void* wr, const float* bia
                   hipStream_t st) {
   if (p.T <= 16) {
     const dim3 grid(unsigned((p.E + 3) / 4));
-    if (p.act == MOE_F32)
-      hipLaunchKernelGGL(k_logits_few<float>, grid, dim3(256), 0, st, (const float*)x,
-                         (const float*)wr, bias, logits, int(p.T), p.H, p.E);
-    else
-      hipLaunchKernelGGL(k_logits_few<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)x,
-                         (const bf16_t*)wr, bias, logits, int(p.T), p.H, p.E);
+#define MOE_LF(TQ, SM)                                                                          \
+  {                                                                                             \
+    if (p.act == MOE_F32)                                                                       \
+      hipLaunchKernelGGL((k_logits_few<float, TQ, SM>), grid, dim3(256), 0, st, (const float*)x, \
+                         (const float*)wr, bias, logits, int(p.T), p.H, p.E);                  \
+    else                                                                                        \
+      hipLaunchKernelGGL((k_logits_few<bf16_t, TQ, SM>), grid, dim3(256), 0, st,               \
+                         (const bf16_t*)x, (const bf16_t*)wr, bias, logits, int(p.T), p.H, p.E); \
+  }
+    if (p.H <= 512) MOE_LF(16, 1)
+    else if (p.H <= 1024) MOE_LF(8, 2)
+    else MOE_LF(4, 4)
+#undef MOE_LF
     return check_launch();
   }
   if (logits_mfma_ok(p)) {
