@@ -248,7 +248,12 @@ __global__ __launch_bounds__(256) void k_decode_gateup(DecodeArgs a) {
   // slot i = t*k + j.  Wave w owns slots [64w, 64w+64): bit (i % 64) of
   // bits[w][e] says slot i chose expert e, so a slot's rank among its expert's
   // rows is a popcount of the lower bits (rows stay in ascending slot order).
-  for (int i = threadIdx.x; i < 4 * E; i += 256) bits_l[i] = 0ull;
+  // With at most four tokens (sixteen lanes each, E + S <= 256, T*k <= 64) wave 0
+  // selects every token and also builds the row tables by itself (one_wave), so the
+  // other waves meet it at a single barrier.
+  const bool one_wave = SEL < 0 && T <= 4 && nslot <= 64 && E + S <= 256;
+  if (!one_wave)
+    for (int i = threadIdx.x; i < 4 * E; i += 256) bits_l[i] = 0ull;
   // the token rows and the logits travel in one memory round trip: the row
   // chunks are loaded into registers, the selection's logits loads follow, and
   // the rows are written to LDS afterwards
@@ -348,10 +353,57 @@ __global__ __launch_bounds__(256) void k_decode_gateup(DecodeArgs a) {
   }
 #endif
   if (prefetcher) wait_vm_lgkm0<MOE_DEC_PF>(); else wait_vm_lgkm0<0>();
+  const bool pub = blockIdx.x == 0;
+  if (one_wave) {
+    if (wv == 0) {
+      // everything below is this wave's own LDS traffic, in program order: the slot
+      // masks (one 64-bit mask per expert), counts, one wave-wide exclusive scan of
+      // (rows | 1 << 16 if active) over four experts per lane, then the placement
+      for (int e = lane; e < E; e += 64) bits_l[e] = 0ull;
+      if (lane < nslot) atomicOr(&bits_l[ids_l[lane]], 1ull << lane);
+      int v[4], sum = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = 4 * lane + q;
+        const int c = e < E ? __popcll(bits_l[e]) : e < E + S ? T : 0;
+        v[q] = c | (c > 0 ? 1 << 16 : 0);
+        sum += v[q];
+      }
+      int incl = sum;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      int run = incl - sum;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = 4 * lane + q;
+        if (e < E + S) {
+          off_l[e] = run & 0xFFFF;
+          if (v[q]) act_l[run >> 16] = e;
+          if (e >= E)
+            for (int t = 0; t < T; ++t) rt_l[(run & 0xFFFF) + t] = t;
+        }
+        run += v[q];
+      }
+      const int total = __shfl(incl, 63, 64);
+      if (lane == 0) {
+        off_l[E + S] = total & 0xFFFF;
+        n_act_l = total >> 16;
+      }
+      if (lane < nslot) {
+        const int e = ids_l[lane];
+        const int r = off_l[e] + __popcll(bits_l[e] & ((1ull << lane) - 1ull));
+        rt_l[r] = lane / k;
+        inv_l[lane] = r;
+      }
+    }
+    __syncthreads();
+  } else {
   __syncthreads();
   if (threadIdx.x < nslot) atomicOr(&bits_l[wv * E + ids_l[threadIdx.x]], 1ull << lane);
   __syncthreads();
-  const bool pub = blockIdx.x == 0;
   int tot = 0, nact = 0;
   for (int e0 = 0; e0 < E + S; e0 += 256) {
     const int e = e0 + threadIdx.x;
@@ -386,6 +438,7 @@ __global__ __launch_bounds__(256) void k_decode_gateup(DecodeArgs a) {
     inv_l[i] = r;
   }
   __syncthreads();
+  }
   if (pub) {
     for (int i = threadIdx.x; i < nslot; i += 256) {
       a.ids[i] = ids_l[i];

@@ -200,9 +200,15 @@ __device__ __forceinline__ float wave_max(float v) {
   return fmaxf(fmaxf(lanef(v, 0), lanef(v, 16)), fmaxf(lanef(v, 32), lanef(v, 48)));
 }
 
+// DPP move whose disabled-lane value is left undefined (every pattern used here reads
+// an enabled lane), so it compiles to one v_mov_b32_dpp without a copy of the source
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32_mov(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_mov_dpp(int(v), CTRL, 0xF, 0xF, false));
+}
 template <int CTRL>
 __device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
-  const uint32_t lo = dpp32<CTRL>(uint32_t(v)), hi = dpp32<CTRL>(uint32_t(v >> 32));
+  const uint32_t lo = dpp32_mov<CTRL>(uint32_t(v)), hi = dpp32_mov<CTRL>(uint32_t(v >> 32));
   const uint64_t w = (uint64_t(hi) << 32) | lo;
   return w > v ? w : v;
 }

@@ -120,11 +120,20 @@ __device__ int select_token_wave(const float* __restrict__ l, int E, int G, int 
 // power of two), or a lane holds V/n whole groups (n < V); G <= 64.  Keys are
 // (score, index) as in select_token_wave.  Returns, in row lane j < k, the j-th
 // chosen expert and its weight through `id_out` / `w_out`.
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
+  v = max(v, dpp32_mov<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = max(v, dpp32_mov<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = max(v, dpp32_mov<0x141>(v));   // row_half_mirror
+  return max(v, dpp32_mov<0x140>(v));   // row_mirror
+}
+// Row maximum of 64-bit keys as two 32-bit maxima (the high words, then the low
+// words of the lanes holding the highest high word): the same lexicographic
+// maximum with 32-bit DPP steps the compiler can fold into the max instructions.
 __device__ __forceinline__ uint64_t row_max_u64(uint64_t v) {
-  v = dpp_max_u64<0xB1>(v);    // quad_perm [1,0,3,2]
-  v = dpp_max_u64<0x4E>(v);    // quad_perm [2,3,0,1]
-  v = dpp_max_u64<0x141>(v);   // row_half_mirror
-  return dpp_max_u64<0x140>(v);   // row_mirror
+  const uint32_t hi = uint32_t(v >> 32), lo = uint32_t(v);
+  const uint32_t mh = row_max_u32(hi);
+  const uint32_t ml = row_max_u32(hi == mh ? lo : 0u);
+  return (uint64_t(mh) << 32) | ml;
 }
 __device__ __forceinline__ float row_sum(float v) {
   v += dppf<0xB1>(v);
@@ -138,6 +147,25 @@ __device__ __forceinline__ float row_segmax(float v, int span) {   // max over a
   if (span >= 8) v = fmaxf(v, dppf<0x141>(v));
   if (span >= 16) v = fmaxf(v, dppf<0x140>(v));
   return v;
+}
+
+// Sorts a lane's V keys into descending order: Batcher's odd-even merge network in
+// its iterative form (valid for any V; checked exhaustively on 0/1 inputs up to 16).
+template <int V>
+__device__ __forceinline__ void sort_keys_desc(uint64_t (&kv)[V]) {
+#pragma unroll
+  for (int p = 1; p < V; p <<= 1)
+#pragma unroll
+    for (int kk = p; kk >= 1; kk >>= 1)
+#pragma unroll
+      for (int j = kk % p; j + kk < V; j += 2 * kk)
+#pragma unroll
+        for (int i = 0; i < kk; ++i)
+          if (i + j + kk < V && (i + j) / (2 * p) == (i + j + kk) / (2 * p)) {
+            const uint64_t a = kv[i + j], b = kv[i + j + kk];
+            kv[i + j] = a > b ? a : b;
+            kv[i + j + kk] = a > b ? b : a;
+          }
 }
 
 template <int V>
@@ -193,16 +221,20 @@ __device__ void select_token_row(const float (&lv)[V], int E, int G, int Gk, int
     const int e = V * r16 + i;
     kv[i] = ((kept >> (e / n)) & 1ull) ? rank_key(lv[i], e) : 0ull;
   }
+  // Each lane's keys in descending order, so its largest remaining key is kv[0]: a
+  // round is one row arg-max over the lanes' heads, and the lane that held the
+  // winner (keys are distinct) moves its next key up.  Same winners, in the same
+  // order, as an arg-max over every remaining key.
+  sort_keys_desc<V>(kv);
   int idsel = 0;
   float lsel = 0.f, lmax = 0.f;
   for (int r = 0; r < k; ++r) {
-    uint64_t best = kv[0];
+    const uint64_t win = row_max_u64(kv[0]);
+    if (kv[0] == win) {
 #pragma unroll
-    for (int i = 1; i < V; ++i) best = kv[i] > best ? kv[i] : best;
-    const uint64_t win = row_max_u64(best);
-#pragma unroll
-    for (int i = 0; i < V; ++i)
-      if (kv[i] == win) kv[i] = 0ull;
+      for (int i = 0; i + 1 < V; ++i) kv[i] = kv[i + 1];
+      kv[V - 1] = 0ull;
+    }
     const float lw = key_score(win);
     if (r == 0) lmax = lw;
     if (r16 == r) { idsel = key_index(win); lsel = lw; }
