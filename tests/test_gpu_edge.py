@@ -36,6 +36,10 @@ CASES = [
     ("h640", 300, 640, 384, 64, 4, 2, 4, 0, "bf16", "bf16", "rms", 0.0, 28),     # register-staged bf16
     ("h640f8", 300, 640, 384, 64, 4, 2, 4, 0, "bf16", "e4m3", "rms", 0.0, 29),   # register-staged fp8
     ("f32b", 90, 256, 128, 16, 4, 2, 4, 1, "f32", "f32", "normal", 0.0, 30),     # fp32 + shared
+    # decode routing tables built by one wave: 64 slots (its slot-mask limit) with
+    # shared experts, and just past its 256-expert limit (the block-wide path)
+    ("w64slots", 4, 512, 256, 128, 8, 4, 16, 2, "bf16", "bf16", "rms", 0.0, 32),
+    ("w258", 4, 512, 256, 256, 8, 4, 8, 2, "bf16", "bf16", "rms", 0.0, 33),
 ]
 
 
