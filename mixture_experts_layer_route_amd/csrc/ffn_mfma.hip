@@ -187,7 +187,7 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmBf16Args p) {
       if (GATEUP) {
         const int col = ct * 64 + wn * 32 + (lane & 31);
         const float g = acc[mi][0][r], u = acc[mi][1][r];
-        p.out16[grow * p.N + col] = f32_to_bf16(silu(g) * u);
+        p.out16[grow * p.N + col] = f32_to_bf16(silu_lp(g) * u);
       } else {
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni) {
@@ -408,7 +408,7 @@ void k_gemm_bf16_v2(GemmBf16Args p) {
 #pragma unroll
           for (int b = 0; b < NI / 2; ++b) {
             const float g = acc[a][b][r], u = acc[a][b + NI / 2][r];
-            stg[row * LS + wn * (BN / 2 / WN) + b * 32 + (lane & 31)] = f32_to_bf16(silu(g) * u);
+            stg[row * LS + wn * (BN / 2 / WN) + b * 32 + (lane & 31)] = f32_to_bf16(silu_lp(g) * u);
           }
         } else {
           const float wr = roww[GATEUP ? 0 : a][GATEUP ? 0 : r];
@@ -656,7 +656,7 @@ void k_gemm_nv4(GemmNv4Args p) {
 #pragma unroll
           for (int b = 0; b < NI / 2; ++b) {
             const float g = acc[a][b][r] * gsc0, u = acc[a][b + NI / 2][r] * gsc1;
-            stg[row * LS + wn * (BN / 2 / WN) + b * 32 + (lane & 31)] = f32_to_bf16(silu(g) * u);
+            stg[row * LS + wn * (BN / 2 / WN) + b * 32 + (lane & 31)] = f32_to_bf16(silu_lp(g) * u);
           }
         } else {
           const float wr2 = roww[GATEUP ? 0 : a][GATEUP ? 0 : r] * gsc0;
@@ -895,10 +895,10 @@ __global__ __launch_bounds__(256) void k_gemm_fp8(GemmFp8Args p) {
       for (int q = 0; q < 4; ++q) {
         const int col = ct * 64 + ww * 32 + 8 * q + 4 * (lane >> 5);
         float4 v;
-        v.x = silu(acc[0][ri][4 * q + 0]) * acc[1][ri][4 * q + 0];
-        v.y = silu(acc[0][ri][4 * q + 1]) * acc[1][ri][4 * q + 1];
-        v.z = silu(acc[0][ri][4 * q + 2]) * acc[1][ri][4 * q + 2];
-        v.w = silu(acc[0][ri][4 * q + 3]) * acc[1][ri][4 * q + 3];
+        v.x = silu_lp(acc[0][ri][4 * q + 0]) * acc[1][ri][4 * q + 0];
+        v.y = silu_lp(acc[0][ri][4 * q + 1]) * acc[1][ri][4 * q + 1];
+        v.z = silu_lp(acc[0][ri][4 * q + 2]) * acc[1][ri][4 * q + 2];
+        v.w = silu_lp(acc[0][ri][4 * q + 3]) * acc[1][ri][4 * q + 3];
         *reinterpret_cast<float4*>(p.hout + grow * p.N + col) = v;
       }
     } else {
@@ -1125,7 +1125,7 @@ void k_gemm_fp8_v2(GemmFp8Args p) {
       float m = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        hv[a][r] = silu(acc[a][0][r]) * acc[a][1][r];
+        hv[a][r] = silu_lp(acc[a][0][r]) * acc[a][1][r];
         m = fmaxf(m, fabsf(hv[a][r]));
       }
       m = fmaxf(m, __shfl_xor(m, 32, 64));

@@ -265,5 +265,10 @@ __device__ __forceinline__ void e4m3_pair(uint32_t two, float& s0, float& s1) {
 }
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+// SiLU with the hardware reciprocal (within about 1 ulp of the correctly rounded
+// quotient) for outputs that are rounded to bf16 or e4m3 right after: the expert
+// GEMM epilogues, where the division sequence was a large share of the epilogue's
+// arithmetic.  The fp32 h of the decode and skinny kernels keeps the exact division.
+__device__ __forceinline__ float silu_lp(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 }  // namespace moe
