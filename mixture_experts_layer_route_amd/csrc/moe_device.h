@@ -71,10 +71,11 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ float bf16_to_f32(bf16_t v) { return __uint_as_float(uint32_t(v) << 16); }
 
 // Round-to-nearest-even fp32 -> bf16 (finite inputs).
+// fp32 -> bf16, round to nearest even: the conversion gfx950 does in one instruction
+// (v_cvt_pk_bf16_f32; the same rounding as adding 0x7FFF plus the kept lsb to the
+// fp32 bits for every finite value, and NaN stays NaN)
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return bf16_t(u >> 16);
+  return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
 }
 
 template <typename T> __device__ __forceinline__ float to_f32(T v);
