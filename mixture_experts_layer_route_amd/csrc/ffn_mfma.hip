@@ -1143,9 +1143,8 @@ void k_gemm_fp8_v2(GemmFp8Args p) {
       const int row = wm * (BM / WM) + a * 32 + (lane & 31);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        uint32_t pk = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pk |= f32_to_e4m3(hv[a][4 * g + i] / scale) << (8 * i);
+        const uint32_t pk = e4m3x4(hv[a][4 * g] / scale, hv[a][4 * g + 1] / scale,
+                                   hv[a][4 * g + 2] / scale, hv[a][4 * g + 3] / scale);
         const int col = wn * (BN / 2 / WN) + 8 * g + 4 * (lane >> 5);
         *reinterpret_cast<uint32_t*>(stg + row * 128 + col) = pk;
       }
@@ -1237,9 +1236,8 @@ __global__ __launch_bounds__(256) void k_quant_e4m3(const TI* __restrict__ in, i
   m = fmaxf(m, dppf<0x141>(m));   // row_half_mirror
   m = fmaxf(m, dppf<0x140>(m));   // row_mirror
   const float scale = m > 0.f ? m / 448.0f : 1.0f;
-  uint32_t c[2] = {0u, 0u};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) c[i >> 2] |= f32_to_e4m3(v[i] / scale) << (8 * (i & 3));
+  const uint32_t c[2] = {e4m3x4(v[0] / scale, v[1] / scale, v[2] / scale, v[3] / scale),
+                         e4m3x4(v[4] / scale, v[5] / scale, v[6] / scale, v[7] / scale)};
   if (live) {
     *reinterpret_cast<uint2*>(codes + off) = make_uint2(c[0], c[1]);
     if (r16 == 0) scales[row * nkb + kb] = scale;

@@ -156,7 +156,7 @@ __device__ __forceinline__ float dot8(const float (&a)[8], const float (&b)[8], 
 // OCP e4m3 (bias 7, 3 mantissa bits, max 448, no infinities), round to nearest
 // even, saturating.  Built from the format definition: normals are
 // (8 + m) * 2^(e-10) for e = 1..15 (code e<<3 | m), subnormals m * 2^-9.
-__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+__device__ __forceinline__ uint32_t f32_to_e4m3_formula(float v) {
   uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
   float a = fminf(fabsf(v), 448.0f);
   uint32_t code;
@@ -170,6 +170,15 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
     if (code > 0x7Eu) code = 0x7Eu;
   }
   return sign | code;
+}
+// Four values -> four codes (byte i = value i) with the gfx950 packed conversion, which
+// rounds to nearest even; the values are clamped to +-448 first so that it saturates
+// like the formula above.  The two agree on every non-NaN fp32 input: compared
+// exhaustively on the device, all 2^32 bit patterns but NaN, with no difference.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  auto cl = [](float v) { return fminf(fmaxf(v, -448.0f), 448.0f); };
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(cl(a), cl(b), 0, false);
+  return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(cl(c), cl(d), lo, true));
 }
 
 // ----------------------------------------------------------------- wave reductions
