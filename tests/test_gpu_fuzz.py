@@ -1,7 +1,7 @@
 """Seeded randomized shapes through the whole layer and the decoder step: 24 valid
 configurations drawn once from a fixed seed across every expert type (fp32, bf16, block
 FP8, NVFP4), grouped and ungrouped routers, shared experts and token counts from 1 to
-300, each checked against the oracle at the layer's bar.  The draw only picks sizes
+300, plus 16 few-token draws, each checked against the oracle at the layer's bar.  The draw only picks sizes
 within the documented limits; nothing here is meant to fail."""
 import numpy as np
 import pytest
@@ -36,7 +36,32 @@ def _draw_cases(n=24, seed=2024):
     return cases
 
 
-CASES = _draw_cases()
+def _draw_decode_cases(n=16, seed=2025):
+    """Few-token draws on expert counts the sixteen-lane selection covers (E = 16 V),
+    where up to four tokens build their row tables in one wave: 1-5 tokens, grouped or
+    not, shared experts, every expert type."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    wts = ["f32", "bf16", "e4m3", "nvfp4"]
+    for i in range(n):
+        wt = wts[i % 4]
+        act = "f32" if wt == "f32" else "bf16"
+        hm = {"f32": 8, "bf16": 8, "e4m3": 128, "nvfp4": 32}[wt]
+        H = int(rng.choice([hm * m for m in range(1, 1 + 1536 // hm)]))
+        I = int(rng.choice([hm * m for m in range(1, 1 + 512 // hm)]))
+        E = int(rng.choice([16, 64, 128, 256]))
+        G = int(rng.choice([g for g in (1, 2, 4, 8) if E // g >= 2]))
+        n_per = E // G
+        Gk = int(rng.integers(1, G + 1))
+        k = int(rng.integers(1, min(16, Gk * n_per) + 1))
+        S = int(rng.choice([0, 1, 2]))
+        T = int(rng.choice([1, 2, 3, 4, 5]))
+        cases.append((f"fzd{i}_{wt}", T, H, I, E, G, Gk, k, S, act, wt,
+                      "rms" if i % 2 else "normal", float(rng.choice([0.0, 0.3])), 4000 + i))
+    return cases
+
+
+CASES = _draw_cases() + _draw_decode_cases()
 
 
 @pytest.fixture(scope="module")
