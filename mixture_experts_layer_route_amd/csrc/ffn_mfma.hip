@@ -469,7 +469,8 @@ struct GemmNv4Args {
 };
 
 __device__ __forceinline__ uint32_t bf16_pair_hi(float lo, float hi) {
-  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+  // one v_perm_b32: bytes 2, 3 of lo, then bytes 2, 3 of hi
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
 
 template <bool GATEUP>
