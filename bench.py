@@ -55,6 +55,9 @@ def parse():
                     help="host time budget for the oracle baseline (0 = skip)")
     ap.add_argument("--event-every", type=int, default=8,
                     help="attach kernel start/stop events to every n-th timed step")
+    ap.add_argument("--no-prefill-leg", action="store_true",
+                    help="decode workload only: skip the 8192-token prefill layer that the "
+                         "default line carries as its second measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (a known byte "
                          "count for scaling the profiler's FETCH_SIZE / WRITE_SIZE) and exit")
@@ -78,21 +81,26 @@ def measured_traffic(workload, which):
     (profiles/<workload>_traffic.json: rocprofv3 FETCH_SIZE and WRITE_SIZE, scaled by a
     copy-kernel calibration).  None when there is none, or when the kernel sources have
     changed since the counters were taken."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
+    if rec.get("sources_sha256") != sources_sha256() or which not in rec.get("kernels", {}):
+        return None
+    return rec["kernels"][which]["hbm_bytes_per_launch"]
+
+
+def sources_sha256():
+    """SHA-256 over the kernel sources (file names and contents, in name order)."""
+    import hashlib
     h = hashlib.sha256()
     src = os.path.join(ROOT, "mixture_experts_layer_route_amd", "csrc")
     for name in sorted(os.listdir(src)):
         h.update(name.encode())
         with open(os.path.join(src, name), "rb") as f:
             h.update(f.read())
-    if rec.get("sources_sha256") != h.hexdigest() or which not in rec.get("kernels", {}):
-        return None
-    return rec["kernels"][which]["hbm_bytes_per_launch"]
+    return h.hexdigest()
 
 
 def kernel_roofline(shape, which, ms, U):
@@ -166,19 +174,36 @@ def oracle_experts(mo, cpu, f):
     return mo.Experts(*(f(cpu[n]) for n in WEIGHT_KEYS), nv=nv, sh_nv=sh_nv)
 
 
-def blas_threads():
-    """Threads numpy's BLAS runs the oracle with."""
+def blas_info():
+    """(library, threads) of the BLAS numpy runs the oracle's matrix products with."""
     try:
         from threadpoolctl import threadpool_info
-        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        infos = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if infos:
+            i = infos[0]
+            name = f"{i.get('internal_api', '?')} {i.get('version', '')}".strip()
+            return name, int(i.get("num_threads", 1))
     except Exception:  # pragma: no cover
-        return os.cpu_count()
+        pass
+    return "unknown", os.cpu_count()
+
+
+def host_cores():
+    return len(os.sched_getaffinity(0))
+
+
+def baseline_entry(value, sample):
+    """cpu_baseline record: `cores` is the threads the oracle ran on (its BLAS threads;
+    the rest of the oracle is single-threaded numpy), beside the host's core count."""
+    blas, threads = blas_info()
+    return {"value": value, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": sample, "host_cores": host_cores(), "blas": blas,
+            "blas_threads": int(threads)}
 
 
 def cpu_baseline(shape, cpu, budget_s):
     """The float64 oracle, as it stands, on a bounded sample of the same workload."""
     from oracle import moe_oracle as mo
-    threads = blas_threads()
     f = lambda t: None if t is None else (t.numpy() if t.dtype.itemsize == 1 else t.float().numpy())
     ex = oracle_experts(mo, cpu, f)
     x, wr, b = f(cpu["x"]), f(cpu["w_router"]), f(cpu["router_bias"])
@@ -192,10 +217,10 @@ def cpu_baseline(shape, cpu, budget_s):
         if time.perf_counter() - t0 >= budget_s:
             break
     el = time.perf_counter() - t0
-    return {"value": round(reps * n_tok / el, 3), "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{reps} x oracle forward of the first {n_tok} of {shape.T} tokens "
-                      f"(full routing + experts + combine, float64 numpy), {el:.1f} s"}
+    return baseline_entry(
+        round(reps * n_tok / el, 3),
+        f"{reps} x oracle forward of the first {n_tok} of {shape.T} tokens "
+        f"(full routing + experts + combine, float64 numpy), {el:.1f} s")
 
 
 def run_stack(args):
@@ -314,34 +339,23 @@ def run_stack(args):
             if time.perf_counter() - t0 >= args.cpu_seconds:
                 break
         el = time.perf_counter() - t0
-        res["cpu_baseline"] = {"value": round(reps * shape.T / el, 3), "unit": "tokens/s",
-                               "cores": blas_threads(), "kind": "oracle",
-                               "sample": f"{reps} x the oracle's {L}-block step on the same "
-                                         f"{shape.T} tokens (float64 numpy), {el:.1f} s"}
+        res["cpu_baseline"] = baseline_entry(
+            round(reps * shape.T / el, 3),
+            f"{reps} x the oracle's {L}-block step on the same {shape.T} tokens "
+            f"(float64 numpy), {el:.1f} s")
     print(json.dumps(res), flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer is built "
-              "and measured on a single MI355X", file=sys.stderr)
-        sys.exit(2)
-    if args.copy_calibration:
-        copy_calibration(args.copy_calibration)
-        return
-    if args.workload == "decode_stack":
-        run_stack(args)
-        return
+def measure(workload, nsets, K, W, event_every):
+    """Time K steps (after W warm-up steps) of one workload's layer, weights rotating over
+    `nsets` copies, with kernel events on every `event_every`-th step; parity of what is
+    timed on sampled tokens.  Returns (partial JSON record, shape, CPU layer)."""
     import torch
     import mixture_experts_layer_route_amd as moe
     import synth
     from oracle import moe_oracle as mo
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    moe.load_library()
-    shape = synth.WORKLOADS[args.workload]
-    nsets = args.sets or DEFAULT_SETS[args.workload]
+    shape = synth.WORKLOADS[workload]
     log(f"workload {shape}; weight sets {nsets}")
     cpu = synth.make_layer(shape)
     dev = {k: (None if v is None else v.cuda()) for k, v in cpu.items()}
@@ -375,12 +389,11 @@ def main():
     err = mo.rel_l2(y.float().cpu().numpy()[sample], ref)
     log(f"parity on {len(sample)} tokens: rel_l2 {err:.3e}; unique experts {U}")
 
-    K, W = args.steps, args.warmup
     for i in range(W):
         moe.forward(cfg, x, None, ws, y=y, wst=wsts[i % nsets])
     # start/stop events attached to the gate/up and down kernel dispatches of every
     # n-th timed step (each attached event costs a few microseconds of queue time)
-    every = max(1, args.event_every)
+    every = max(1, event_every)
     timed = list(range(0, K, every))
     ev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(moe.TIMED_EVENTS)] for i in timed}
     for row in ev.values():
@@ -435,6 +448,35 @@ def main():
         "roofline": roof,
         "step_roofline": step_roofline(shape, ms_per_step, U),
     }
+    return res, shape, cpu
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer is built "
+              "and measured on a single MI355X", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+    if args.workload == "decode_stack":
+        run_stack(args)
+        return
+    import torch
+    import mixture_experts_layer_route_amd as moe
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    moe.load_library()
+    res, shape, cpu = measure(args.workload, args.sets or DEFAULT_SETS[args.workload], args.steps,
+                              args.warmup, args.event_every)
+    if args.workload == "decode" and not args.no_prefill_leg:
+        # the metric's second half: the 8192-token prefill layer, timed the same way
+        leg, _, _ = measure("prefill", DEFAULT_SETS["prefill"], min(args.steps, 50),
+                            min(args.warmup, 10), args.event_every)
+        res["prefill_leg"] = {k: leg[k] for k in (
+            "value", "unit", "ms_per_step", "steps", "warmup", "config", "kernel_us",
+            "ms_per_step_without_kernel_events", "parity_rel_l2", "roofline", "step_roofline")}
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(shape, cpu, args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -7,8 +7,8 @@
  *     comment, config paragraph: 128 experts in 8 groups of 16 with 4 groups
  *     kept, hidden 1536, SwiGLU experts whose limit lists are null (no clamp);
  *     list "What it does not cover": the router is group-limited, and the bf16
- *     experts run each expert on just the rows that picked it, which today
- *     costs a host synchronisation per layer.
+ *     experts are computed per expert over the rows routed to it, a grouping
+ *     that costs a host synchronisation per layer there.
  *   - HelloSun/ling30tiny model card, routing table (模型與路由): 8 experts per
  *     token; numeric-check summary (數值檢查摘要): routing plus a weighted layer.
  *   - llama.cpp PR "Add TML Inkling architecture", PR summary: 256 experts,
@@ -149,8 +149,9 @@ int moe_route(const moe_config* cfg, const void* x, const void* w_router, const 
               void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
- * Permutation ("each expert on just the rows that picked it", TensorFold #1247,
- * "What it does not cover"), computed on the device without a host sync.
+ * Permutation: the slots grouped by expert (the rows-per-expert grouping of
+ * TensorFold #1247, list "What it does not cover"), computed on the device
+ * without a host sync.
  * R = T*k + T*S rows.  Rows of routed expert e are the slots (t,j) with
  * topk_ids[t,j] == e, in ascending (t, j) order; shared expert s owns rows
  * [T*k + s*T, T*k + (s+1)*T), one per token in order.
@@ -230,6 +231,24 @@ int moe_forward_timed(const moe_config* cfg, const void* x, const moe_weights* w
 int moe_forward_residual(const moe_config* cfg, const void* x, const void* norm_weight,
                          float norm_eps, const moe_weights* w, void* x_out, int32_t* topk_ids_out,
                          float* topk_w_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Where a call leaves inspectable intermediate results in the workspace, for tests
+ * and debugging (host only, no device work).  After moe_forward / moe_forward_timed /
+ * moe_forward_residual (and moe_route with logits == NULL) the workspace holds:
+ *   MOE_WS_LOGITS      [T,E] fp32 router logits the routing was decided on (bias included);
+ *   MOE_WS_ACT_CODES   [T,H] uint8 e4m3 codes of x (block-FP8 experts only, else 0 bytes);
+ *   MOE_WS_ACT_SCALES  [T,H/128] fp32 scales of those codes (block-FP8 only);
+ *   MOE_WS_NORM_ROWS   [T,H] act_dtype normalised rows (moe_forward_residual only).
+ * The contents stay valid until the next call that uses the same workspace.  Writes the
+ * byte offset from the workspace start and the slot's size; MOE_ERR_ARG for an unknown
+ * slot or a null output pointer, or a validation error of the config.
+ */
+#define MOE_WS_LOGITS      0
+#define MOE_WS_ACT_CODES   1
+#define MOE_WS_ACT_SCALES  2
+#define MOE_WS_NORM_ROWS   3
+int moe_workspace_slot(const moe_config* cfg, int slot, size_t* offset, size_t* bytes);
 
 /* Static description of a status code (for MOE_ERR_HIP: the last HIP error text
    seen by this thread).  Never NULL. */

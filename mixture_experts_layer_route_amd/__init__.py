@@ -39,7 +39,8 @@ class MoeWeights(ctypes.Structure):
 
 ENTRY_POINTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn",
                 "moe_combine", "moe_forward", "moe_forward_timed", "moe_forward_residual",
-                "moe_strerror")
+                "moe_workspace_slot", "moe_strerror")
+WS_LOGITS, WS_ACT_CODES, WS_ACT_SCALES, WS_NORM_ROWS = 0, 1, 2, 3   # MOE_WS_* slots
 TIMED_EVENTS = 4   # MOE_TIMED_EVENTS: start/stop of the gate/up kernel, start/stop of the down kernel
 
 _lib = None
@@ -66,6 +67,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_forward": [cfgp, P, wp, P, P, P, P, SZ, P],
         "moe_forward_timed": [cfgp, P, wp, P, P, P, P, SZ, P, P],
         "moe_forward_residual": [cfgp, P, P, ctypes.c_float, wp, P, P, P, P, SZ, P],
+        "moe_workspace_slot": [cfgp, ctypes.c_int, ctypes.POINTER(SZ), ctypes.POINTER(SZ)],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -111,6 +113,14 @@ def workspace_size(cfg: MoeConfig) -> int:
     n = ctypes.c_size_t(0)
     _check(load_library().moe_workspace_size(ctypes.byref(cfg), ctypes.byref(n)))
     return int(n.value)
+
+
+def workspace_slot(cfg: MoeConfig, slot: int):
+    """(byte offset, bytes) of an inspectable workspace slot (MOE_WS_*)."""
+    off, n = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(load_library().moe_workspace_slot(ctypes.byref(cfg), slot, ctypes.byref(off),
+                                             ctypes.byref(n)))
+    return int(off.value), int(n.value)
 
 
 def alloc_workspace(cfg: MoeConfig, device="cuda") -> torch.Tensor:

@@ -3,7 +3,7 @@
 //
 // With a few tokens the layer is a stream over the chosen experts' weights
 // (TensorFold issue #1247 "Ling-3.0-tiny on a Qualcomm board", list "What it does
-// not cover": each expert runs on just the rows that picked it), so both kernels
+// not cover": experts computed over the rows routed to them), so both kernels
 // are organised around that stream:
 //   gate/up: every block first routes the T tokens itself from the logits into
 //     LDS (sixteen lanes or a wave per token select; the rows of each expert are

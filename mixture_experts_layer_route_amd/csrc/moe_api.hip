@@ -162,6 +162,24 @@ int moe_workspace_size(const moe_config* cfg, size_t* bytes) {
   return MOE_OK;
 }
 
+int moe_workspace_slot(const moe_config* cfg, int slot, size_t* offset, size_t* bytes) {
+  if (!offset || !bytes) return MOE_ERR_ARG;
+  Plan p;
+  MOE_TRY(make_plan(cfg, &p));
+  const bool fp8 = p.wt == MOE_E4M3_B128;
+  switch (slot) {
+    case MOE_WS_LOGITS: *offset = p.o_logits; *bytes = size_t(p.T) * p.E * 4; break;
+    case MOE_WS_ACT_CODES: *offset = p.o_xq; *bytes = fp8 ? size_t(p.T) * p.H : 0; break;
+    case MOE_WS_ACT_SCALES: *offset = p.o_sx; *bytes = fp8 ? size_t(p.T) * (p.H / 128) * 4 : 0; break;
+    case MOE_WS_NORM_ROWS:
+      *offset = p.o_xn;
+      *bytes = size_t(p.T) * p.H * (p.act == MOE_F32 ? 4 : 2);
+      break;
+    default: return MOE_ERR_ARG;
+  }
+  return MOE_OK;
+}
+
 int moe_route(const moe_config* cfg, const void* x, const void* w_router, const float* router_bias,
               int32_t* topk_ids, float* topk_w, float* logits, void* ws, size_t ws_bytes,
               hipStream_t stream) {

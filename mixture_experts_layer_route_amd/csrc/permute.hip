@@ -1,8 +1,8 @@
 // Permutation: per-expert row lists, built on the device with no host sync.
 //
 // TensorFold issue #1247 "Ling-3.0-tiny on a Qualcomm board" (jschmied's comment,
-// list "What it does not cover") runs each bf16 expert on just the rows that
-// picked it, at the cost of a host synchronisation per layer.  Here the rows are
+// list "What it does not cover") computes each bf16 expert over the rows routed
+// to it, paying a host synchronisation per layer for the grouping.  Here the rows are
 // grouped on the device: a per-block histogram, one exclusive scan into expert
 // offsets (plus the schedule the expert kernels read), and a stable scatter.
 // Rows of one expert are ordered by ascending (token, slot); shared experts own
@@ -169,7 +169,8 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int32_t* __restrict__ blk,
   if (e >= E && e < E + S) cnt = int(T);
   build_schedule(cnt, E + S, BM, offs, active, meta, tiles, tmp);
   __syncthreads();
-  if (e <= E + S) offsets[e] = offs[e];
+  // E + S may be 1024: the total offsets[E + S] then lies beyond the last thread
+  for (int i = threadIdx.x; i <= E + S; i += blockDim.x) offsets[i] = offs[i];
   int run = mine ? offs[ge] : 0;
   for (int b0 = 0; b0 < nblk; b0 += CB) {
     const int nb = min(CB, nblk - b0);
@@ -262,7 +263,8 @@ __global__ __launch_bounds__(1024) void k_perm_scan_reg(int32_t* __restrict__ bl
   }
   build_schedule(cnt, E + S, BM, offs, active, meta, tiles, tmp);
   __syncthreads();
-  if (tid <= E + S) offsets[tid] = offs[tid];
+  // E + S may be 1024: the total offsets[E + S] then lies beyond the last thread
+  for (int i = threadIdx.x; i <= E + S; i += blockDim.x) offsets[i] = offs[i];
   if (mine) {
     int r = offs[ge] + psum[tid];
 #pragma unroll
@@ -366,7 +368,8 @@ __global__ __launch_bounds__(1024) void k_route_permute_small(
   }
   build_schedule(cnt, E + S, BM, offs, active, meta, tiles, tmp);
   __syncthreads();
-  if (e <= E + S) offsets[e] = offs[e];
+  // E + S may be 1024: the total offsets[E + S] then lies beyond the last thread
+  for (int i = threadIdx.x; i <= E + S; i += blockDim.x) offsets[i] = offs[i];
   if (e < E && cnt > 0) {
     int r = offs[e];
     for (int i = 0; i < nslot; ++i) {

@@ -9,9 +9,10 @@ What the layer computes comes from the pages:
     comment: the config paragraph gives the Ling-3.0-tiny MoE shape (128
     experts, 8 groups of 16, 4 groups kept, hidden 1536) and says the SwiGLU
     limit lists are null (no clamp); the list "What it does not cover" says the
-    router is group-limited and that the bf16 experts run each expert on the
-    rows that picked it; the list "What #874's CUDA path now covers" describes
-    checking against a float64 forward on the same routing by relative L2.
+    router is group-limited and that the bf16 experts are computed per expert
+    over the rows routed to it; the list "What #874's CUDA path now covers" describes
+    checking by relative L2 against a float64 forward pass that uses identical
+    expert choices.
   * HelloSun/ling30tiny model card, routing table (模型與路由): 8 experts active
     per token, 128 experts per layer; the numeric-check summary (數值檢查摘要)
     names the layer as routing plus a weighted sum of the chosen experts.
@@ -219,11 +220,13 @@ def e4m3_encode(v) -> np.ndarray:
     return (mag | sign).astype(np.uint8)
 
 
-def quantize_act(v, block: int = FP8_BLOCK) -> np.ndarray:
-    """Activation quantisation of reading R9, per row per `block` along the last axis.
+def quantize_act_codes(v, block: int = FP8_BLOCK):
+    """Activation quantisation of reading R9, per row per `block` along the last axis,
+    as stored: (codes uint8 [rows, cols], scales float32 [rows, cols / block]).
 
-    Returns the dequantised float64 values code * scale.  The decisions are taken
-    in fp32: the row values are first held in fp32 (as the kernels hold them)."""
+    The decisions are taken in fp32: the row values are first held in fp32 (as the
+    kernels hold them), scale = fp32(amax) / 448 by one IEEE fp32 division (1 for an
+    all-zero block), code = e4m3 of the fp32 quotient v / scale."""
     v32 = np.asarray(v, dtype=np.float64).astype(np.float32)
     rows, cols = v32.shape
     blocks = v32.reshape(rows, cols // block, block)
@@ -231,8 +234,15 @@ def quantize_act(v, block: int = FP8_BLOCK) -> np.ndarray:
     scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
     scale[amax == 0] = np.float32(1.0)
     q32 = (blocks / scale[:, :, None]).astype(np.float32)
-    codes = e4m3_encode(q32)
-    return (e4m3_decode(codes) * scale[:, :, None].astype(np.float64)).reshape(rows, cols)
+    return e4m3_encode(q32).reshape(rows, cols), scale
+
+
+def quantize_act(v, block: int = FP8_BLOCK) -> np.ndarray:
+    """Activation quantisation of reading R9: the dequantised float64 values code * scale."""
+    codes, scale = quantize_act_codes(v, block)
+    rows, cols = codes.shape
+    vals = e4m3_decode(codes).reshape(rows, cols // block, block)
+    return (vals * scale[:, :, None].astype(np.float64)).reshape(rows, cols)
 
 
 def dequant_blocks(codes, scales, block: int = FP8_BLOCK) -> np.ndarray:
@@ -384,8 +394,8 @@ def swiglu_expert(X, Wg, Wu, Wd, fp8: bool = False) -> np.ndarray:
 def expert_ffn(x, offsets, row_token, experts: Experts) -> np.ndarray:
     """Unweighted expert outputs in permuted row order: y_perm[r] = FFN_{expert(r)}(x[row_token[r]]).
 
-    Each expert runs on just the rows that picked it (TensorFold #1247, "What it does
-    not cover", bf16 expert paragraph), shared experts on every token."""
+    Every expert sees only the rows routed to it (the rows-per-expert grouping of
+    TensorFold #1247, list "What it does not cover"), shared experts every token."""
     x = _f64(x)
     offsets = np.asarray(offsets, dtype=np.int64)
     row_token = np.asarray(row_token, dtype=np.int64)
@@ -419,7 +429,7 @@ def combine(y_perm, offsets, inv, w, S: int = 0) -> np.ndarray:
 def forward(x, w_router, bias, experts: Experts, G: int, Gk: int, k: int, ids=None) -> dict:
     """The whole layer, expert-major: route, permute, run each expert on its rows, combine.
 
-    With `ids` given (forced routing, the "same routing" comparison of TensorFold #1247
+    With `ids` given (forced routing: the identical-choice comparison of TensorFold #1247
     "What #874's CUDA path now covers"), those experts are used and their weights are
     the oracle's own scores renormalised over them."""
     logits = router_logits(x, w_router, bias)
@@ -453,7 +463,16 @@ def forward_tokenmajor(x, experts: Experts, ids, w) -> np.ndarray:
 
 
 def rel_l2(a, ref) -> float:
-    """||a - ref||_2 / ||ref||_2 over the whole array, in float64."""
+    """||a - ref||_2 / ||ref||_2 over the whole array, in float64 (the relative L2 of
+    TensorFold #1247, list "What #874's CUDA path now covers")."""
     a = _f64(a)
     ref = _f64(ref)
     return float(np.linalg.norm((a - ref).ravel()) / np.linalg.norm(ref.ravel()))
+
+
+def row_rel_l2(a, ref) -> np.ndarray:
+    """Relative L2 of each row (token) of [T, H] arrays: ||a[t] - ref[t]|| / ||ref[t]||.
+    A wrong row that the whole-array figure would dilute stands out here."""
+    a = _f64(a)
+    ref = _f64(ref)
+    return np.linalg.norm(a - ref, axis=1) / np.linalg.norm(ref, axis=1)

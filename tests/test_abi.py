@@ -146,3 +146,26 @@ def test_forward_timed_rejects_missing_events(lib):
     ev = (ctypes.c_void_p * moe.TIMED_EVENTS)(*([1 << 40] * (moe.TIMED_EVENTS - 1) + [None]))
     assert lib.moe_forward_timed(ctypes.byref(cfg), fake, ctypes.byref(w), fake, None, None, fake,
                                  1 << 40, None, ev) == -1
+
+
+def test_workspace_slots_lie_inside_the_workspace(lib):
+    for kw in (dict(), dict(wt="e4m3", T=2048), dict(T=8192), dict(act="f32", wt="f32", H=256, I=128,
+                                                                  E=16, G=4, Gk=2, k=4)):
+        cfg = _cfg(**kw)
+        total = moe.workspace_size(cfg)
+        spans = []
+        for slot in (moe.WS_LOGITS, moe.WS_ACT_CODES, moe.WS_ACT_SCALES, moe.WS_NORM_ROWS):
+            off, n = moe.workspace_slot(cfg, slot)
+            assert off % 256 == 0 and off + n <= total, (kw, slot)
+            if n:
+                spans.append((off, off + n))
+        spans.sort()
+        assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:])), kw
+        T, H, E = cfg.num_tokens, cfg.hidden, cfg.num_experts
+        assert moe.workspace_slot(cfg, moe.WS_LOGITS)[1] == T * E * 4
+        fp8 = kw.get("wt") == "e4m3"
+        assert moe.workspace_slot(cfg, moe.WS_ACT_CODES)[1] == (T * H if fp8 else 0)
+        assert moe.workspace_slot(cfg, moe.WS_ACT_SCALES)[1] == (T * H // 32 if fp8 else 0)
+    n = ctypes.c_size_t(0)
+    assert lib.moe_workspace_slot(ctypes.byref(_cfg()), 7, ctypes.byref(n), ctypes.byref(n)) == -1
+    assert lib.moe_workspace_slot(ctypes.byref(_cfg()), 0, None, ctypes.byref(n)) == -1

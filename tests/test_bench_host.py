@@ -1,6 +1,7 @@
 """Host-side checks of bench.py (no GPU): the one-GPU guard, the algorithmic bytes and
 flops behind the roofline entries, and the rule that counter traffic is reported only
 while the kernel sources match the ones the counters were taken on."""
+import json
 import os
 import shutil
 import subprocess
@@ -60,10 +61,14 @@ def test_counter_traffic_only_while_the_sources_match(tmp_path, monkeypatch):
     src = os.path.join(ROOT, "mixture_experts_layer_route_amd", "csrc")
     dst = tmp_path / "mixture_experts_layer_route_amd" / "csrc"
     shutil.copytree(src, dst)
-    shutil.copytree(os.path.join(ROOT, "profiles"), tmp_path / "profiles")
+    os.makedirs(tmp_path / "profiles")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    rec = {"sources_sha256": bench.sources_sha256(),
+           "kernels": {"gateup": {"hbm_bytes_per_launch": 123456}}}
+    with open(tmp_path / "profiles" / "decode_traffic.json", "w") as f:
+        json.dump(rec, f)
     got = bench.measured_traffic("decode", "gateup")
-    assert isinstance(got, int) and got > 0
+    assert got == 123456
     assert bench.measured_traffic("decode", "no_such_kernel") is None
     assert bench.measured_traffic("no_such_workload", "gateup") is None
     with open(dst / "combine.hip", "a") as f:

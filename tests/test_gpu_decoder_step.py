@@ -41,11 +41,11 @@ def _bf16_step(v):
 
 
 def _xn_from_ws(moe, cfg, ws, shape):
-    """The step's normalised rows, left in the workspace's last slot (256-byte aligned,
-    T*H elements of the activation type)."""
+    """The step's normalised rows (workspace slot MOE_WS_NORM_ROWS, T*H elements of the
+    activation type)."""
     esz = 4 if shape.act == "f32" else 2
-    n = shape.T * shape.H * esz
-    o = moe.workspace_size(cfg) - ((n + 255) // 256) * 256
+    o, n = moe.workspace_slot(cfg, moe.WS_NORM_ROWS)
+    assert n == shape.T * shape.H * esz
     raw = ws[o:o + n].cpu()
     return raw.view(torch.float32 if esz == 4 else torch.bfloat16).reshape(shape.T, shape.H)
 

@@ -232,3 +232,51 @@ def test_fp8_layer_with_exact_values_equals_dense_with_h_quantised():
     g, u = x @ Wg.T, x @ Wu.T
     h = g * scipy.special.expit(g) * u
     assert mo.rel_l2(y8, mo.quantize_act(h) @ Wd.T) < 1e-14
+
+
+# ----------------------------------------------------------------- parity metrics
+def test_rel_l2_hand_values():
+    """||a - ref|| / ||ref|| over the whole array, worked by hand: a missing square root,
+    a division by ||a||, or a per-row mean would each give a different number."""
+    ref = np.array([[3.0, 4.0]])                       # ||ref|| = 5
+    a = ref + np.array([[0.6, 0.8]])                   # ||a - ref|| = 1, ||a|| = 6
+    assert mo.rel_l2(a, ref) == pytest.approx(0.2, abs=1e-15)      # not 0.04, not 1/6
+    ref2 = np.array([[3.0, 4.0], [6.0, 8.0]])          # ||ref2||^2 = 125
+    a2 = ref2 + np.array([[0.0, 0.0], [0.0, 5.0]])     # ||a2 - ref2|| = 5
+    assert mo.rel_l2(a2, ref2) == pytest.approx(1 / np.sqrt(5), abs=1e-15)   # per-row mean: 0.25
+    assert mo.rel_l2(ref2, ref2) == 0.0
+    assert mo.rel_l2(-ref2, ref2) == pytest.approx(2.0, abs=1e-15)
+
+
+def test_row_rel_l2_hand_values():
+    ref = np.array([[3.0, 4.0], [6.0, 8.0], [0.0, 2.0]])
+    a = ref + np.array([[0.6, 0.8], [0.0, 0.0], [1.0, 0.0]])
+    np.testing.assert_allclose(mo.row_rel_l2(a, ref), [0.2, 0.0, 0.5], rtol=0, atol=1e-15)
+
+
+def test_quantize_act_codes_hand_and_torch():
+    """Stored form of reading R9.  A block whose amax is 896 has scale exactly 2, so
+    its codes are those of the halved values; other blocks follow fp32 division and
+    torch's saturating-free e4m3 cast of the fp32 quotient (a library routine)."""
+    vals = mo.e4m3_values()
+    fin = np.sort(vals[np.isfinite(vals) & (vals >= 0)])
+    row = np.zeros((1, 256), np.float32)
+    row[0, :128] = 2.0 * np.resize(fin, 128)           # values 2 * e4m3, amax 896
+    row[0, 127] = -896.0
+    rng = np.random.default_rng(41)
+    row[0, 128:] = rng.standard_normal(128).astype(np.float32) * 3
+    codes, scales = mo.quantize_act_codes(row)
+    assert codes.dtype == np.uint8 and codes.shape == (1, 256) and scales.shape == (1, 2)
+    assert scales[0, 0] == np.float32(2.0)
+    assert codes[0, 127] == 0xFE                        # -448
+    assert np.array_equal(mo.e4m3_decode(codes[0, :127]) * 2.0, row[0, :127].astype(np.float64))
+    amax = np.float32(np.abs(row[0, 128:]).max())
+    assert scales[0, 1] == amax / np.float32(448.0)    # one IEEE fp32 division
+    q32 = (row[0, 128:] / scales[0, 1]).astype(np.float32)
+    ref = torch.from_numpy(np.clip(q32, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8)
+    assert np.array_equal(codes[0, 128:], ref.numpy())
+    # all-zero block: scale 1, codes 0; dequantised form agrees with quantize_act
+    z_codes, z_scales = mo.quantize_act_codes(np.zeros((2, 128)))
+    assert np.all(z_codes == 0) and np.all(z_scales == 1.0)
+    deq = mo.e4m3_decode(codes).reshape(1, 2, 128) * scales[:, :, None].astype(np.float64)
+    assert np.array_equal(deq.reshape(1, 256), mo.quantize_act(row))
