@@ -58,6 +58,8 @@ extern "C" {
 #define MOE_ERR_UNSUPPORTED -2   /* shape/dtype combination outside the supported set */
 #define MOE_ERR_WORKSPACE   -3   /* workspace smaller than moe_workspace_size() */
 #define MOE_ERR_HIP         -4   /* a HIP launch failed; moe_strerror() has the HIP text */
+#define MOE_ERR_SCRATCH     -5   /* moe_forward_noalloc: the config needs more scratch than
+                                    MOE_NOALLOC_SCRATCH_BYTES */
 
 /* Element types. */
 typedef enum {
@@ -231,6 +233,25 @@ int moe_forward_timed(const moe_config* cfg, const void* x, const moe_weights* w
 int moe_forward_residual(const moe_config* cfg, const void* x, const void* norm_weight,
                          float norm_eps, const moe_weights* w, void* x_out, int32_t* topk_ids_out,
                          float* topk_w_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_forward for callers that cannot allocate device memory or pass a workspace:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, work and results as moe_forward (bit for bit), but the scratch is a
+ * fixed array of MOE_NOALLOC_SCRATCH_BYTES inside the library's device code, one copy
+ * per GPU, held from the first call on that GPU until the process ends; no call
+ * allocates or frees anything.  Enough for decode and small batches (moe_workspace_size
+ * <= 16 MiB: up to ~256 tokens of the Ling-shaped layer); larger configs return
+ * MOE_ERR_SCRATCH before enqueuing anything.  Every call on one GPU shares that GPU's
+ * array: calls whose work overlaps on the device (other host threads, or other streams
+ * not ordered with this one) RACE and must not be issued; calls on one stream, or on
+ * streams ordered by events, are safe.  Nothing in the array needs to start at zero
+ * (moe_forward ignores its workspace's contents on entry).  The first call on a device
+ * looks the array's device address up (hipGetSymbolAddress) with that device current.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (16u << 20)
+int moe_forward_noalloc(const moe_config* cfg, const void* x, const moe_weights* w, void* y,
+                        int32_t* topk_ids_out, float* topk_w_out, hipStream_t stream);
 
 /*
  * Where a call leaves inspectable intermediate results in the workspace, for tests

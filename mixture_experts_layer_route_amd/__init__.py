@@ -39,7 +39,8 @@ class MoeWeights(ctypes.Structure):
 
 ENTRY_POINTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn",
                 "moe_combine", "moe_forward", "moe_forward_timed", "moe_forward_residual",
-                "moe_workspace_slot", "moe_strerror")
+                "moe_workspace_slot", "moe_forward_noalloc", "moe_strerror")
+NOALLOC_SCRATCH_BYTES = 16 << 20   # MOE_NOALLOC_SCRATCH_BYTES
 WS_LOGITS, WS_ACT_CODES, WS_ACT_SCALES, WS_NORM_ROWS = 0, 1, 2, 3   # MOE_WS_* slots
 TIMED_EVENTS = 4   # MOE_TIMED_EVENTS: start/stop of the gate/up kernel, start/stop of the down kernel
 
@@ -68,6 +69,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_forward_timed": [cfgp, P, wp, P, P, P, P, SZ, P, P],
         "moe_forward_residual": [cfgp, P, P, ctypes.c_float, wp, P, P, P, P, SZ, P],
         "moe_workspace_slot": [cfgp, ctypes.c_int, ctypes.POINTER(SZ), ctypes.POINTER(SZ)],
+        "moe_forward_noalloc": [cfgp, P, wp, P, P, P, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -180,6 +182,20 @@ def forward(cfg, x, weights: dict, ws, y: Optional[torch.Tensor] = None,
         wst = weights_struct(weights)
     _check(load_library().moe_forward(ctypes.byref(cfg), _ptr(x), ctypes.byref(wst), _ptr(y),
                                       _ptr(ids), _ptr(wts), _ptr(ws), ws.numel(), _stream()))
+    return y
+
+
+def forward_noalloc(cfg, x, weights: dict, y: Optional[torch.Tensor] = None,
+                    ids: Optional[torch.Tensor] = None, wts: Optional[torch.Tensor] = None,
+                    wst: Optional[MoeWeights] = None):
+    """The whole layer on the library's own fixed scratch (no workspace argument, no
+    allocation inside the call).  Returns y (and writes ids / wts when given)."""
+    if y is None:
+        y = torch.empty((cfg.num_tokens, cfg.hidden), dtype=x.dtype, device=x.device)
+    if wst is None:
+        wst = weights_struct(weights)
+    _check(load_library().moe_forward_noalloc(ctypes.byref(cfg), _ptr(x), ctypes.byref(wst),
+                                              _ptr(y), _ptr(ids), _ptr(wts), _stream()))
     return y
 
 

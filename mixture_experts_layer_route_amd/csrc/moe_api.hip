@@ -5,10 +5,38 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "moe_internal.h"
 
+// Scratch of moe_forward_noalloc: a fixed array in device memory, one copy per GPU,
+// held until the process ends.  In host code `scratch` is only a stand-in for the
+// symbol; its device address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
 namespace moe {
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch` (looked up once per device).
+static int noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return record_hip_error(err);
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return record_hip_error(err);
+    if (!ptr) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
 
 static thread_local char g_hip_error[256] = "no HIP error recorded";
 
@@ -321,6 +349,19 @@ int moe_forward_timed(const moe_config* cfg, const void* x, const moe_weights* w
   return forward_impl(cfg, x, w, y, topk_ids_out, topk_w_out, ws, ws_bytes, stream, kernel_events);
 }
 
+int moe_forward_noalloc(const moe_config* cfg, const void* x, const moe_weights* w, void* y,
+                        int32_t* topk_ids_out, float* topk_w_out, hipStream_t stream) {
+  Plan p;
+  MOE_TRY(make_plan(cfg, &p));
+  if (!x || !y || !w || !w->w_router) return MOE_ERR_ARG;
+  MOE_TRY(check_experts(p, w));
+  if (p.total > size_t(MOE_NOALLOC_SCRATCH_BYTES)) return MOE_ERR_SCRATCH;
+  void* ws = nullptr;
+  MOE_TRY(noalloc_scratch(&ws));
+  return forward_impl(cfg, x, w, y, topk_ids_out, topk_w_out, ws, MOE_NOALLOC_SCRATCH_BYTES,
+                      stream, nullptr);
+}
+
 int moe_forward_residual(const moe_config* cfg, const void* x, const void* norm_weight,
                          float norm_eps, const moe_weights* w, void* x_out, int32_t* topk_ids_out,
                          float* topk_w_out, void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -336,6 +377,8 @@ const char* moe_strerror(int status) {
     case MOE_ERR_UNSUPPORTED: return "unsupported configuration (shape or dtype combination)";
     case MOE_ERR_WORKSPACE: return "workspace smaller than moe_workspace_size()";
     case MOE_ERR_HIP: return g_hip_error;
+    case MOE_ERR_SCRATCH:
+      return "config needs more scratch than moe_forward_noalloc holds (MOE_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

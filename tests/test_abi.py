@@ -169,3 +169,24 @@ def test_workspace_slots_lie_inside_the_workspace(lib):
     n = ctypes.c_size_t(0)
     assert lib.moe_workspace_slot(ctypes.byref(_cfg()), 7, ctypes.byref(n), ctypes.byref(n)) == -1
     assert lib.moe_workspace_slot(ctypes.byref(_cfg()), 0, None, ctypes.byref(n)) == -1
+
+
+def test_forward_noalloc_rejects_before_any_device_work(lib):
+    """Validation and the scratch limit are decided on the host, before the first HIP call."""
+    fake = ctypes.c_void_p(1 << 40)
+    w = moe.MoeWeights()
+    cfg = _cfg(T=16)
+    assert lib.moe_forward_noalloc(ctypes.byref(cfg), None, ctypes.byref(w), fake, None, None,
+                                   None) == -1
+    w.w_router = w.w_gate = w.w_up = w.w_down = 1 << 40
+    assert lib.moe_forward_noalloc(ctypes.byref(cfg), fake, ctypes.byref(w), None, None, None,
+                                   None) == -1
+    big = _cfg(T=8192)
+    assert moe.workspace_size(big) > moe.NOALLOC_SCRATCH_BYTES
+    assert lib.moe_forward_noalloc(ctypes.byref(big), fake, ctypes.byref(w), fake, None, None,
+                                   None) == -5
+    assert b"MOE_NOALLOC_SCRATCH_BYTES" in lib.moe_strerror(-5)
+    assert moe.workspace_size(_cfg(T=256)) <= moe.NOALLOC_SCRATCH_BYTES
+    txt = open(os.path.join(ROOT, "include", "moe.h")).read()
+    assert re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \(16u << 20\)", txt)
+    assert moe.NOALLOC_SCRATCH_BYTES == 16 << 20
