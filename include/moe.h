@@ -254,6 +254,52 @@ int moe_forward_noalloc(const moe_config* cfg, const void* x, const moe_weights*
                         int32_t* topk_ids_out, float* topk_w_out, hipStream_t stream);
 
 /*
+ * Expert paging: the routed experts of a layer live in host memory and an HBM arena of
+ * N slots holds the ones recent calls routed to (the HelloSun/ling30tiny model card:
+ * introduction, where inactive experts stay off the compute device and a bounded
+ * arena holds the selected ones; its RAM-limit table reports the arena in slots and a
+ * hot rate).  Every decision is taken on the device after the routing, so no call
+ * waits for the host.  Policy: per call the distinct routed experts are looked up; a
+ * resident one is a hit; misses are copied from the store into the slots this call
+ * does not need, least recently used first (a slot's stamp is the number of the last
+ * call that used it; never-used slots first), ties to the lower slot, misses taken in
+ * ascending expert order.  Shared experts are not paged (every token uses them).
+ * Supported: fp32 and bf16 experts; k <= N <= E and N >= min(E, T*k) (every expert one
+ * call needs fits), else MOE_ERR_UNSUPPORTED.
+ *
+ * State: device memory of moe_pager_state_layout() bytes, owned by the caller, one per
+ * (layer, arena); moe_pager_reset() initialises it (a kernel on `stream`: empty arena,
+ * zero counters).  Layout, at the offsets the layout call writes (offsets[0..3]):
+ *   int64 counters[8]: [0] calls, [1] routed (token, slot) references, [2] lookups
+ *     (distinct experts needed, summed over calls), [3] hits, [4] misses, [5] bytes
+ *     copied from the store; hot rate = hits / lookups;
+ *   int32 key_slot[E] (slot of each expert or -1), int32 slot_key[N] (expert in each
+ *   slot or -1), int64 stamp[N].
+ * Calls that share a state must be ordered on the device (one stream).
+ */
+int moe_pager_state_layout(const moe_config* cfg, int32_t num_slots, size_t* offsets,
+                           size_t* bytes);
+int moe_pager_reset(const moe_config* cfg, int32_t num_slots, void* state, hipStream_t stream);
+/* Workspace bytes of moe_forward_paged for `cfg` and `num_slots` (host only). */
+int moe_paged_workspace_size(const moe_config* cfg, int32_t num_slots, size_t* bytes);
+/*
+ * moe_forward with the routed experts paged.  host_experts: w_gate, w_up [E, I, H] and
+ * w_down [E, H, I] in pinned host memory (hipHostMalloc or a pinned torch tensor; device
+ * memory is accepted too), read by the GPU over the host link; its other fields are
+ * ignored.  resident: device memory - w_router, router_bias, the arena's w_gate, w_up
+ * [N, I, H] and w_down [N, H, I], and the shared experts sh_* (S > 0).  The call routes
+ * (moe_route's semantics), updates the arena on the device (k_pager_plan, then the copy
+ * of the misses), then runs the permutation, experts and combine of moe_permute /
+ * moe_expert_ffn / moe_combine over the slots: y equals, bit for bit, that sequence of
+ * calls on the resident layer.  Errors as moe_forward; MOE_ERR_ARG also when HIP does
+ * not know a store pointer (not pinned).
+ */
+int moe_forward_paged(const moe_config* cfg, const void* x, const moe_weights* host_experts,
+                      const moe_weights* resident, int32_t num_slots, void* state, void* y,
+                      int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                      hipStream_t stream);
+
+/*
  * Where a call leaves inspectable intermediate results in the workspace, for tests
  * and debugging (host only, no device work).  After moe_forward / moe_forward_timed /
  * moe_forward_residual (and moe_route with logits == NULL) the workspace holds:

@@ -39,7 +39,8 @@ class MoeWeights(ctypes.Structure):
 
 ENTRY_POINTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn",
                 "moe_combine", "moe_forward", "moe_forward_timed", "moe_forward_residual",
-                "moe_workspace_slot", "moe_forward_noalloc", "moe_strerror")
+                "moe_workspace_slot", "moe_forward_noalloc", "moe_pager_state_layout",
+                "moe_pager_reset", "moe_paged_workspace_size", "moe_forward_paged", "moe_strerror")
 NOALLOC_SCRATCH_BYTES = 16 << 20   # MOE_NOALLOC_SCRATCH_BYTES
 WS_LOGITS, WS_ACT_CODES, WS_ACT_SCALES, WS_NORM_ROWS = 0, 1, 2, 3   # MOE_WS_* slots
 TIMED_EVENTS = 4   # MOE_TIMED_EVENTS: start/stop of the gate/up kernel, start/stop of the down kernel
@@ -70,6 +71,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_forward_residual": [cfgp, P, P, ctypes.c_float, wp, P, P, P, P, SZ, P],
         "moe_workspace_slot": [cfgp, ctypes.c_int, ctypes.POINTER(SZ), ctypes.POINTER(SZ)],
         "moe_forward_noalloc": [cfgp, P, wp, P, P, P, P],
+        "moe_pager_state_layout": [cfgp, ctypes.c_int32, ctypes.POINTER(SZ), ctypes.POINTER(SZ)],
+        "moe_pager_reset": [cfgp, ctypes.c_int32, P, P],
+        "moe_paged_workspace_size": [cfgp, ctypes.c_int32, ctypes.POINTER(SZ)],
+        "moe_forward_paged": [cfgp, P, wp, wp, ctypes.c_int32, P, P, P, P, P, SZ, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -197,6 +202,71 @@ def forward_noalloc(cfg, x, weights: dict, y: Optional[torch.Tensor] = None,
     _check(load_library().moe_forward_noalloc(ctypes.byref(cfg), _ptr(x), ctypes.byref(wst),
                                               _ptr(y), _ptr(ids), _ptr(wts), _stream()))
     return y
+
+
+PAGER_COUNTERS = ("calls", "refs", "lookups", "hits", "misses", "bytes_copied")
+
+
+def pager_state_layout(cfg, num_slots: int):
+    """(offsets of counters, key_slot, slot_key, stamp; total bytes) of a pager state."""
+    offs = (ctypes.c_size_t * 4)()
+    n = ctypes.c_size_t(0)
+    _check(load_library().moe_pager_state_layout(ctypes.byref(cfg), num_slots, offs,
+                                                 ctypes.byref(n)))
+    return tuple(int(v) for v in offs), int(n.value)
+
+
+def alloc_pager_state(cfg, num_slots: int, device="cuda") -> torch.Tensor:
+    """A pager state, initialised (empty arena, zero counters) on the current stream."""
+    _, n = pager_state_layout(cfg, num_slots)
+    state = torch.empty(n, dtype=torch.uint8, device=device)
+    _check(load_library().moe_pager_reset(ctypes.byref(cfg), num_slots, _ptr(state), _stream()))
+    return state
+
+
+def pager_tables(cfg, num_slots: int, state: torch.Tensor) -> dict:
+    """Counters and residency tables of a pager state, copied to the host."""
+    (oc, ok, osl, ost), _ = pager_state_layout(cfg, num_slots)
+    raw = state.cpu()
+    E = cfg.num_experts
+    c = raw[oc:oc + 64].view(torch.int64).tolist()
+    out = dict(zip(PAGER_COUNTERS, c))
+    out["key_slot"] = raw[ok:ok + 4 * E].view(torch.int32).numpy().copy()
+    out["slot_key"] = raw[osl:osl + 4 * num_slots].view(torch.int32).numpy().copy()
+    out["stamp"] = raw[ost:ost + 8 * num_slots].view(torch.int64).numpy().copy()
+    return out
+
+
+def paged_workspace(cfg, num_slots: int, device="cuda") -> torch.Tensor:
+    n = ctypes.c_size_t(0)
+    _check(load_library().moe_paged_workspace_size(ctypes.byref(cfg), num_slots, ctypes.byref(n)))
+    return torch.empty(max(int(n.value), 256), dtype=torch.uint8, device=device)
+
+
+def forward_paged(cfg, x, host_experts: MoeWeights, resident: MoeWeights, num_slots: int,
+                  state, ws, y: Optional[torch.Tensor] = None, ids: Optional[torch.Tensor] = None,
+                  wts: Optional[torch.Tensor] = None):
+    """The layer with its routed experts paged from pinned host memory into an arena of
+    `num_slots` slots (device-side decisions).  `host_experts` holds host pointers
+    (pinned tensors: use weights_struct_host), `resident` device pointers."""
+    if y is None:
+        y = torch.empty((cfg.num_tokens, cfg.hidden), dtype=x.dtype, device=x.device)
+    _check(load_library().moe_forward_paged(ctypes.byref(cfg), _ptr(x), ctypes.byref(host_experts),
+                                            ctypes.byref(resident), num_slots, _ptr(state),
+                                            _ptr(y), _ptr(ids), _ptr(wts), _ptr(ws), ws.numel(),
+                                            _stream()))
+    return y
+
+
+def weights_struct_host(w: dict) -> MoeWeights:
+    """Weight struct of pinned host tensors (the paged layer's expert store)."""
+    def hp(t):
+        if t is None:
+            return None
+        if not (t.is_pinned() and t.is_contiguous()):
+            raise ValueError("the expert store must be contiguous pinned host tensors")
+        return t.data_ptr()
+    return MoeWeights(*[hp(w.get(n)) for n, _ in MoeWeights._fields_])
 
 
 def forward_residual(cfg, x, norm_weight, weights: dict, ws, x_out: Optional[torch.Tensor] = None,

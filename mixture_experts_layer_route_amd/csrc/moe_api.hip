@@ -176,6 +176,81 @@ static int run_experts(const Plan& p, const void* x, const int32_t* off, const i
   return launch_down_mfma(p, hq, off, tiles, meta, w, row_w, y_perm32, y_perm16, shq, st);
 }
 
+// Paged layer: the routing plan (original experts) and the slot-space plan (the
+// arena's N slots as the experts of the permutation and the expert kernels).
+struct PagedPlan {
+  Plan route, slots;
+  int N;
+  size_t o_slots, o_ids_slot, o_copies, o_yp, total;
+  int64_t mat_bytes[3];
+};
+
+static int make_paged_plan(const moe_config* c, int32_t num_slots, PagedPlan* pp) {
+  PagedPlan q{};
+  MOE_TRY(make_plan(c, &q.route));
+  const Plan& p = q.route;
+  if (p.wt != MOE_F32 && p.wt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  // every expert one call can need fits, and no more slots than experts
+  if (num_slots < std::min<int64_t>(p.E, p.Rk) || num_slots > p.E) return MOE_ERR_UNSUPPORTED;
+  moe_config cs = *c;
+  cs.num_experts = num_slots;
+  cs.num_groups = 1;
+  cs.topk_groups = 1;
+  MOE_TRY(make_plan(&cs, &q.slots));
+  q.N = num_slots;
+  size_t o = align256(p.total);
+  q.o_slots = o;
+  o = align256(o + q.slots.total);
+  q.o_ids_slot = o;
+  o = align256(o + size_t(p.Rk) * 4);
+  q.o_copies = o;
+  o = align256(o + size_t(1 + 2 * std::min<int64_t>(num_slots, p.Rk)) * 4);
+  q.o_yp = o;
+  o = align256(o + size_t(p.R) * p.H * 4);
+  q.total = o;
+  const int64_t b = p.wt == MOE_F32 ? 4 : 2;
+  q.mat_bytes[0] = q.mat_bytes[1] = q.mat_bytes[2] = int64_t(p.I) * p.H * b;
+  *pp = q;
+  return MOE_OK;
+}
+
+// Device address under which a kernel reads `p`: pinned host memory (hipHostMalloc,
+// torch pin_memory) or device memory; MOE_ERR_ARG for memory HIP does not know.  For
+// host memory the pointer attributes and hipHostGetDevicePointer must agree.
+static int device_view(const void* p, const void** out) {
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess || !a.devicePointer) {
+    (void)hipGetLastError();   // the failed query must not surface as a launch error later
+    return MOE_ERR_ARG;
+  }
+  if (a.type == hipMemoryTypeDevice) {
+    *out = p;
+    return MOE_OK;
+  }
+  if (a.type != hipMemoryTypeHost) return MOE_ERR_ARG;
+  const char* hp = static_cast<const char*>(a.hostPointer);
+  const void* v = static_cast<const char*>(a.devicePointer) + (hp ? static_cast<const char*>(p) - hp : 0);
+  void* d = nullptr;
+  if (hipHostGetDevicePointer(&d, const_cast<void*>(p), 0) != hipSuccess || d != v) {
+    (void)hipGetLastError();
+    return MOE_ERR_ARG;
+  }
+  *out = v;
+  return MOE_OK;
+}
+
+// device_view of a whole array of `bytes`: its first and last byte must both be known
+// to HIP and map to one contiguous device range.
+static int device_range(const void* p, int64_t bytes, const void** out) {
+  const void* first = nullptr;
+  const void* last = nullptr;
+  MOE_TRY(device_view(p, &first));
+  MOE_TRY(device_view(static_cast<const char*>(p) + bytes - 1, &last));
+  if (static_cast<const char*>(last) != static_cast<const char*>(first) + bytes - 1) return MOE_ERR_ARG;
+  *out = first;
+  return MOE_OK;
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -360,6 +435,84 @@ int moe_forward_noalloc(const moe_config* cfg, const void* x, const moe_weights*
   MOE_TRY(noalloc_scratch(&ws));
   return forward_impl(cfg, x, w, y, topk_ids_out, topk_w_out, ws, MOE_NOALLOC_SCRATCH_BYTES,
                       stream, nullptr);
+}
+
+int moe_pager_state_layout(const moe_config* cfg, int32_t num_slots, size_t* offsets,
+                           size_t* bytes) {
+  if (!bytes) return MOE_ERR_ARG;
+  PagedPlan pp;
+  MOE_TRY(make_paged_plan(cfg, num_slots, &pp));
+  const PagerLayout L = pager_layout(pp.route.E, num_slots);
+  if (offsets) {
+    offsets[0] = L.o_counters;
+    offsets[1] = L.o_key_slot;
+    offsets[2] = L.o_slot_key;
+    offsets[3] = L.o_stamp;
+  }
+  *bytes = L.total;
+  return MOE_OK;
+}
+
+int moe_pager_reset(const moe_config* cfg, int32_t num_slots, void* state, hipStream_t stream) {
+  PagedPlan pp;
+  MOE_TRY(make_paged_plan(cfg, num_slots, &pp));
+  if (!state) return MOE_ERR_ARG;
+  return launch_pager_reset(pp.route.E, num_slots, state, stream);
+}
+
+int moe_paged_workspace_size(const moe_config* cfg, int32_t num_slots, size_t* bytes) {
+  if (!bytes) return MOE_ERR_ARG;
+  PagedPlan pp;
+  MOE_TRY(make_paged_plan(cfg, num_slots, &pp));
+  *bytes = pp.total;
+  return MOE_OK;
+}
+
+int moe_forward_paged(const moe_config* cfg, const void* x, const moe_weights* host_experts,
+                      const moe_weights* resident, int32_t num_slots, void* state, void* y,
+                      int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
+  PagedPlan pp;
+  MOE_TRY(make_paged_plan(cfg, num_slots, &pp));
+  const Plan& p = pp.route;
+  const Plan& q = pp.slots;
+  if (!x || !y || !state || !host_experts || !resident || !resident->w_router) return MOE_ERR_ARG;
+  if (!host_experts->w_gate || !host_experts->w_up || !host_experts->w_down) return MOE_ERR_ARG;
+  MOE_TRY(check_experts(q, resident));
+  MOE_TRY(check_ws(p, ws, ws_bytes));
+  if (ws_bytes < pp.total) return MOE_ERR_WORKSPACE;
+  PagerCopyArgs ca{};
+  MOE_TRY(device_range(host_experts->w_gate, p.E * pp.mat_bytes[0], &ca.src[0]));
+  MOE_TRY(device_range(host_experts->w_up, p.E * pp.mat_bytes[1], &ca.src[1]));
+  MOE_TRY(device_range(host_experts->w_down, p.E * pp.mat_bytes[2], &ca.src[2]));
+  ca.dst[0] = const_cast<void*>(resident->w_gate);
+  ca.dst[1] = const_cast<void*>(resident->w_up);
+  ca.dst[2] = const_cast<void*>(resident->w_down);
+  for (int j = 0; j < 3; ++j) ca.chunks[j] = pp.mat_bytes[j] / 16;
+
+  // routing over the layer's experts
+  float* logits = at<float>(ws, p.o_logits);
+  int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, p.o_ids);
+  float* wts = topk_w_out ? topk_w_out : at<float>(ws, p.o_w);
+  MOE_TRY(launch_logits(p, x, resident->w_router, resident->router_bias, logits, stream));
+  MOE_TRY(launch_select(p, logits, ids, wts, nullptr, stream));
+  // residency: plan on the device, copy the misses into their slots
+  int32_t* ids_slot = at<int32_t>(ws, pp.o_ids_slot);
+  int32_t* copies = at<int32_t>(ws, pp.o_copies);
+  MOE_TRY(launch_pager_plan(ids, int(p.Rk), p.E, pp.N, 3 * pp.mat_bytes[0], state, ids_slot,
+                            copies, stream));
+  MOE_TRY(launch_pager_copy(copies, ca, int(std::min<int64_t>(pp.N, p.Rk)), stream));
+  // the rest of the layer over the slots: permutation, experts, combine
+  void* wq = static_cast<char*>(ws) + pp.o_slots;
+  int32_t* off = at<int32_t>(wq, q.o_off);
+  int32_t* rowtok = at<int32_t>(wq, q.o_rowtok);
+  int32_t* inv = at<int32_t>(wq, q.o_inv);
+  MOE_TRY(launch_permute(q, ids_slot, nullptr, at<int32_t>(wq, q.o_blk), off,
+                         at<int32_t>(wq, q.o_active), at<int32_t>(wq, q.o_meta),
+                         at<int2>(wq, q.o_tiles), rowtok, inv, nullptr, q.bm, stream));
+  float* yp = at<float>(ws, pp.o_yp);
+  MOE_TRY(run_experts(q, x, off, rowtok, resident, wq, yp, nullptr, nullptr, stream));
+  return launch_combine(q, yp, off, inv, wts, nullptr, y, stream);
 }
 
 int moe_forward_residual(const moe_config* cfg, const void* x, const void* norm_weight,

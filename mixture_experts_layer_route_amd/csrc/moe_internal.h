@@ -123,4 +123,20 @@ int launch_combine(const Plan& p, const float* y_perm, const int32_t* offsets, c
 int launch_combine_preweighted(const Plan& p, const bf16_t* y_perm, const int32_t* offsets,
                                const int32_t* inv, const void* res, void* y, hipStream_t st);
 
+// Expert paging (pager.hip): device state layout, planner and copy kernels.
+struct PagerLayout {
+  size_t o_counters, o_key_slot, o_slot_key, o_stamp, total;
+};
+PagerLayout pager_layout(int E, int N);
+struct PagerCopyArgs {
+  const void* src[3];   // device views of the store's gate, up, down arrays [E, ...]
+  void* dst[3];         // arena arrays [N, ...]
+  int64_t chunks[3];    // 16-byte chunks per expert matrix
+};
+int launch_pager_reset(int E, int N, void* state, hipStream_t st);
+int launch_pager_plan(const int32_t* ids, int nslot, int E, int N, int64_t expert_bytes,
+                      void* state, int32_t* ids_slot, int32_t* copies, hipStream_t st);
+int launch_pager_copy(const int32_t* copies, const PagerCopyArgs& a, int max_copies,
+                      hipStream_t st);
+
 }  // namespace moe
