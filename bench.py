@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode",
                     choices=["tiny", "decode", "prefill", "fp8", "inkling", "decode_nvfp4",
-                             "prefill_nvfp4", "decode_stack"])
+                             "prefill_nvfp4", "decode_stack", "paged"])
     ap.add_argument("--sets", type=int, default=0, help="weight copies rotated per step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="host time budget for the oracle baseline (0 = skip)")
@@ -451,6 +451,100 @@ def measure(workload, nsets, K, W, event_every):
     return res, shape, cpu
 
 
+HOST_LINK_PEAK_GBS = 64.0        # PCIe 5.0 x16 between the MI355X and its host, one direction
+
+
+def run_paged(args):
+    """Single-stream decode through the 23 MoE blocks of the stack with every block's
+    routed experts in pinned host memory and an HBM arena of N slots per block (the
+    HelloSun/ling30tiny RAM-limit table measured on one MI355X): tokens/s, hot rate,
+    MiB copied from the host per token and the host-link rate, per arena size."""
+    import torch
+    import mixture_experts_layer_route_amd as moe
+    import synth
+
+    base = synth.WORKLOADS["decode"]
+    shape = synth.LayerShape("paged", T=1, H=base.H, I=base.I, E=base.E, G=base.G, Gk=base.Gk,
+                             k=base.k, S=0, act="bf16", wt="bf16", x_dist="rms", bias_std=1.0,
+                             seed=8)
+    L = synth.STACK_BLOCKS
+    log(f"workload {shape}; {L} blocks, experts in pinned host memory")
+    cpu = synth.make_layer(shape)
+    mats = ("w_gate", "w_up", "w_down")
+    blocks = []
+    for l in range(L):
+        store = {k: torch.empty(cpu[k].shape, dtype=cpu[k].dtype, pin_memory=True).copy_(cpu[k])
+                 for k in mats}                                    # one store per block
+        router = synth.make_router(shape.E, shape.H, shape.act, 10_000 + l).cuda()
+        bias = torch.from_numpy(np.random.default_rng(30_000 + l).standard_normal(
+            shape.E, dtype=np.float32)).cuda()
+        blocks.append((store, moe.weights_struct_host(store), router, bias))
+    cfg = moe.make_config(shape.T, shape.H, shape.I, shape.E, shape.G, shape.Gk, shape.k,
+                          shape.S, shape.act, shape.wt)
+    rng = np.random.default_rng(9)
+    pool = torch.from_numpy(rng.standard_normal((256, shape.H), dtype=np.float32))
+    pool = (pool / pool.pow(2).mean(dim=1, keepdim=True).sqrt()).to(torch.bfloat16).cuda()
+    expert_bytes = 3 * shape.I * shape.H * 2
+    K, W = min(args.steps, 64), min(args.warmup, 32)
+    sweep = []
+    for N in (8, 16, 32, 64, 128):
+        arenas, states = [], []
+        for l in range(L):
+            ar = {"w_gate": torch.empty((N, shape.I, shape.H), dtype=torch.bfloat16, device="cuda"),
+                  "w_up": torch.empty((N, shape.I, shape.H), dtype=torch.bfloat16, device="cuda"),
+                  "w_down": torch.empty((N, shape.H, shape.I), dtype=torch.bfloat16, device="cuda"),
+                  "w_router": blocks[l][2], "router_bias": blocks[l][3]}
+            arenas.append((ar, moe.weights_struct(ar)))
+            states.append(moe.alloc_pager_state(cfg, N))
+        ws = moe.paged_workspace(cfg, N)
+        y = torch.empty((1, shape.H), dtype=torch.bfloat16, device="cuda")
+
+        def token(i):
+            for l in range(L):
+                x = pool[(i * L + l) % pool.shape[0]].view(1, -1)
+                moe.forward_paged(cfg, x, blocks[l][1], arenas[l][1], N, states[l], ws, y=y)
+
+        for i in range(W):
+            token(i)
+        torch.cuda.synchronize()
+        before = [moe.pager_tables(cfg, N, st) for st in states]
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(W, W + K):
+            token(i)
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / K
+        after = [moe.pager_tables(cfg, N, st) for st in states]
+        d = {c: sum(a[c] - b[c] for a, b in zip(after, before)) for c in moe.PAGER_COUNTERS}
+        rec = {"slots_per_block": N, "arena_GiB": round(L * N * expert_bytes / 2 ** 30, 3),
+               "tokens_per_s": round(1e3 / ms, 2), "ms_per_token": round(ms, 4),
+               "hot_rate": round(d["hits"] / max(1, d["lookups"]), 4),
+               "MiB_per_token_from_host": round(d["bytes_copied"] / K / 2 ** 20, 2),
+               "host_GB_per_s": round(d["bytes_copied"] / K / (ms * 1e-3) / 1e9, 2)}
+        log(json.dumps(rec))
+        sweep.append(rec)
+        del arenas, states, ws
+        torch.cuda.empty_cache()
+    mid = next(r for r in sweep if r["slots_per_block"] == 32)
+    link = max(r["host_GB_per_s"] for r in sweep)
+    res = {
+        "metric": METRIC, "value": mid["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": K, "warmup": W, "ms_per_step": mid["ms_per_token"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "paged", "blocks": L, "T": 1, "H": shape.H, "I": shape.I,
+                   "E": shape.E, "G": shape.G, "Gk": shape.Gk, "k": shape.k,
+                   "router_bias_std": shape.bias_std, "slots_per_block": 32,
+                   "store": "pinned host memory, one copy of the block's experts per block"},
+        "arena_sweep": sweep,
+        "roofline": {"bound": "host_link", "achieved": link, "peak": HOST_LINK_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(link / HOST_LINK_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "expert copies host -> HBM (k_pager_copy), best arena size",
+                     "per_launch": f"misses x {expert_bytes} B per expert"},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -462,6 +556,9 @@ def main():
         return
     if args.workload == "decode_stack":
         run_stack(args)
+        return
+    if args.workload == "paged":
+        run_paged(args)
         return
     import torch
     import mixture_experts_layer_route_amd as moe
