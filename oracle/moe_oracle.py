@@ -42,6 +42,15 @@ plainest the rest supports):
       elements along the input dimension and one fp32 scale per expert matrix:
       weight = e2m1(code) * e4m3(block scale) * matrix scale.  Activations stay
       in their own type (no activation quantisation).
+  R19 MXFP4 experts (the OCP Microscaling format gfx950's matrix cores take natively; the
+      pages name 4-bit experts - NVFP4 in TensorFold #1247's list "What it does not
+      cover", ROCmFP4 on the graysoft page - and give no layout): FP4 E2M1 codes, two per
+      byte with element 2i in the low nibble, one E8M0 scale per 32 consecutive inputs:
+      weight = e2m1(code) * 2^(scale - 127).
+  R20 With MXFP4 experts the activations (x, and h before the down projection) are
+      quantised per row per 32 along K to MXFP8: E8M0 shared exponent
+      X = floor(log2(amax)) - 8, E4M3 elements RNE(v / 2^X) saturating at +-448; an
+      all-zero block gets X = -127.  Decisions in fp32, as the kernels take them.
   R16 The decoder-layer step around the MoE block (the config paragraph of
       TensorFold #1247: 24 layers, a dense layer 0, so 23 MoE layers) is
       x_out = x + MoE(RMSNorm(x)) with RMSNorm(x) = x / sqrt(mean(x^2) + eps) * gamma
@@ -285,6 +294,55 @@ def dequant_nvfp4(packed, block_scales, matrix_scale) -> np.ndarray:
     return vals * sc * float(matrix_scale)
 
 
+# --------------------------------------------------------------------------- MX formats (R19, R20)
+MX_BLOCK = 32
+
+
+def e8m0_values() -> np.ndarray:
+    """Value of each of the 256 E8M0 scale codes of the OCP Microscaling spec: 2^(c - 127),
+    code 255 is NaN."""
+    vals = np.ldexp(1.0, np.arange(256) - 127).astype(np.float64)
+    vals[255] = np.nan
+    return vals
+
+
+def dequant_mxfp4(packed, scales) -> np.ndarray:
+    """[rows, K/2] packed E2M1 codes (element 2i in the low nibble) and [rows, K/32] E8M0
+    scale codes -> float64 [rows, K] weights (reading R19: value = e2m1 * 2^(s - 127))."""
+    vals = e2m1_values()[nvfp4_unpack(packed)]
+    sc = np.repeat(e8m0_values()[np.asarray(scales, dtype=np.uint8)], MX_BLOCK, axis=-1)
+    return vals * sc
+
+
+def quantize_mxfp8_codes(v):
+    """Activation quantisation of reading R20, per row per 32 along the last axis, as
+    stored: (E4M3 codes uint8 [rows, cols], E8M0 scale codes uint8 [rows, cols/32]).
+
+    The OCP Microscaling conversion with E4M3 elements: shared exponent
+    X = floor(log2(amax)) - 8 (8 = exponent of E4M3's largest normal, 448 = 1.75 * 2^8),
+    element = E4M3 round-to-nearest-even of v / 2^X, saturating at +-448 (values from
+    448 up to 512 can occur and clip); an all-zero block gets X = -127 and zero codes.
+    Decisions in fp32: the values are first held in fp32, where division by 2^X is exact."""
+    v32 = np.asarray(v, dtype=np.float64).astype(np.float32)
+    rows, cols = v32.shape
+    blocks = v32.reshape(rows, cols // MX_BLOCK, MX_BLOCK)
+    amax = np.abs(blocks).max(axis=2).astype(np.float64)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))          # amax = m * 2^ex, 0.5 <= m < 1
+    X = np.where(amax > 0, ex - 1 - 8, -127)
+    X = np.clip(X, -127, 127)
+    q = blocks.astype(np.float64) / np.ldexp(1.0, X)[:, :, None]
+    codes = e4m3_encode(q.astype(np.float32)).reshape(rows, cols)
+    return codes, (X + 127).astype(np.uint8)
+
+
+def quantize_mxfp8(v) -> np.ndarray:
+    """Reading R20's activation quantisation, dequantised to float64 (code value * 2^X)."""
+    codes, sc = quantize_mxfp8_codes(v)
+    rows, cols = codes.shape
+    vals = e4m3_decode(codes).reshape(rows, cols // MX_BLOCK, MX_BLOCK)
+    return (vals * e8m0_values()[sc][:, :, None]).reshape(rows, cols)
+
+
 # --------------------------------------------------------------------------- decoder step (R16)
 RMS_EPS = 1e-6
 
@@ -339,16 +397,20 @@ class Experts:
 
     def __init__(self, w_gate, w_up, w_down, s_gate=None, s_up=None, s_down=None,
                  sh_gate=None, sh_up=None, sh_down=None, sh_s_gate=None, sh_s_up=None,
-                 sh_s_down=None, nv=None, sh_nv=None):
+                 sh_s_down=None, nv=None, sh_nv=None, mx=None, sh_mx=None):
         self.fp8 = s_gate is not None
-        self.routed = (w_gate, w_up, w_down, s_gate, s_up, s_down, nv)
-        self.shared = (sh_gate, sh_up, sh_down, sh_s_gate, sh_s_up, sh_s_down, sh_nv)
+        self.mx = mx is not None
+        self.routed = (w_gate, w_up, w_down, s_gate, s_up, s_down, nv, mx)
+        self.shared = (sh_gate, sh_up, sh_down, sh_s_gate, sh_s_up, sh_s_down, sh_nv, sh_mx)
         self.E = len(w_gate)
         self.S = 0 if sh_gate is None else len(sh_gate)
 
     @staticmethod
     def _decode(pack, e):
-        wg, wu, wd, sg, su, sd, nv = pack
+        wg, wu, wd, sg, su, sd, nv, mx = pack
+        if mx is not None:
+            bg, bu, bd = mx
+            return dequant_mxfp4(wg[e], bg[e]), dequant_mxfp4(wu[e], bu[e]), dequant_mxfp4(wd[e], bd[e])
         if nv is not None:
             bg, bu, bd, gg, gu, gd = nv
             return (dequant_nvfp4(wg[e], bg[e], gg[e]), dequant_nvfp4(wu[e], bu[e], gu[e]),
@@ -357,6 +419,11 @@ class Experts:
             return _f64(wg[e]), _f64(wu[e]), _f64(wd[e])
         return (dequant_blocks(wg[e], sg[e]), dequant_blocks(wu[e], su[e]),
                 dequant_blocks(wd[e], sd[e]))
+
+    @property
+    def quant(self):
+        """Activation quantisation of these experts: "mx" (R20), True (R9) or False."""
+        return "mx" if self.mx else self.fp8
 
     def expert(self, e: int):
         """(Wg [I,H], Wu [I,H], Wd [H,I]) of expert e; e >= E addresses shared expert e - E."""
@@ -375,19 +442,21 @@ def sigmoid(z) -> np.ndarray:
     return out
 
 
-def swiglu_expert(X, Wg, Wu, Wd, fp8: bool = False) -> np.ndarray:
+def swiglu_expert(X, Wg, Wu, Wd, fp8=False) -> np.ndarray:
     """One SwiGLU expert on rows X (reading R6; TensorFold #1247 config paragraph: no clamp).
 
     h = silu(X Wg^T) * (X Wu^T), silu(z) = z * sigmoid(z);  Y = h Wd^T.
-    With fp8 experts X and h are quantised per row per 128 first (reading R9)."""
+    With block-FP8 experts (fp8 True) X and h are quantised per row per 128 first
+    (reading R9); with MXFP4 experts (fp8 == "mx") per row per 32 to MXFP8 (reading R20)."""
     X = _f64(X)
+    quant = quantize_mxfp8 if fp8 == "mx" else quantize_act
     if fp8:
-        X = quantize_act(X)
+        X = quant(X)
     g = X @ Wg.T
     u = X @ Wu.T
     h = g * sigmoid(g) * u
     if fp8:
-        h = quantize_act(h)
+        h = quant(h)
     return h @ Wd.T
 
 
@@ -404,7 +473,7 @@ def expert_ffn(x, offsets, row_token, experts: Experts) -> np.ndarray:
         r0, r1 = int(offsets[e]), int(offsets[e + 1])
         if r1 > r0:
             Wg, Wu, Wd = experts.expert(e)
-            y_perm[r0:r1] = swiglu_expert(x[row_token[r0:r1]], Wg, Wu, Wd, experts.fp8)
+            y_perm[r0:r1] = swiglu_expert(x[row_token[r0:r1]], Wg, Wu, Wd, experts.quant)
     return y_perm
 
 
@@ -455,10 +524,10 @@ def forward_tokenmajor(x, experts: Experts, ids, w) -> np.ndarray:
     for t in range(T):
         for j in range(ids.shape[1]):
             Wg, Wu, Wd = experts.expert(int(ids[t, j]))
-            y[t] += w[t, j] * swiglu_expert(x[t:t + 1], Wg, Wu, Wd, experts.fp8)[0]
+            y[t] += w[t, j] * swiglu_expert(x[t:t + 1], Wg, Wu, Wd, experts.quant)[0]
         for s in range(experts.S):
             Wg, Wu, Wd = experts.expert(experts.E + s)
-            y[t] += swiglu_expert(x[t:t + 1], Wg, Wu, Wd, experts.fp8)[0]
+            y[t] += swiglu_expert(x[t:t + 1], Wg, Wu, Wd, experts.quant)[0]
     return y
 
 

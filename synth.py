@@ -17,6 +17,9 @@ Shapes and value distributions follow the five workloads of the layer:
   decode_nvfp4  the decode layer with NVFP4 experts (4-bit E2M1 codes, an E4M3
             scale per 16 inputs, an fp32 scale per expert matrix)
   prefill_nvfp4 the prefill layer (router bias included) with NVFP4 experts
+  decode_mxfp4, prefill_mxfp4  the decode and prefill layers with MXFP4 experts (4-bit
+            E2M1 codes, an E8M0 scale per 32 inputs); the layer quantises its
+            activations per 32 to MXFP8
   decode_stack  23 decode MoE blocks of a decoder step (x + MoE(RMSNorm(x)) each): the
             decode layer's experts copied per block, a router and a norm weight
             drawn per block (make_router, make_norm_weight)
@@ -33,7 +36,7 @@ Inkling architecture".  The intermediate size 512 and the hidden size
 Draw order (numpy PCG64, ``default_rng(seed)``), every tensor drawn in float32:
   x; router weight; router bias (prefill only); then for each expert
   e = 0..E+S-1: gate, up, down (for fp8 each tensor is followed by its
-  per-block scale factors u ~ U(0.5, 2); NVFP4 draws nothing extra).
+  per-block scale factors u ~ U(0.5, 2); NVFP4 and MXFP4 draw nothing extra).
 """
 from __future__ import annotations
 
@@ -43,7 +46,7 @@ from typing import Optional
 import numpy as np
 import torch
 
-F32, BF16, E4M3, NVFP4 = "f32", "bf16", "e4m3", "nvfp4"
+F32, BF16, E4M3, NVFP4, MXFP4 = "f32", "bf16", "e4m3", "nvfp4", "mxfp4"
 
 
 @dataclasses.dataclass(frozen=True)
@@ -85,6 +88,10 @@ WORKLOADS = {
                                S=0, act=BF16, wt=NVFP4, x_dist="rms", bias_std=0.0, seed=5),
     "prefill_nvfp4": LayerShape("prefill_nvfp4", T=8192, H=1536, I=512, E=128, G=8, Gk=4, k=8,
                                 S=0, act=BF16, wt=NVFP4, x_dist="rms", bias_std=0.5, seed=7),
+    "decode_mxfp4": LayerShape("decode_mxfp4", T=4, H=1536, I=512, E=128, G=8, Gk=4, k=8,
+                               S=0, act=BF16, wt=MXFP4, x_dist="rms", bias_std=0.0, seed=10),
+    "prefill_mxfp4": LayerShape("prefill_mxfp4", T=8192, H=1536, I=512, E=128, G=8, Gk=4, k=8,
+                                S=0, act=BF16, wt=MXFP4, x_dist="rms", bias_std=0.5, seed=11),
     "decode_stack": LayerShape("decode_stack", T=4, H=1536, I=512, E=128, G=8, Gk=4, k=8,
                                S=0, act=BF16, wt=BF16, x_dist="normal", bias_std=0.0, seed=6),
 }
@@ -162,6 +169,35 @@ def _encode_nvfp4(w: np.ndarray):
     return torch.from_numpy(packed), bcode.view(torch.uint8), torch.from_numpy(g)
 
 
+MX_BLOCK = 32
+
+
+def _encode_mxfp4(w: np.ndarray):
+    """Store expert matrices [n, rows, K] as MXFP4: packed E2M1 codes [n, rows, K/2]
+    (element 2i in the low nibble) and E8M0 scale codes [n, rows, K/32].
+
+    Per block of 32 inputs, the OCP Microscaling conversion: shared exponent
+    X = floor(log2(amax)) - 2 (2 = exponent of E2M1's largest value, 6 = 1.5 * 2^2),
+    code = nearest E2M1 value of w / 2^X, ties to the even code, saturating at 6; an
+    all-zero block gets X = -127.  The stored pair is the weight for every consumer.
+    """
+    n, rows, K = w.shape
+    blocks = w.reshape(n, rows, K // MX_BLOCK, MX_BLOCK).astype(np.float64)
+    amax = np.abs(blocks).max(axis=3)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))
+    X = np.clip(np.where(amax > 0, ex - 1 - 2, -127), -127, 127)
+    q = (blocks / np.ldexp(1.0, X)[..., None]).reshape(n, rows, K).astype(np.float32)
+    a = np.minimum(np.abs(q), np.float32(6.0))
+    idx = np.zeros(a.shape, dtype=np.uint8)
+    for m in E2M1_MID:
+        idx += a > m
+    last = E2M1_MID.size - 1
+    idx += (idx <= last) & (a == E2M1_MID[np.minimum(idx, last)]) & (idx % 2 == 1)   # ties: even code
+    codes = (idx | np.where(np.signbit(q), 8, 0)).astype(np.uint8)
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    return torch.from_numpy(packed), torch.from_numpy((X + 127).astype(np.uint8))
+
+
 def make_norm_weight(H: int, act: str, seed: int) -> torch.Tensor:
     """Pre-MoE RMSNorm weight [H] for the decoder step: 1 + 0.1 * N(0, 1) drawn in float32
     from ``default_rng(seed)`` (its own stream, so the layer draws above are unchanged),
@@ -201,7 +237,7 @@ def make_layer(shape: LayerShape) -> dict:
     if shape.bias_std > 0:
         bias = torch.from_numpy(rng.standard_normal(E, dtype=np.float32) * np.float32(shape.bias_std))
 
-    fp8, nv = shape.wt == E4M3, shape.wt == NVFP4
+    fp8, nv, mx = shape.wt == E4M3, shape.wt == NVFP4, shape.wt == MXFP4
     mats = {n: [] for n in ("gate", "up", "down")}
     scales = {n: [] for n in ("gate", "up", "down")}
     gscales = {n: [] for n in ("gate", "up", "down")}
@@ -212,7 +248,7 @@ def make_layer(shape: LayerShape) -> dict:
                 c, s = _encode_blocks(rng, w)
                 mats[name].append(c)
                 scales[name].append(s)
-            elif nv:
+            elif nv or mx:
                 mats[name].append(w)             # encoded below, all experts at once
             else:
                 mats[name].append(_store(w, shape.wt))
@@ -221,6 +257,10 @@ def make_layer(shape: LayerShape) -> dict:
         for name in ("gate", "up", "down"):
             c, b, g = _encode_nvfp4(np.stack(mats[name]))
             mats[name], scales[name], gscales[name] = list(c), list(b), list(g)
+    if mx:
+        for name in ("gate", "up", "down"):
+            c, b = _encode_mxfp4(np.stack(mats[name]))
+            mats[name], scales[name] = list(c), list(b)
     out = {"x": x, "w_router": w_router, "router_bias": bias}
     for name in ("gate", "up", "down"):
         out["w_" + name] = torch.stack(mats[name][:E])
@@ -231,11 +271,15 @@ def make_layer(shape: LayerShape) -> dict:
         else:
             out["s_" + name] = None
             out["sh_s_" + name] = None
-        if nv:
+        if nv or mx:
             out["b_" + name] = torch.stack(scales[name][:E])
             out["sh_b_" + name] = torch.stack(scales[name][E:]) if S else None
+        if nv:
             out["g_" + name] = torch.stack(gscales[name][:E])
             out["sh_g_" + name] = torch.stack(gscales[name][E:]) if S else None
+        elif mx:
+            for key in ("g_", "sh_g_"):
+                out[key + name] = None
         else:
             for key in ("b_", "sh_b_", "g_", "sh_g_"):
                 out[key + name] = None

@@ -9,7 +9,7 @@ from oracle import moe_oracle as mo
 import synth
 
 NEAR_TIE = 1e-4          # float64 logit margin below which either routing is acceptable
-TOL = {"f32": 5e-3, "bf16": 5e-3, "e4m3": 2e-2, "nvfp4": 5e-3}   # rel L2 bounds of the layer output
+TOL = {"f32": 5e-3, "bf16": 5e-3, "e4m3": 2e-2, "nvfp4": 5e-3, "mxfp4": 2e-2}   # rel L2 bounds of the layer output
 TOL_F32_INTERNAL = 1e-5  # fp32 layers must also be this close (no silent bf16 downcast)
 # every single token's output within TOKEN_FACTOR times the layer bound: a wrong row that
 # the whole-output figure would dilute (one bad (token, slot) row adds ~4e-3 in quadrature
@@ -31,12 +31,17 @@ def np_exact(t):
 
 
 def oracle_experts(layer) -> mo.Experts:
-    nv = sh_nv = None
-    if layer.get("b_gate") is not None:
+    nv = sh_nv = mx = sh_mx = None
+    if layer.get("b_gate") is not None and layer.get("g_gate") is None:      # MXFP4
+        mx = tuple(np_exact(layer[n]) for n in ("b_gate", "b_up", "b_down"))
+        if layer.get("sh_b_gate") is not None:
+            sh_mx = tuple(np_exact(layer["sh_" + n]) for n in ("b_gate", "b_up", "b_down"))
+    elif layer.get("b_gate") is not None:
         nv = tuple(np_exact(layer[n]) for n in NV_KEYS)
         if layer.get("sh_b_gate") is not None:
             sh_nv = tuple(np_exact(layer["sh_" + n]) for n in NV_KEYS)
-    return mo.Experts(*(np_exact(layer[n]) for n in WEIGHT_KEYS), nv=nv, sh_nv=sh_nv)
+    return mo.Experts(*(np_exact(layer[n]) for n in WEIGHT_KEYS), nv=nv, sh_nv=sh_nv, mx=mx,
+                      sh_mx=sh_mx)
 
 
 def to_device(layer, device="cuda") -> dict:
