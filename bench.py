@@ -35,7 +35,30 @@ NV_KEYS = ("b_gate", "b_up", "b_down", "g_gate", "g_up", "g_down")
 # weight copies rotated per step so that the weight stream comes from HBM, not from
 # the 256 MB last-level cache (one NVFP4 copy of the decode layer is ~170 MB)
 DEFAULT_SETS = {"tiny": 1, "decode": 8, "prefill": 2, "fp8": 4, "inkling": 1, "decode_nvfp4": 16,
-                "prefill_nvfp4": 4, "decode_stack": 1}
+                "prefill_nvfp4": 4, "decode_mxfp4": 16, "prefill_mxfp4": 4, "decode_stack": 1}
+PREFILL = ("prefill", "prefill_nvfp4", "prefill_mxfp4")
+
+
+def mfma_peak(shape):
+    """Dense matrix-core peak of the workload's contraction: MXFP4 experts multiply fp4
+    weights by fp8 activations on the block-scaled MFMA (the fp8 rate); the other prefill
+    layers run bf16 MFMAs."""
+    return FP8_PEAK_TFLOPS if shape.wt == "mxfp4" else BF16_PEAK_TFLOPS
+
+
+def weight_bytes(shape, mats):
+    """Bytes of `mats` expert matrices of one expert, with their scales."""
+    I, H = shape.I, shape.H
+    wbytes = {"e4m3": 1, "f32": 4, "bf16": 2, "nvfp4": 0.5, "mxfp4": 0.5}[shape.wt]
+    if shape.wt == "e4m3":
+        scales = mats * (I // 128) * (H // 128) * 4
+    elif shape.wt == "nvfp4":
+        scales = mats * (I * H // 16 + 4)          # e4m3 per 16 inputs + fp32 per matrix
+    elif shape.wt == "mxfp4":
+        scales = mats * (I * H // 32)              # e8m0 per 32 inputs
+    else:
+        scales = 0
+    return int(mats * I * H * wbytes) + scales
 
 
 def log(*a):
@@ -49,7 +72,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode",
                     choices=["tiny", "decode", "prefill", "fp8", "inkling", "decode_nvfp4",
-                             "prefill_nvfp4", "decode_stack", "paged"])
+                             "prefill_nvfp4", "decode_mxfp4", "prefill_mxfp4", "decode_stack",
+                             "paged"])
     ap.add_argument("--sets", type=int, default=0, help="weight copies rotated per step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="host time budget for the oracle baseline (0 = skip)")
@@ -112,22 +136,16 @@ def kernel_roofline(shape, which, ms, U):
     mats = 2 if which == "gateup" else 1          # gate+up, or down
     name = ("gate/up expert kernel (SwiGLU fused)" if which == "gateup"
             else "down expert kernel (routing weight applied)")
-    if shape.name in ("prefill", "prefill_nvfp4"):
+    if shape.name in PREFILL:
         flops = 2.0 * R * H * I * mats
         achieved = flops / (ms * 1e-3) / 1e12
-        return {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+        peak = mfma_peak(shape)
+        return {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": measured_traffic(shape.name, which),
                 "kernel": name, "kernel_us": round(ms * 1e3, 2),
                 "per_launch": f"{flops / 1e9:.2f} GFLOP = 2*R*H*I*{mats}, R={R} rows"}
-    wbytes = {"e4m3": 1, "f32": 4, "bf16": 2, "nvfp4": 0.5}[shape.wt]
-    if shape.wt == "e4m3":
-        scales = mats * (I // 128) * (H // 128) * 4
-    elif shape.wt == "nvfp4":
-        scales = mats * (I * H // 16 + 4)          # e4m3 per 16 inputs + fp32 per matrix
-    else:
-        scales = 0
-    per_expert = int(mats * I * H * wbytes) + scales
+    per_expert = weight_bytes(shape, mats)
     abytes = U * per_expert
     achieved = abytes / (ms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -143,20 +161,14 @@ def step_roofline(shape, ms, U):
     bytes the method must move (each touched expert's weights once, the router, x, y)."""
     T, H, I, E, k, S = shape.T, shape.H, shape.I, shape.E, shape.k, shape.S
     act = 4 if shape.act == "f32" else 2
-    if shape.name in ("prefill", "prefill_nvfp4"):
+    if shape.name in PREFILL:
         flops = 2.0 * T * (k + S) * H * I * 3 + 2.0 * T * E * H
         achieved = flops / (ms * 1e-3) / 1e12
-        return {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+        peak = mfma_peak(shape)
+        return {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "per_step": f"{flops / 1e9:.2f} GFLOP (experts 2*R*H*I*3 + router 2*T*E*H)"}
-    wbytes = {"e4m3": 1, "f32": 4, "bf16": 2, "nvfp4": 0.5}[shape.wt]
-    if shape.wt == "e4m3":
-        scales = 3 * (I // 128) * (H // 128) * 4
-    elif shape.wt == "nvfp4":
-        scales = 3 * (I * H // 16 + 4)
-    else:
-        scales = 0
-    per_expert = int(3 * I * H * wbytes) + scales
+    per_expert = weight_bytes(shape, 3)
     nbytes = U * per_expert + E * H * act + 2 * T * H * act
     achieved = nbytes / (ms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -166,12 +178,16 @@ def step_roofline(shape, ms, U):
 
 def oracle_experts(mo, cpu, f):
     """The oracle's expert set over the synthetic layer's stored weights."""
-    nv = sh_nv = None
-    if cpu.get("b_gate") is not None:
+    nv = sh_nv = mx = sh_mx = None
+    if cpu.get("b_gate") is not None and cpu.get("g_gate") is None:        # MXFP4
+        mx = tuple(f(cpu[n]) for n in ("b_gate", "b_up", "b_down"))
+        if cpu.get("sh_b_gate") is not None:
+            sh_mx = tuple(f(cpu["sh_" + n]) for n in ("b_gate", "b_up", "b_down"))
+    elif cpu.get("b_gate") is not None:
         nv = tuple(f(cpu[n]) for n in NV_KEYS)
         if cpu.get("sh_b_gate") is not None:
             sh_nv = tuple(f(cpu["sh_" + n]) for n in NV_KEYS)
-    return mo.Experts(*(f(cpu[n]) for n in WEIGHT_KEYS), nv=nv, sh_nv=sh_nv)
+    return mo.Experts(*(f(cpu[n]) for n in WEIGHT_KEYS), nv=nv, sh_nv=sh_nv, mx=mx, sh_mx=sh_mx)
 
 
 def blas_info():
@@ -435,7 +451,8 @@ def measure(workload, nsets, K, W, event_every):
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": K, "warmup": W, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
-        "dtype": {"f32": "f32", "bf16": "bf16", "e4m3": "e4m3+bf16", "nvfp4": "nvfp4+bf16"}[shape.wt],
+        "dtype": {"f32": "f32", "bf16": "bf16", "e4m3": "e4m3+bf16", "nvfp4": "nvfp4+bf16",
+                  "mxfp4": "mxfp4+mxfp8"}[shape.wt],
         "data": "synthetic",
         "config": {"workload": shape.name, "T": shape.T, "H": shape.H, "I": shape.I,
                    "E": shape.E, "G": shape.G, "Gk": shape.Gk, "k": shape.k, "S": shape.S,

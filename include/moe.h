@@ -67,21 +67,31 @@ typedef enum {
   MOE_BF16 = 1,       /* bfloat16 */
   MOE_E4M3_B128 = 2,  /* expert weights only: OCP e4m3 codes (uint8) with one fp32
                          scale per 128x128 block, value = decode(code) * scale */
-  MOE_NVFP4 = 3       /* expert weights only: FP4 E2M1 codes, two per byte (element 2i
+  MOE_NVFP4 = 3,      /* expert weights only: FP4 E2M1 codes, two per byte (element 2i
                          in the low nibble), one OCP e4m3 scale per 16 consecutive
                          inputs and one fp32 scale per expert matrix,
                          value = e2m1(code) * e4m3(block scale) * matrix scale.  The
                          4-bit expert format TensorFold issue #1247 "Ling-3.0-tiny on a
                          Qualcomm board" names in its list "What it does not cover";
                          its layout is not on the pages and this one is a reading. */
+  MOE_MXFP4 = 4       /* expert weights only: OCP Microscaling FP4 - E2M1 codes, two per
+                         byte (element 2i in the low nibble), one E8M0 scale code per 32
+                         consecutive inputs, value = e2m1(code) * 2^(scale - 127).  The layer
+                         then quantises its activations (x, and h before the down
+                         projection) per row per 32 to MXFP8 (E4M3 codes, E8M0 shared
+                         exponent floor(log2(amax)) - 8), and both operands go into the
+                         block-scaled matrix cores.  A reading of the 4-bit experts the
+                         pages name (TensorFold #1247, list "What it does not cover"; the
+                         graysoft ROCmFP4 page) with the format gfx950 takes natively. */
 } moe_dtype;
 
 /*
  * Layer configuration.  Supported element-type pairs (act_dtype, weight_dtype):
  *   (MOE_F32, MOE_F32), (MOE_BF16, MOE_BF16), (MOE_BF16, MOE_E4M3_B128),
- *   (MOE_BF16, MOE_NVFP4).
+ *   (MOE_BF16, MOE_NVFP4), (MOE_BF16, MOE_MXFP4).
  * Constraints: T >= 1; H, I >= 1 and multiples of 8 (of 128 for e4m3 experts, of
- * 32 for NVFP4 experts, which also need H <= 2048, I <= 1024 and k + S <= 32);
+ * 32 for NVFP4 experts, which also need H <= 2048, I <= 1024 and k + S <= 32; MXFP4
+ * experts need H % 256 == 0, I % 128 == 0, H <= 2048 and I <= 2048);
  * E >= 1; G >= 1 with E % G == 0; 1 <= Gk <= G; 1 <= k <= Gk * E / G;
  * k <= 16; E + S <= 1024; T * (k + S) < 2^31.
  */
@@ -100,7 +110,8 @@ typedef struct {
 
 /* Weights of one layer (device pointers).  s_* scales are used only for MOE_E4M3_B128,
  * b_* and g_* only for MOE_NVFP4 (whose w_* arrays then hold packed codes:
- * gate/up [E, I, H/2] bytes, down [E, H, I/2] bytes). */
+ * gate/up [E, I, H/2] bytes, down [E, H, I/2] bytes).  MOE_MXFP4 uses the same packed
+ * w_* arrays and b_* as E8M0 scale codes, gate/up [E, I, H/32], down [E, H, I/32]. */
 typedef struct {
   const void*  w_router;      /* [E, H] act_dtype */
   const float* router_bias;   /* [E] fp32, added to the logits before the softmax; NULL = none */
@@ -304,8 +315,9 @@ int moe_forward_paged(const moe_config* cfg, const void* x, const moe_weights* h
  * and debugging (host only, no device work).  After moe_forward / moe_forward_timed /
  * moe_forward_residual (and moe_route with logits == NULL) the workspace holds:
  *   MOE_WS_LOGITS      [T,E] fp32 router logits the routing was decided on (bias included);
- *   MOE_WS_ACT_CODES   [T,H] uint8 e4m3 codes of x (block-FP8 experts only, else 0 bytes);
- *   MOE_WS_ACT_SCALES  [T,H/128] fp32 scales of those codes (block-FP8 only);
+ *   MOE_WS_ACT_CODES   [T,H] uint8 e4m3 codes of x (block-FP8 and MXFP4 experts only,
+ *                      else 0 bytes);
+ *   MOE_WS_ACT_SCALES  their scales: [T,H/128] fp32 (block-FP8), [T,H/32] uint8 E8M0 (MXFP4);
  *   MOE_WS_NORM_ROWS   [T,H] act_dtype normalised rows (moe_forward_residual only).
  * The contents stay valid until the next call that uses the same workspace.  Writes the
  * byte offset from the workspace start and the slot's size; MOE_ERR_ARG for an unknown

@@ -17,8 +17,9 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
-MOE_F32, MOE_BF16, MOE_E4M3_B128, MOE_NVFP4 = 0, 1, 2, 3
-_DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "e4m3": MOE_E4M3_B128, "nvfp4": MOE_NVFP4}
+MOE_F32, MOE_BF16, MOE_E4M3_B128, MOE_NVFP4, MOE_MXFP4 = 0, 1, 2, 3, 4
+_DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "e4m3": MOE_E4M3_B128, "nvfp4": MOE_NVFP4,
+           "mxfp4": MOE_MXFP4}
 
 
 class MoeConfig(ctypes.Structure):

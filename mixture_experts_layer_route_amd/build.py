@@ -14,7 +14,8 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 
 SOURCES = ["moe_api.hip", "route.hip", "permute.hip", "ffn_skinny.hip", "ffn_mfma.hip",
-           "combine.hip", "decode.hip", "pager.hip"]
+           "combine.hip", "decode.hip", "pager.hip",
+           "ffn_mx.hip"]
 ARCH = "gfx950"
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

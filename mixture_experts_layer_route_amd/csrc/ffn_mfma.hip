@@ -20,21 +20,13 @@
 // gate columns and the matching up columns, so g and u of one (row, i) sit in the
 // same lane and register.
 #include "moe_internal.h"
+#include "gemm_common.h"
 
 namespace moe {
 
 constexpr int TM = 128;   // rows per tile (the schedule's BM)
 constexpr int TN = 128;   // output columns (or weight rows) per tile
 
-
-template <typename T>
-__device__ __forceinline__ const T* expert_mat(const T* routed, const T* shared, int e, int E,
-                                               int64_t stride) {
-  return e < E ? routed + int64_t(e) * stride : shared + int64_t(e - E) * stride;
-}
-
-// Row (M index) held by accumulator register r of a 32x32 MFMA block, for this lane.
-__device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
 // ===========================================================================
 // bf16: BK = 64 bf16 per slab (128 bytes per row = 8 chunks).
@@ -53,25 +45,6 @@ struct GemmBf16Args {
   float* out32;               // down: unweighted y_perm [R, H]
   int K, N, E;                // K: reduction length; N: output width (I for h, H for y)
 };
-
-// Work item of a grouped-GEMM workgroup.  Workgroup b runs on XCD b % 8; the
-// n = ntiles * ncol real items (tile-major, column block fastest) are split into 8
-// contiguous runs, one per XCD, so that the workgroups sharing an expert's weight
-// slabs and a tile's activation rows share one L2.  The grid must hold at least
-// 8 * ceil(n / 8) workgroups; the surplus returns false.
-__device__ __forceinline__ bool xcd_item(int ntiles, int ncol, int& tile, int& ct) {
-  const int n = ntiles * ncol;
-  const int per = (n + 7) >> 3;
-  const int slot = int(blockIdx.x >> 3);
-  const int j = int(blockIdx.x & 7) * per + slot;
-  if (slot >= per || j >= n) return false;
-  tile = j / ncol;
-  ct = j - tile * ncol;
-  return true;
-}
-
-// grid for xcd_item: max_items rounded up to a multiple of the 8 XCDs
-static inline unsigned xcd_grid(int64_t max_items) { return unsigned((max_items + 7) / 8 * 8); }
 
 template <bool GATEUP>
 __global__ __launch_bounds__(256) void k_gemm_bf16(GemmBf16Args p) {

@@ -65,11 +65,14 @@ int make_plan(const moe_config* c, Plan* p) {
   const bool dense16 = act == MOE_BF16 && wt == MOE_BF16;
   const bool fp8 = act == MOE_BF16 && wt == MOE_E4M3_B128;
   const bool nv4 = act == MOE_BF16 && wt == MOE_NVFP4;
-  if (!(dense32 || dense16 || fp8 || nv4)) return MOE_ERR_UNSUPPORTED;
+  const bool mx4 = act == MOE_BF16 && wt == MOE_MXFP4;
+  if (!(dense32 || dense16 || fp8 || nv4 || mx4)) return MOE_ERR_UNSUPPORTED;
   if (H % 8 || I % 8) return MOE_ERR_UNSUPPORTED;
   if (fp8 && (H % 128 || I % 128)) return MOE_ERR_UNSUPPORTED;
   // NVFP4 experts: the decode kernels (a handful of tokens) or the expert-major ones
   if (nv4 && (H % 32 || I % 32 || H > 2048 || I > 1024 || k + S > 32)) return MOE_ERR_UNSUPPORTED;
+  // MXFP4 experts: the block-scaled matrix-core kernels only
+  if (mx4 && (H % 256 || I % 128 || H > 2048 || I > 2048)) return MOE_ERR_UNSUPPORTED;
   if (E % G || G > 64 || Gk > G) return MOE_ERR_UNSUPPORTED;
   if (int64_t(k) > int64_t(Gk) * (E / G) || k > 16) return MOE_ERR_UNSUPPORTED;
   if (E + S > 1024) return MOE_ERR_UNSUPPORTED;
@@ -109,10 +112,12 @@ int make_plan(const moe_config* c, Plan* p) {
   q.o_h = take(size_t(q.R) * I * 4);
   q.o_ypw = take(q.skinny ? 0 : size_t(q.R) * H * 2);
   q.o_yp32 = take(q.skinny && !q.fused_down ? size_t(q.R) * H * 4 : 0);
-  q.o_xq = take(fp8 ? size_t(T) * H : 0);
-  q.o_sx = take(fp8 ? size_t(T) * (H / 128) * 4 : 0);
-  q.o_hq = take(fp8 ? size_t(q.R) * I : 0);
-  q.o_shq = take(fp8 ? size_t(q.R) * (I / 128) * 4 : 0);
+  // activation codes and scales: fp32 per 128 (block FP8) or one E8M0 byte per 32 (MXFP4),
+  // the same number of bytes
+  q.o_xq = take(fp8 || mx4 ? size_t(T) * H : 0);
+  q.o_sx = take(fp8 || mx4 ? size_t(T) * (H / 128) * 4 : 0);
+  q.o_hq = take(fp8 || mx4 ? size_t(q.R) * I : 0);
+  q.o_shq = take(fp8 || mx4 ? size_t(q.R) * (I / 128) * 4 : 0);
   q.o_xn = take(size_t(T) * H * (act == MOE_F32 ? 4 : 2));   // normalised rows (decoder step)
   q.total = o;
   *p = q;
@@ -137,6 +142,10 @@ static int check_experts(const Plan& p, const moe_weights* w) {
   if (p.wt == MOE_E4M3_B128) {
     if (!w->s_gate || !w->s_up || !w->s_down) return MOE_ERR_ARG;
     if (p.S > 0 && (!w->sh_s_gate || !w->sh_s_up || !w->sh_s_down)) return MOE_ERR_ARG;
+  }
+  if (p.wt == MOE_MXFP4) {
+    if (!w->b_gate || !w->b_up || !w->b_down) return MOE_ERR_ARG;
+    if (p.S > 0 && (!w->sh_b_gate || !w->sh_b_up || !w->sh_b_down)) return MOE_ERR_ARG;
   }
   if (p.wt == MOE_NVFP4) {
     if (!w->b_gate || !w->b_up || !w->b_down || !w->g_gate || !w->g_up || !w->g_down)
@@ -171,6 +180,13 @@ static int run_experts(const Plan& p, const void* x, const int32_t* off, const i
   uint8_t* hq = at<uint8_t>(ws, p.o_hq);
   float* shq = at<float>(ws, p.o_shq);
   float* h = at<float>(ws, p.o_h);
+  if (p.wt == MOE_MXFP4) {
+    uint8_t* sx8 = at<uint8_t>(ws, p.o_sx);
+    uint8_t* shq8 = at<uint8_t>(ws, p.o_shq);
+    MOE_TRY(launch_quant_mx(x, p.T, p.H, xq, sx8, st));
+    MOE_TRY(launch_gateup_mx4(p, xq, sx8, rowtok, off, tiles, meta, w, hq, shq8, st));
+    return launch_down_mx4(p, hq, shq8, off, tiles, meta, w, row_w, y_perm32, y_perm16, st);
+  }
   MOE_TRY(launch_quant(p, x, true, p.T, p.H, xq, sx, st));
   MOE_TRY(launch_gateup_mfma(p, x, rowtok, off, tiles, meta, w, h, xq, sx, hq, shq, st));
   return launch_down_mfma(p, hq, off, tiles, meta, w, row_w, y_perm32, y_perm16, shq, st);
@@ -269,11 +285,14 @@ int moe_workspace_slot(const moe_config* cfg, int slot, size_t* offset, size_t* 
   if (!offset || !bytes) return MOE_ERR_ARG;
   Plan p;
   MOE_TRY(make_plan(cfg, &p));
-  const bool fp8 = p.wt == MOE_E4M3_B128;
+  const bool fp8 = p.wt == MOE_E4M3_B128, mx4 = p.wt == MOE_MXFP4;
   switch (slot) {
     case MOE_WS_LOGITS: *offset = p.o_logits; *bytes = size_t(p.T) * p.E * 4; break;
-    case MOE_WS_ACT_CODES: *offset = p.o_xq; *bytes = fp8 ? size_t(p.T) * p.H : 0; break;
-    case MOE_WS_ACT_SCALES: *offset = p.o_sx; *bytes = fp8 ? size_t(p.T) * (p.H / 128) * 4 : 0; break;
+    case MOE_WS_ACT_CODES: *offset = p.o_xq; *bytes = fp8 || mx4 ? size_t(p.T) * p.H : 0; break;
+    case MOE_WS_ACT_SCALES:
+      *offset = p.o_sx;
+      *bytes = fp8 ? size_t(p.T) * (p.H / 128) * 4 : mx4 ? size_t(p.T) * (p.H / 32) : 0;
+      break;
     case MOE_WS_NORM_ROWS:
       *offset = p.o_xn;
       *bytes = size_t(p.T) * p.H * (p.act == MOE_F32 ? 4 : 2);
@@ -396,6 +415,14 @@ static int forward_impl(const moe_config* cfg, const void* x, const moe_weights*
     MOE_TRY(launch_gateup_mfma(p, x, rowtok, off, tiles, meta, w, h, nullptr, nullptr, nullptr,
                                nullptr, stream));
     MOE_TRY(launch_down_mfma(p, h, off, tiles, meta, w, row_w, nullptr, ypw, nullptr, stream));
+  } else if (p.wt == MOE_MXFP4) {
+    uint8_t* xq = at<uint8_t>(ws, p.o_xq);
+    uint8_t* sx8 = at<uint8_t>(ws, p.o_sx);
+    uint8_t* hq = at<uint8_t>(ws, p.o_hq);
+    uint8_t* shq8 = at<uint8_t>(ws, p.o_shq);
+    MOE_TRY(launch_quant_mx(x, p.T, p.H, xq, sx8, stream));
+    MOE_TRY(launch_gateup_mx4(p, xq, sx8, rowtok, off, tiles, meta, w, hq, shq8, stream));
+    MOE_TRY(launch_down_mx4(p, hq, shq8, off, tiles, meta, w, row_w, nullptr, ypw, stream));
   } else {
     uint8_t* xq = at<uint8_t>(ws, p.o_xq);
     float* sx = at<float>(ws, p.o_sx);

@@ -123,6 +123,17 @@ int launch_combine(const Plan& p, const float* y_perm, const int32_t* offsets, c
 int launch_combine_preweighted(const Plan& p, const bf16_t* y_perm, const int32_t* offsets,
                                const int32_t* inv, const void* res, void* y, hipStream_t st);
 
+// MXFP4 experts on the block-scaled matrix cores (ffn_mx.hip)
+bool mx4_ok(const Plan& p);
+int launch_quant_mx(const void* in, int64_t rows, int K, uint8_t* codes, uint8_t* scales,
+                    hipStream_t st);
+int launch_gateup_mx4(const Plan& p, const uint8_t* xq, const uint8_t* sx, const int32_t* row_token,
+                      const int32_t* offsets, const int2* tiles, const int32_t* meta,
+                      const moe_weights* w, uint8_t* hq, uint8_t* shq, hipStream_t st);
+int launch_down_mx4(const Plan& p, const uint8_t* hq, const uint8_t* shq, const int32_t* offsets,
+                    const int2* tiles, const int32_t* meta, const moe_weights* w,
+                    const float* row_w, float* out32, bf16_t* out16, hipStream_t st);
+
 // Expert paging (pager.hip): device state layout, planner and copy kernels.
 struct PagerLayout {
   size_t o_counters, o_key_slot, o_slot_key, o_stamp, total;
