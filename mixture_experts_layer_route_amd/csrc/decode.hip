@@ -45,6 +45,10 @@ __device__ __forceinline__ const TW* dexpert(const TW* routed, const TW* shared,
 // Tag type: expert weights stored as NVFP4 (packed E2M1 codes, e4m3 scale per 16
 // inputs, fp32 scale per matrix).
 struct nvfp4_t {};
+// Tag type: expert weights stored as MXFP4 (packed E2M1 codes, an E8M0 scale per 32
+// inputs, no matrix scale); x and h enter the products as MXFP8 (E4M3 elements with
+// a shared power-of-two exponent per 32).
+struct mxfp4_t {};
 
 template <typename TB>
 __device__ __forceinline__ const TB* nv_expert(const TB* routed, const TB* shared, int e, int E,
@@ -117,6 +121,8 @@ struct DecodeArgs {
   float* h;            // [R, I] fp32
   void* y;             // [T, H]
   const void* res;     // [T, H] residual added to y (the decoder step), or null
+  uint8_t* xq;         // MXFP4 experts: x's E4M3 codes [T, H] and E8M0 scales [T, H/32],
+  uint8_t* sxq;        //   written by block 0
   int T, H, I, E, S, G, Gk, k;
 };
 
@@ -215,6 +221,141 @@ __device__ __forceinline__ void decode_gateup_nv(const DecodeArgs& a, const bf16
   }
 }
 
+// Gate/up item loop for MXFP4 experts, laid out as the NVFP4 loop (item = active
+// expert and 4 rows of I, a 16-lane DPP row per weight row, lane cc taking the 32-input
+// chunks cc, cc+16, ...).  A chunk is one MX block of the weight row and of the token
+// row, so its partial dot (E2M1 values times the E4M3 values of x: exact products,
+// fp32 sums) is scaled once, by 2 to the sum of the two shared exponents.  xs holds
+// the token rows' E4M3 values (unscaled, as bf16) and sx_l their E8M0 codes.
+template <int NS>
+__device__ __forceinline__ void decode_gateup_mx(const DecodeArgs& a, const bf16_t* xs,
+                                                 const uint8_t* sx_l, const int32_t* off_l,
+                                                 const int32_t* act_l, const int32_t* rt_l,
+                                                 int n_act, int lane) {
+  struct Buf {
+    uint4 g[NS], u[NS];
+    int sg[NS], su[NS];
+  };
+  const int H = a.H, I = a.I, E = a.E;
+  const int H2 = H / 2, HC = H / 32;
+  const int q = lane >> 4, cc = lane & 15;
+  const int ipe = I / 4;
+  const int total = n_act * ipe;
+  const int64_t cstr = int64_t(I) * H2, bstr = int64_t(I) * HC;
+  const int gstride = gridDim.x * 4;
+  const uint8_t* wg = static_cast<const uint8_t*>(a.wg);
+  const uint8_t* wu = static_cast<const uint8_t*>(a.wu);
+  const uint8_t* shg = static_cast<const uint8_t*>(a.shg);
+  const uint8_t* shu = static_cast<const uint8_t*>(a.shu);
+  auto load = [&](int item, Buf& b) {
+    const int u = item / ipe, row = (item - u * ipe) * 4 + q;
+    const int e = act_l[u];
+    const uint8_t* gp = nv_expert(wg, shg, e, E, cstr) + int64_t(row) * H2;
+    const uint8_t* up = nv_expert(wu, shu, e, E, cstr) + int64_t(row) * H2;
+    const uint8_t* gs = nv_expert(a.bg, a.shbg, e, E, bstr) + int64_t(row) * HC;
+    const uint8_t* us = nv_expert(a.bu, a.shbu, e, E, bstr) + int64_t(row) * HC;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int c = cc + 16 * s;
+      if (c < HC) {
+        b.g[s] = *reinterpret_cast<const uint4*>(gp + c * 16);
+        b.u[s] = *reinterpret_cast<const uint4*>(up + c * 16);
+        b.sg[s] = gs[c];
+        b.su[s] = us[c];
+      }
+    }
+  };
+  auto compute = [&](int item, const Buf& b) {
+    const int u = item / ipe, i0 = (item - u * ipe) * 4;
+    const int e = act_l[u];
+    for (int r = off_l[e]; r < off_l[e + 1]; ++r) {
+      const int t = rt_l[r];
+      const bf16_t* xr = xs + int64_t(t) * H;
+      const uint8_t* sr = sx_l + t * HC;
+      float ag = 0.f, au = 0.f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int c = cc + 16 * s;
+        if (c < HC) {
+          uint32_t xv[16];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const uint4 t4 = *reinterpret_cast<const uint4*>(xr + c * 32 + v * 8);
+            xv[4 * v] = t4.x; xv[4 * v + 1] = t4.y; xv[4 * v + 2] = t4.z; xv[4 * v + 3] = t4.w;
+          }
+          const int xe = int(sr[c]) - 254;
+          const float dg = dot16_fp4_bf16(b.g[s].x, b.g[s].y, xv) + dot16_fp4_bf16(b.g[s].z, b.g[s].w, xv + 8);
+          const float du = dot16_fp4_bf16(b.u[s].x, b.u[s].y, xv) + dot16_fp4_bf16(b.u[s].z, b.u[s].w, xv + 8);
+          ag += ldexpf(dg, b.sg[s] + xe);
+          au += ldexpf(du, b.su[s] + xe);
+        }
+      }
+      ag = row_sum(ag);
+      au = row_sum(au);
+      if (cc == 0) a.h[int64_t(r) * I + i0 + q] = silu(ag) * au;
+    }
+  };
+  Buf ba, bb;
+  int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item < total) load(item, ba);
+  while (item < total) {
+    int nxt = item + gstride;
+    if (nxt < total) load(nxt, bb);
+    compute(item, ba);
+    item = nxt;
+    if (item >= total) break;
+    nxt = item + gstride;
+    if (nxt < total) load(nxt, ba);
+    compute(item, bb);
+    item = nxt;
+  }
+}
+
+// The block's token rows (bf16 in LDS) -> MXFP8 in place: each 32-input block gets
+// its shared exponent X (kept as the E8M0 code X + 127) and its elements become their
+// E4M3 values, held unscaled as bf16 (exact: an E4M3 value has four significant bits
+// and lies within bf16's range).  Four lanes (a DPP quad) hold one block, eight values
+// each.  Block 0 also writes the codes and scales to global memory.
+__device__ __forceinline__ void quantize_rows_mx(bf16_t* xs, uint8_t* sx_l, int n8,
+                                                 uint8_t* xq, uint8_t* sxq, bool pub) {
+  for (int i0 = 0; i0 < n8; i0 += 256) {        // same trip count in every lane: quads stay whole
+    const int i = i0 + int(threadIdx.x);
+    const bool live = i < n8;
+    const uint4 raw = live ? *reinterpret_cast<const uint4*>(xs + int64_t(i) * 8) : make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = __uint_as_float(w[j] << 16);
+      v[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+    float m = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+    m = fmaxf(m, dppf<0xB1>(m));    // quad_perm [1,0,3,2]
+    m = fmaxf(m, dppf<0x4E>(m));    // quad_perm [2,3,0,1]
+    const int X = mx_exponent(m);
+    const float inv = mx_inv_scale(X);
+    const uint32_t c0 = e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+    const uint32_t c1 = e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+    if (live) {
+      auto bits = [](auto f) {
+        return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xFFFF0000u);
+      };
+      *reinterpret_cast<uint4*>(xs + int64_t(i) * 8) =
+          make_uint4(bits(__builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c0, 1.0f, false)),
+                     bits(__builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c0, 1.0f, true)),
+                     bits(__builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c1, 1.0f, false)),
+                     bits(__builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c1, 1.0f, true)));
+      if ((threadIdx.x & 3) == 0) sx_l[i >> 2] = uint8_t(X + 127);
+      if (pub) {
+        *reinterpret_cast<uint2*>(xq + int64_t(i) * 8) = make_uint2(c0, c1);
+        if ((threadIdx.x & 3) == 0) sxq[i >> 2] = uint8_t(X + 127);
+      }
+    }
+  }
+}
+
 // SEL > 0: a wave per token (select_token_wave<SEL>); SEL < 0: sixteen lanes per
 // token, four tokens per wave (select_token_row<-SEL>)
 template <typename TA, typename TW, int NS, int SEL>
@@ -302,7 +443,7 @@ __global__ __launch_bounds__(256) void k_decode_gateup(DecodeArgs a) {
   bool prefetcher = false;
 #if MOE_DEC_PF > 0
   // (not for 4-bit weights: their stream is short and arithmetic-bound, measured neutral)
-  if constexpr (SEL < 0 && !std::is_same<TW, nvfp4_t>::value) {
+  if constexpr (SEL < 0 && !std::is_same<TW, nvfp4_t>::value && !std::is_same<TW, mxfp4_t>::value) {
     constexpr int V = -SEL;
     const int ngrp = (T + 3) / 4;
     if (wv >= ngrp) {                                  // uniform over the wave
@@ -452,6 +593,12 @@ __global__ __launch_bounds__(256) void k_decode_gateup(DecodeArgs a) {
   // ---------------------------------------------------------------- 2. gate/up
   if constexpr (std::is_same<TW, nvfp4_t>::value) {
     decode_gateup_nv<NS>(a, xs, off_l, act_l, rt_l, n_act_l, lane);
+  } else if constexpr (std::is_same<TW, mxfp4_t>::value) {
+    // the E8M0 codes of the token rows sit where the prefetch scratch would be
+    uint8_t* sx_l = lds_raw + ((bits_off + size_t(4) * E * 8 + 15) & ~size_t(15));
+    quantize_rows_mx(reinterpret_cast<bf16_t*>(xs), sx_l, T * H / 8, a.xq, a.sxq, pub);
+    __syncthreads();
+    decode_gateup_mx<NS>(a, reinterpret_cast<const bf16_t*>(xs), sx_l, off_l, act_l, rt_l, n_act_l, lane);
   } else {
   const int ipe = I / NI;
   const int total = n_act_l * ipe;
@@ -626,6 +773,24 @@ __global__ __launch_bounds__(256) void k_decode_down(DecodeArgs a) {
   }
 }
 
+// One 32-value block -> MXFP8 in place: the values become their E4M3 values (unscaled,
+// exact in fp32); returns the E8M0 code X + 127 of the shared exponent.
+__device__ __forceinline__ int quantize_block_mx(float (&v)[32]) {
+  float m = 0.f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) m = fmaxf(m, fabsf(v[j]));
+  const int X = mx_exponent(m);
+  const float inv = mx_inv_scale(X);
+#pragma unroll
+  for (int j = 0; j < 32; j += 4) {
+    const uint32_t c = e4m3x4(v[j] * inv, v[j + 1] * inv, v[j + 2] * inv, v[j + 3] * inv);
+    const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c, 1.0f, false);
+    const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c, 1.0f, true);
+    v[j] = lo[0]; v[j + 1] = lo[1]; v[j + 2] = hi[0]; v[j + 3] = hi[1];
+  }
+  return X + 127;
+}
+
 // Down + combine for NVFP4 experts.  Block item = (token t, 4*RG output columns);
 // the four waves split the token's k + S slots (slot j to wave j % 4, SP slots per
 // load batch), so each h row is fetched once per item and the weight rows of
@@ -634,12 +799,16 @@ __global__ __launch_bounds__(256) void k_decode_down(DecodeArgs a) {
 // of h and of the weight row.  The slot weight w[t,j] is folded with the matrix
 // scale of the slot's expert.  Per-wave partial sums meet in LDS and are added in
 // wave order, so the result does not depend on timing.
-template <int NSD, int RG, int SP>
+// MX: MXFP4 down weights (an E8M0 scale per 32 inputs, no matrix scale); a lane's
+// 32-input chunk of h is one MX block, so the lane quantises it to MXFP8 by itself
+// (quantize_block_mx) and scales the chunk's dot by 2 to the sum of the two exponents.
+template <int NSD, int RG, int SP, bool MX>
 __global__ __launch_bounds__(256) void k_decode_down_nv(DecodeArgs a) {
   constexpr int NRB = 4 * RG;
   const int T = a.T, H = a.H, I = a.I, E = a.E, S = a.S, k = a.k;
   const int nslot = T * k, nsl = k + S;
   const int I2 = I / 2, I16 = I / 16, IC = I / 32;
+  const int SB = MX ? IC : I16;                    // scale bytes per weight row
   __shared__ int32_t ids_l[256], inv_l[256];
   __shared__ float w_l[256];
   __shared__ int32_t offsh_l[32];
@@ -658,7 +827,7 @@ __global__ __launch_bounds__(256) void k_decode_down_nv(DecodeArgs a) {
 
   const int nb = (H + NRB - 1) / NRB;
   const int items = T * nb;
-  const int64_t cstr = int64_t(H) * I2, bstr = int64_t(H) * I16;
+  const int64_t cstr = int64_t(H) * I2, bstr = int64_t(H) * SB;
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
     const int t = item / nb, n0 = (item - t * nb) * NRB;
     float acc[RG];
@@ -684,7 +853,7 @@ __global__ __launch_bounds__(256) void k_decode_down_nv(DecodeArgs a) {
             r = offsh_l[j - k] + t;
             wt[m] = 1.f;
           }
-          wt[m] *= e < E ? a.gd[e] : a.shgd[e - E];
+          if (!MX) wt[m] *= e < E ? a.gd[e] : a.shgd[e - E];
           const uint8_t* cp = nv_expert(wd, shd, e, E, cstr);
           const uint8_t* bp = nv_expert(a.bd, a.shbd, e, E, bstr);
 #pragma unroll
@@ -703,7 +872,10 @@ __global__ __launch_bounds__(256) void k_decode_down_nv(DecodeArgs a) {
                 const int n = n0 + 4 * g + q;
                 if (n < H) {
                   wc[m][g][s] = *reinterpret_cast<const uint4*>(cp + int64_t(n) * I2 + c * 16);
-                  wsc[m][g][s] = *reinterpret_cast<const uint16_t*>(bp + int64_t(n) * I16 + c * 2);
+                  if (MX)
+                    wsc[m][g][s] = bp[int64_t(n) * SB + c];
+                  else
+                    wsc[m][g][s] = *reinterpret_cast<const uint16_t*>(bp + int64_t(n) * SB + c * 2);
                 }
               }
             }
@@ -713,6 +885,12 @@ __global__ __launch_bounds__(256) void k_decode_down_nv(DecodeArgs a) {
 #pragma unroll
       for (int m = 0; m < SP; ++m) {
         if (j0 + 4 * m < nsl) {
+          int hx[NSD];     // MX: h's E8M0 codes less both biases (added to the weight's code)
+#pragma unroll
+          for (int s = 0; s < NSD; ++s) {
+            hx[s] = 0;
+            if (MX && cc + 16 * s < IC) hx[s] = quantize_block_mx(hv[m][s]) - 254;
+          }
 #pragma unroll
           for (int g = 0; g < RG; ++g) {
             const int n = n0 + 4 * g + q;
@@ -721,10 +899,16 @@ __global__ __launch_bounds__(256) void k_decode_down_nv(DecodeArgs a) {
             for (int s = 0; s < NSD; ++s) {
               const int c = cc + 16 * s;
               if (c < IC && n < H) {
-                float s0, s1;
-                e4m3_pair(wsc[m][g][s], s0, s1);
-                d = fmaf(dot16_fp4_f32(wc[m][g][s].x, wc[m][g][s].y, hv[m][s]), s0, d);
-                d = fmaf(dot16_fp4_f32(wc[m][g][s].z, wc[m][g][s].w, hv[m][s] + 16), s1, d);
+                if (MX) {
+                  const float p = dot16_fp4_f32(wc[m][g][s].x, wc[m][g][s].y, hv[m][s]) +
+                                  dot16_fp4_f32(wc[m][g][s].z, wc[m][g][s].w, hv[m][s] + 16);
+                  d += ldexpf(p, int(wsc[m][g][s]) + hx[s]);
+                } else {
+                  float s0, s1;
+                  e4m3_pair(wsc[m][g][s], s0, s1);
+                  d = fmaf(dot16_fp4_f32(wc[m][g][s].x, wc[m][g][s].y, hv[m][s]), s0, d);
+                  d = fmaf(dot16_fp4_f32(wc[m][g][s].z, wc[m][g][s].w, hv[m][s] + 16), s1, d);
+                }
               }
             }
             acc[g] = fmaf(wt[m], d, acc[g]);
@@ -991,9 +1175,12 @@ __global__ __launch_bounds__(256) void k_nv_down_batch(DecodeArgs a,
 // ---------------------------------------------------------------------------
 static size_t decode_lds(const Plan& p) {
   const size_t tsize = p.act == MOE_F32 ? 4 : 2;
+  // after the token rows, the tables and the slot masks: the prefetch scratch (1 KB per
+  // wave) or, for MXFP4 experts, the E8M0 codes of the token rows; 16-byte aligned
+  const size_t tail = p.wt == MOE_MXFP4 ? size_t(p.T) * (p.H / 32) + 16
+                                        : MOE_DEC_PF > 0 ? 4096 + 16 : 0;
   return ((size_t(p.T) * p.H * tsize + 15) & ~size_t(15)) +
-         size_t(2 * (p.E + p.S) + 1 + p.R + 3 * p.T * p.k + 1) * 4 + size_t(4) * p.E * 8 + 8 +
-         (MOE_DEC_PF > 0 ? 4096 + 16 : 0);   // prefetch scratch, 1 KB per wave, 16-byte aligned
+         size_t(2 * (p.E + p.S) + 1 + p.R + 3 * p.T * p.k + 1) * 4 + size_t(4) * p.E * 8 + 8 + tail;
 }
 
 bool decode_ffn_ok(const Plan& p) {
@@ -1031,9 +1218,10 @@ static int launch_decode_t(const Plan& p, const DecodeArgs& a, hipStream_t st) {
   return check_launch();
 }
 
-template <int NS, int NSD, int Q>
+template <typename TW, int NS, int NSD, int Q>
 static int launch_decode_nv_t(const Plan& p, const DecodeArgs& a, hipStream_t st) {
-  const auto k1 = k_decode_gateup<bf16_t, nvfp4_t, NS, Q>;
+  constexpr bool MX = std::is_same<TW, mxfp4_t>::value;
+  const auto k1 = k_decode_gateup<bf16_t, TW, NS, Q>;
   const size_t lds = decode_lds(p);
   int b1 = 0, b2 = 0;
   // the 4-bit items end in conversion-heavy arithmetic once their data has arrived, so
@@ -1048,15 +1236,15 @@ static int launch_decode_nv_t(const Plan& p, const DecodeArgs& a, hipStream_t st
   launch_kernel(p, kTimeGateUp, k1, dim3(b1), dim3(256), lds, st, a);
   MOE_TRY(check_launch());
   if (rg == 4) {
-    const auto k2 = k_decode_down_nv<NSD, 4, SP>;
+    const auto k2 = k_decode_down_nv<NSD, 4, SP, MX>;
     MOE_TRY(persistent_blocks(reinterpret_cast<const void*>(k2), 0, &b2));
     launch_kernel(p, kTimeDown, k2, dim3(int(std::min<int64_t>(b2, items(4)))), dim3(256), 0, st, a);
   } else if (rg == 2) {
-    const auto k2 = k_decode_down_nv<NSD, 2, SP>;
+    const auto k2 = k_decode_down_nv<NSD, 2, SP, MX>;
     MOE_TRY(persistent_blocks(reinterpret_cast<const void*>(k2), 0, &b2));
     launch_kernel(p, kTimeDown, k2, dim3(int(std::min<int64_t>(b2, items(2)))), dim3(256), 0, st, a);
   } else {
-    const auto k2 = k_decode_down_nv<NSD, 1, SP>;
+    const auto k2 = k_decode_down_nv<NSD, 1, SP, MX>;
     MOE_TRY(persistent_blocks(reinterpret_cast<const void*>(k2), 0, &b2));
     launch_kernel(p, kTimeDown, k2, dim3(int(std::min<int64_t>(b2, items(1)))), dim3(256), 0, st, a);
   }
@@ -1117,8 +1305,10 @@ int launch_nv_down_batch(const Plan& p, const float* h, const int32_t* offsets,
 
 int launch_decode_ffn(const Plan& p, const void* x, const float* logits, const moe_weights* w,
                       int32_t* ids, float* wts, int32_t* offsets, int32_t* row_token,
-                      int32_t* inv, float* h, const void* res, void* y, hipStream_t st) {
+                      int32_t* inv, float* h, const void* res, void* y, uint8_t* xq,
+                      uint8_t* sxq, hipStream_t st) {
   DecodeArgs a{};
+  a.xq = xq; a.sxq = sxq;
   a.x = x; a.logits = logits;
   a.wg = w->w_gate; a.wu = w->w_up; a.wd = w->w_down;
   a.shg = w->sh_gate; a.shu = w->sh_up; a.shd = w->sh_down;
@@ -1131,33 +1321,38 @@ int launch_decode_ffn(const Plan& p, const void* x, const float* logits, const m
   a.T = int(p.T); a.H = p.H; a.I = p.I; a.E = p.E; a.S = p.S; a.G = p.G; a.Gk = p.Gk; a.k = p.k;
   const int ns = (p.H + 511) / 512, nsd = (p.I + 511) / 512;
   const bool rows = select_rows_ok(p);
+  // 4-bit experts (NVFP4 or MXFP4): bf16 activations, their own item loops
+#define MOE_NQ(TW, NSV, NSDV)                                                    \
+  {                                                                              \
+    if (rows) {                                                                  \
+      if (p.E == 128) return launch_decode_nv_t<TW, NSV, NSDV, -8>(p, a, st);    \
+      if (p.E == 256) return launch_decode_nv_t<TW, NSV, NSDV, -16>(p, a, st);   \
+      if (p.E == 64) return launch_decode_nv_t<TW, NSV, NSDV, -4>(p, a, st);     \
+      if (p.E == 16) return launch_decode_nv_t<TW, NSV, NSDV, -1>(p, a, st);     \
+    }                                                                            \
+    if (p.E <= 64) return launch_decode_nv_t<TW, NSV, NSDV, 1>(p, a, st);        \
+    if (p.E <= 128) return launch_decode_nv_t<TW, NSV, NSDV, 2>(p, a, st);       \
+    if (p.E <= 256) return launch_decode_nv_t<TW, NSV, NSDV, 4>(p, a, st);       \
+    if (p.E <= 512) return launch_decode_nv_t<TW, NSV, NSDV, 8>(p, a, st);       \
+    return launch_decode_nv_t<TW, NSV, NSDV, 16>(p, a, st);                      \
+  }
+#define MOE_NNS(TW, NSDV)                 \
+  {                                       \
+    if (ns <= 1) MOE_NQ(TW, 1, NSDV)      \
+    if (ns == 2) MOE_NQ(TW, 2, NSDV)      \
+    if (ns == 3) MOE_NQ(TW, 3, NSDV)      \
+    MOE_NQ(TW, 4, NSDV)                   \
+  }
   if (p.wt == MOE_NVFP4) {
-#define MOE_NQ(NSV, NSDV)                                                    \
-  {                                                                          \
-    if (rows) {                                                              \
-      if (p.E == 128) return launch_decode_nv_t<NSV, NSDV, -8>(p, a, st);    \
-      if (p.E == 256) return launch_decode_nv_t<NSV, NSDV, -16>(p, a, st);   \
-      if (p.E == 64) return launch_decode_nv_t<NSV, NSDV, -4>(p, a, st);     \
-      if (p.E == 16) return launch_decode_nv_t<NSV, NSDV, -1>(p, a, st);     \
-    }                                                                        \
-    if (p.E <= 64) return launch_decode_nv_t<NSV, NSDV, 1>(p, a, st);        \
-    if (p.E <= 128) return launch_decode_nv_t<NSV, NSDV, 2>(p, a, st);       \
-    if (p.E <= 256) return launch_decode_nv_t<NSV, NSDV, 4>(p, a, st);       \
-    if (p.E <= 512) return launch_decode_nv_t<NSV, NSDV, 8>(p, a, st);       \
-    return launch_decode_nv_t<NSV, NSDV, 16>(p, a, st);                      \
+    if (nsd <= 1) MOE_NNS(nvfp4_t, 1)
+    MOE_NNS(nvfp4_t, 2)
   }
-#define MOE_NNS(NSDV)                 \
-  {                                   \
-    if (ns <= 1) MOE_NQ(1, NSDV)      \
-    if (ns == 2) MOE_NQ(2, NSDV)      \
-    if (ns == 3) MOE_NQ(3, NSDV)      \
-    MOE_NQ(4, NSDV)                   \
+  if (p.wt == MOE_MXFP4) {
+    if (nsd <= 1) MOE_NNS(mxfp4_t, 1)
+    MOE_NNS(mxfp4_t, 2)
   }
-    if (nsd <= 1) MOE_NNS(1)
-    MOE_NNS(2)
 #undef MOE_NNS
 #undef MOE_NQ
-  }
 #define MOE_DQ(TA, TW, NSV, NSDV)                                            \
   {                                                                          \
     if (rows) {                                                              \

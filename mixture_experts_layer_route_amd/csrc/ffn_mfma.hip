@@ -929,7 +929,8 @@ void k_gemm_fp8_v2(GemmFp8Args p) {
   constexpr int BM = C::BM, BN = C::BN, W = C::W, WM = C::WM, WN = C::WN, MI = C::MI, NI = C::NI;
   constexpr int AJ = C::AJ, BJ = C::BJ, L = C::L, NT = C::NT, SMAX = C::SMAX;
   __shared__ uint4 smem[C::RING_U4];
-  __shared__ float sa_l[BM * SMAX];      // activation scales [row][slab]
+  constexpr int SST = SMAX + 1;          // row stride of sa_l: odd, so 32 rows hit 32 banks
+  __shared__ float sa_l[BM * SST];       // activation scales [row][slab]
   __shared__ float sw_l[4 * SMAX];       // weight block scales [block][slab]
   const int ncol = GATEUP ? p.N / (BN / 2) : p.N / BN;
   int tile, ct;
@@ -996,7 +997,7 @@ void k_gemm_fp8_v2(GemmFp8Args p) {
 #pragma unroll
     for (int u = 0; u < SP; ++u) {
       const int i = tid + u * NT;
-      if (i < BM * nkb) sa_l[(i / nkb) * SMAX + i % nkb] = sv[u];
+      if (i < BM * nkb) sa_l[(i / nkb) * SST + i % nkb] = sv[u];
     }
     if (tid < 2 * nkb) {
       const int blk = tid / nkb, kb = tid - blk * nkb;
@@ -1050,7 +1051,7 @@ void k_gemm_fp8_v2(GemmFp8Args p) {
     __builtin_amdgcn_sched_barrier(0);
     float sact[MI], swt[NI];
 #pragma unroll
-    for (int a = 0; a < MI; ++a) sact[a] = sa_l[(wm * (BM / WM) + a * 32 + (lane & 31)) * SMAX + kt];
+    for (int a = 0; a < MI; ++a) sact[a] = sa_l[(wm * (BM / WM) + a * 32 + (lane & 31)) * SST + kt];
 #pragma unroll
     for (int b = 0; b < NI; ++b) swt[b] = sw_l[(GATEUP ? b : swb0) * SMAX + kt];
 #pragma unroll
@@ -1120,7 +1121,7 @@ void k_gemm_fp8_v2(GemmFp8Args p) {
         const uint32_t pk = e4m3x4(hv[a][4 * g] / scale, hv[a][4 * g + 1] / scale,
                                    hv[a][4 * g + 2] / scale, hv[a][4 * g + 3] / scale);
         const int col = wn * (BN / 2 / WN) + 8 * g + 4 * (lane >> 5);
-        *reinterpret_cast<uint32_t*>(stg + row * 128 + col) = pk;
+        *reinterpret_cast<uint32_t*>(stg + stg128(row, col)) = pk;
       }
       if (wn == 0 && lane < 32 && row < rows)
         p.qscale[int64_t(base + m0 + row) * (p.N / 128) + ct] = scale;
@@ -1130,7 +1131,7 @@ void k_gemm_fp8_v2(GemmFp8Args p) {
     for (int i = tid; i < rows * 8; i += NT) {
       const int row = i >> 3, c = i & 7;
       *reinterpret_cast<uint4*>(p.qout + int64_t(base + m0 + row) * p.N + ct * 128 + c * 16) =
-          *reinterpret_cast<const uint4*>(stg + row * 128 + c * 16);
+          *reinterpret_cast<const uint4*>(stg + stg128(row, c * 16));
     }
     return;
   }

@@ -71,13 +71,6 @@ __device__ __forceinline__ int swz4(int row, int chunk) { return row * 4 + (chun
 __device__ __forceinline__ int dma_chunk4(int lane, int j) {
   return (lane & 3) ^ (((16 * j + (lane >> 2)) >> 2) & 3);
 }
-// E8M0 shared exponent of a block whose largest magnitude is m (finite, >= 0), and the
-// power of two 2^-X that maps the block onto the E4M3 grid (exact multiplication).
-__device__ __forceinline__ int mx_exponent(float m) {
-  const int e = int((__float_as_uint(m) >> 23) & 0xFF) - 127 - 8;   // floor(log2 m) - 8
-  return min(max(e, -127), 127);
-}
-__device__ __forceinline__ float mx_inv_scale(int X) { return __uint_as_float(uint32_t(127 - X) << 23); }
 
 template <bool GATEUP>
 __global__ __launch_bounds__(Mx4Tile::NT) __attribute__((amdgpu_waves_per_eu(2)))
@@ -259,7 +252,7 @@ void k_gemm_mx4(GemmMx4Args p) {
         const uint32_t pk = e4m3x4(hv[4 * g] * inv, hv[4 * g + 1] * inv, hv[4 * g + 2] * inv,
                                    hv[4 * g + 3] * inv);
         const int col = wn * 32 + 8 * g + 4 * (lane >> 5);
-        *reinterpret_cast<uint32_t*>(stg + row * 128 + col) = pk;
+        *reinterpret_cast<uint32_t*>(stg + stg128(row, col)) = pk;
       }
       if (lane < 32 && row < rows)
         p.qscale[int64_t(base + m0 + row) * (p.N / 32) + ct * 4 + wn] = uint8_t(X + 127);
@@ -268,7 +261,7 @@ void k_gemm_mx4(GemmMx4Args p) {
     for (int i = tid; i < rows * 8; i += NT) {
       const int row = i >> 3, c = i & 7;
       *reinterpret_cast<uint4*>(p.qout + int64_t(base + m0 + row) * p.N + ct * 128 + c * 16) =
-          *reinterpret_cast<const uint4*>(stg + row * 128 + c * 16);
+          *reinterpret_cast<const uint4*>(stg + stg128(row, c * 16));
     }
     return;
   }

@@ -30,6 +30,15 @@ __device__ __forceinline__ bool xcd_item(int ntiles, int ncol, int& tile, int& c
   return true;
 }
 
+// Byte offset of column col (0..127) of row `row` in an LDS staging tile of 128-byte
+// rows (the gate/up epilogues' E4M3 codes of h).  The 16-byte chunks of a row are
+// permuted by (row >> 1) & 7: a wave stores one column of 32 consecutive rows at a
+// time, which without the permutation would all fall on the same bank; the copy-out
+// reads whole chunks.
+__device__ __forceinline__ int stg128(int row, int col) {
+  return row * 128 + ((((col >> 4) ^ (row >> 1)) & 7) << 4) + (col & 15);
+}
+
 // grid for xcd_item: max_items rounded up to a multiple of the 8 XCDs
 static inline unsigned xcd_grid(int64_t max_items) { return unsigned((max_items + 7) / 8 * 8); }
 

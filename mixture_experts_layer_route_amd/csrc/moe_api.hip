@@ -71,7 +71,8 @@ int make_plan(const moe_config* c, Plan* p) {
   if (fp8 && (H % 128 || I % 128)) return MOE_ERR_UNSUPPORTED;
   // NVFP4 experts: the decode kernels (a handful of tokens) or the expert-major ones
   if (nv4 && (H % 32 || I % 32 || H > 2048 || I > 1024 || k + S > 32)) return MOE_ERR_UNSUPPORTED;
-  // MXFP4 experts: the block-scaled matrix-core kernels only
+  // MXFP4 experts: the decode kernels (a handful of tokens) or the block-scaled
+  // matrix-core kernels
   if (mx4 && (H % 256 || I % 128 || H > 2048 || I > 2048)) return MOE_ERR_UNSUPPORTED;
   if (E % G || G > 64 || Gk > G) return MOE_ERR_UNSUPPORTED;
   if (int64_t(k) > int64_t(Gk) * (E / G) || k > 16) return MOE_ERR_UNSUPPORTED;
@@ -92,6 +93,11 @@ int make_plan(const moe_config* c, Plan* p) {
   q.fused_down = q.skinny && T <= 16;
   // NVFP4 batches the decode kernels do not take run the expert-major kernels + combine
   if (nv4 && q.fused_down && !decode_ffn_ok(q)) q.fused_down = false;
+  // MXFP4: the decode kernels where they apply, else the matrix-core kernels
+  if (mx4) {
+    q.skinny = q.fused_down = T <= 16 && q.Rk <= 8 * int64_t(E);
+    if (q.skinny && !decode_ffn_ok(q)) q.skinny = q.fused_down = false;
+  }
   q.max_active = std::min<int64_t>(E, q.Rk) + S;
   q.bm = gemm_tile_rows(q);
   q.max_tiles = q.Rk / q.bm + std::min<int64_t>(E, q.Rk) + int64_t(S) * ((T + q.bm - 1) / q.bm);
@@ -164,7 +170,8 @@ static int run_experts(const Plan& p, const void* x, const int32_t* off, const i
   int32_t* active = at<int32_t>(ws, p.o_active);
   int32_t* meta = at<int32_t>(ws, p.o_meta);
   int2* tiles = at<int2>(ws, p.o_tiles);
-  if (p.skinny) {
+  // (MXFP4 experts have no skinny kernels: the matrix-core ones take every batch here)
+  if (p.skinny && p.wt != MOE_MXFP4) {
     float* h = at<float>(ws, p.o_h);
     MOE_TRY(launch_gateup_skinny(p, x, rowtok, off, active, meta, w, h, st));
     return launch_down_skinny(p, h, off, active, meta, w, y_perm32, st);
@@ -384,7 +391,7 @@ static int forward_impl(const moe_config* cfg, const void* x, const moe_weights*
       MOE_TRY(launch_logits(p, x, w->w_router, w->router_bias, logits, stream));
     }
     return launch_decode_ffn(p, x, logits, w, ids, wts, off, rowtok, inv, at<float>(ws, p.o_h),
-                             res, y, stream);
+                             res, y, at<uint8_t>(ws, p.o_xq), at<uint8_t>(ws, p.o_sx), stream);
   }
   if (gamma) {
     MOE_TRY(launch_rmsnorm(p, x, gamma, eps, xn, stream));

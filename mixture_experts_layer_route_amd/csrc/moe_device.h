@@ -181,6 +181,16 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
   return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(cl(c), cl(d), lo, true));
 }
 
+// MXFP8 activations (OCP Microscaling, E4M3 elements): the E8M0 shared exponent X of
+// a block whose largest magnitude is m (finite, >= 0; all-zero and subnormal blocks
+// give the clamp -127), and the power of two 2^-X that maps the block onto the E4M3
+// grid (exact multiplication; X <= 119 for finite m, so the result is a normal float).
+__device__ __forceinline__ int mx_exponent(float m) {
+  const int e = int((__float_as_uint(m) >> 23) & 0xFF) - 127 - 8;   // floor(log2 m) - 8
+  return min(max(e, -127), 127);
+}
+__device__ __forceinline__ float mx_inv_scale(int X) { return __uint_as_float(uint32_t(127 - X) << 23); }
+
 // ----------------------------------------------------------------- wave reductions
 // DPP steps inside each row of 16 lanes (quad swaps, half-row and row mirrors),
 // then the four row results combined through readlane in a fixed order, so the

@@ -87,10 +87,12 @@ bool select_rows_ok(const Plan& p);
 int gemm_tile_rows(const Plan& p);
 // the NVFP4 matrix-core kernels cover this shape
 bool nv4_mfma_ok(const Plan& p);
-// Decode path: gate/up (with in-kernel routing) then down + combine.
+// Decode path: gate/up (with in-kernel routing) then down + combine.  xq / sxq receive
+// x's MXFP8 codes and E8M0 scales when the experts are MXFP4 (unused otherwise).
 int launch_decode_ffn(const Plan& p, const void* x, const float* logits, const moe_weights* w,
                       int32_t* ids, float* wts, int32_t* offsets, int32_t* row_token,
-                      int32_t* inv, float* h, const void* res, void* y, hipStream_t st);
+                      int32_t* inv, float* h, const void* res, void* y, uint8_t* xq,
+                      uint8_t* sxq, hipStream_t st);
 // NVFP4 experts beyond the decode kernels: expert-major gate/up (h fp32) and down
 // (unweighted fp32 rows), reading the permutation from global memory
 int launch_nv_gateup_batch(const Plan& p, const void* x, const int32_t* row_token,

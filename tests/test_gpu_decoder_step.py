@@ -113,7 +113,8 @@ def _run(moe, shape, inplace=False, scale=1.0):
 CASES = [
     # workload or explicit shape, T override
     ("decode", None), ("decode", 1), ("decode", 16), ("decode_nvfp4", None), ("prefill", 300),
-    ("tiny", None), ("tiny", 300), ("fp8", 130), ("inkling", 100),
+    ("tiny", None), ("tiny", 300), ("fp8", 130), ("inkling", 100), ("decode_mxfp4", None),
+    ("prefill_mxfp4", 300),
 ]
 
 
