@@ -82,6 +82,10 @@ def parse():
     ap.add_argument("--no-prefill-leg", action="store_true",
                     help="decode workload only: skip the 8192-token prefill layer that the "
                          "default line carries as its second measurement")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="only time the vendor BLAS (torch.bmm / torch.mm, bf16) on the prefill "
+                         "layer's expert-GEMM shapes with equal rows per expert, as a ceiling for "
+                         "the grouped kernels, and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (a known byte "
                          "count for scaling the profiler's FETCH_SIZE / WRITE_SIZE) and exit")
@@ -98,6 +102,45 @@ def copy_calibration(mib):
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "repeats": 5}),
           flush=True)
+
+
+def library_gemm(steps=20):
+    """The vendor BLAS on the prefill layer's expert GEMMs (bf16, fp32 accumulation) with
+    the 65,536 routed rows split evenly over the 128 experts (512 each, no padding, no
+    gather, no epilogue): batched gate/up [E,512,H] x [E,H,2I] and down [E,512,I] x
+    [E,I,H], and the same flops as one dense GEMM.  A reference point for the grouped
+    kernels, which also gather rows, pad ragged tiles and fuse SwiGLU / the weights."""
+    import torch
+    import synth
+    sh = synth.WORKLOADS["prefill"]
+    E, H, I, R = sh.E, sh.H, sh.I, sh.T * sh.k
+    M = R // E
+    g = torch.Generator(device="cuda").manual_seed(7)
+    def rnd(*dims):
+        return (torch.randn(*dims, device="cuda", generator=g) * 0.05).to(torch.bfloat16)
+    cases = {
+        "gateup_bmm": (lambda a, b: torch.bmm(a, b), rnd(E, M, H), rnd(E, H, 2 * I), 2 * R * H * 2 * I),
+        "down_bmm": (lambda a, b: torch.bmm(a, b), rnd(E, M, I), rnd(E, I, H), 2 * R * I * H),
+        "gateup_dense_mm": (lambda a, b: torch.mm(a, b), rnd(R, H), rnd(H, 2 * I), 2 * R * H * 2 * I),
+        "down_dense_mm": (lambda a, b: torch.mm(a, b), rnd(R, I), rnd(I, H), 2 * R * I * H),
+    }
+    out = {"library": f"torch {torch.__version__} (hipBLASLt / rocBLAS)", "rows_per_expert": M}
+    for name, (fn, a, b, flops) in cases.items():
+        for _ in range(5):
+            fn(a, b)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            fn(a, b)
+        t1.record()
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) * 1e3 / steps
+        tf = flops / us / 1e6
+        out[name] = {"us": round(us, 2), "TFLOP/s": round(tf, 1),
+                     "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
+        log(name, out[name])
+    print(json.dumps(out), flush=True)
 
 
 def measured_traffic(workload, which):
@@ -570,6 +613,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.library_gemm:
+        library_gemm()
         return
     if args.workload == "decode_stack":
         run_stack(args)
