@@ -86,6 +86,10 @@ def parse():
                     help="only time the vendor BLAS (torch.bmm / torch.mm, bf16) on the prefill "
                          "layer's expert-GEMM shapes with equal rows per expert, as a ceiling for "
                          "the grouped kernels, and exit")
+    ap.add_argument("--peaks", action="store_true",
+                    help="only measure what this GPU achieves on plain work (a 4 GiB streaming "
+                         "read, a 4 GiB copy, a large bf16 GEMM through the vendor BLAS), the "
+                         "context for the roofline fractions against the published peaks, and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (a known byte "
                          "count for scaling the profiler's FETCH_SIZE / WRITE_SIZE) and exit")
@@ -140,6 +144,38 @@ def library_gemm(steps=20):
         out[name] = {"us": round(us, 2), "TFLOP/s": round(tf, 1),
                      "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
         log(name, out[name])
+    print(json.dumps(out), flush=True)
+
+
+def peaks(steps=10):
+    """Achieved rates on plain work, next to the published peaks: HBM read (a sum over a
+    4 GiB bf16 tensor), HBM copy (4 GiB read + 4 GiB written), and a 8192^3 bf16 GEMM."""
+    import torch
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e-3 / steps       # seconds per call
+    n = 4 << 30
+    src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")
+    acc = torch.empty((), dtype=torch.float32, device="cuda")
+    t_read = timed(lambda: torch.sum(src, dim=0, dtype=torch.float32, out=acc))
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: dst.copy_(src))
+    del src, dst
+    m = 8192
+    a = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    b = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    t_mm = timed(lambda: torch.mm(a, b))
+    out = {"hbm_read_GBs": round(n / t_read / 1e9, 1), "hbm_copy_GBs": round(2 * n / t_copy / 1e9, 1),
+           "bf16_gemm_8192_TFLOPs": round(2 * m ** 3 / t_mm / 1e12, 1),
+           "published": {"hbm_GBs": HBM_PEAK_GBS, "bf16_TFLOPs": BF16_PEAK_TFLOPS}}
     print(json.dumps(out), flush=True)
 
 
@@ -484,6 +520,17 @@ def measure(workload, nsets, K, W, event_every):
     end.record()
     torch.cuda.synchronize()
     ms_plain = start.elapsed_time(end) / K
+    # the spread over single steps: up to 100 more steps, each between its own event pair
+    n1 = min(K, 100)
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(n1)]
+    for i, (a, b) in enumerate(pairs):
+        a.record()
+        moe.forward(cfg, x, None, ws, y=y, wst=wsts[i % nsets])
+        b.record()
+    torch.cuda.synchronize()
+    step_us = [a.elapsed_time(b) * 1e3 for a, b in pairs]
+    step_pct = [round(float(np.percentile(step_us, q)), 2) for q in (10, 50, 90)]
     log(f"step {ms_per_step * 1e3:.2f} us (untimed kernels {ms_plain * 1e3:.2f} us); kernels: "
         + ", ".join(f"{n} {v * 1e3:.2f} us" for n, v in kern_ms.items()))
     tokens_per_s = shape.T / (ms_per_step * 1e-3)
@@ -504,6 +551,8 @@ def measure(workload, nsets, K, W, event_every):
         "kernel_us_p10_p50_p90": kern_pct,
         "kernel_events_on_steps": f"every {every}th ({len(timed)} of {K})",
         "ms_per_step_without_kernel_events": round(ms_plain, 5),
+        "step_us_p10_p50_p90": step_pct,
+        "step_us_samples": f"{n1} single steps, one event pair each",
         "parity_rel_l2": float(f"{err:.3e}"),
         "roofline": roof,
         "step_roofline": step_roofline(shape, ms_per_step, U),
@@ -617,6 +666,9 @@ def main():
     if args.library_gemm:
         library_gemm()
         return
+    if args.peaks:
+        peaks()
+        return
     if args.workload == "decode_stack":
         run_stack(args)
         return
@@ -636,7 +688,8 @@ def main():
                             min(args.warmup, 10), args.event_every)
         res["prefill_leg"] = {k: leg[k] for k in (
             "value", "unit", "ms_per_step", "steps", "warmup", "config", "kernel_us",
-            "ms_per_step_without_kernel_events", "parity_rel_l2", "roofline", "step_roofline")}
+            "ms_per_step_without_kernel_events", "step_us_p10_p50_p90", "parity_rel_l2",
+            "roofline", "step_roofline")}
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(shape, cpu, args.cpu_seconds)
     print(json.dumps(res), flush=True)
