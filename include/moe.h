@@ -79,8 +79,10 @@ typedef enum {
                          consecutive inputs, value = e2m1(code) * 2^(scale - 127).  The layer
                          then quantises its activations (x, and h before the down
                          projection) per row per 32 to MXFP8 (E4M3 codes, E8M0 shared
-                         exponent floor(log2(amax)) - 8), and both operands go into the
-                         block-scaled matrix cores.  A reading of the 4-bit experts the
+                         exponent floor(log2(amax)) - 8); batches beyond a handful of
+                         tokens multiply both operands on the block-scaled matrix cores,
+                         up to 16 tokens the decode kernels form the same E2M1 x E4M3
+                         products on the vector units.  A reading of the 4-bit experts the
                          pages name (TensorFold #1247, list "What it does not cover"; the
                          graysoft ROCmFP4 page) with the format gfx950 takes natively. */
 } moe_dtype;

@@ -20,8 +20,9 @@
 // slower on MI355X than the launch it saves (the cross-XCD arrival counting and
 // cache write-back cost tens of microseconds), so the halves are two launches.
 // NVFP4 experts have their own item loops here (decode, and the expert-major ones
-// for batches the decode kernels do not take); the decoder step adds the residual
-// in the down kernels.
+// for batches the decode kernels do not take), and MXFP4 experts share the NVFP4
+// decode layout with MX block scales and MXFP8 activations; the decoder step adds
+// the residual in the down kernels.
 #include <type_traits>
 
 #include "moe_internal.h"
