@@ -441,6 +441,52 @@ def run_stack(args):
     print(json.dumps(res), flush=True)
 
 
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000   # hipEventDisableSystemFence
+SETTLE_S = 0.25                  # seconds of back-to-back layer runs before the warm-up
+
+
+class HipTimer:
+    """Timing-only HIP events created with hipEventDisableSystemFence: recording one skips
+    the system-scope release a default event performs (a cache write-back and invalidate),
+    so events attached to the kernels of a timed step cost little and disturb nothing after
+    them.  They are read only after a device synchronisation.  Calls go to the HIP runtime
+    that torch (and the MoE library) already use in this process."""
+
+    def __init__(self):
+        path = next(l.split()[-1] for l in open("/proc/self/maps") if "libamdhip64" in l)
+        hip = ctypes.CDLL(path)
+        hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                            ctypes.c_void_p]
+        hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip, self.events = hip, []
+
+    def _check(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} returned HIP error {rc}")
+
+    def event(self):
+        e = ctypes.c_void_p()
+        self._check(self.hip.hipEventCreateWithFlags(ctypes.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE),
+                    "hipEventCreateWithFlags")
+        self.events.append(e)
+        return e
+
+    def record(self, e, stream):
+        self._check(self.hip.hipEventRecord(e, ctypes.c_void_p(stream)), "hipEventRecord")
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        self._check(self.hip.hipEventElapsedTime(ctypes.byref(out), a, b), "hipEventElapsedTime")
+        return float(out.value)
+
+    def close(self):
+        for e in self.events:
+            self.hip.hipEventDestroy(e)
+        self.events = []
+
+
 def measure(workload, nsets, K, W, event_every):
     """Time K steps (after W warm-up steps) of one workload's layer, weights rotating over
     `nsets` copies, with kernel events on every `event_every`-th step; parity of what is
@@ -469,33 +515,40 @@ def measure(workload, nsets, K, W, event_every):
     wts = torch.empty((shape.T, shape.k), dtype=torch.float32, device="cuda")
 
     # parity of what is timed: set 0, sampled tokens against the oracle on the GPU's routing
+    # (the output is kept here and checked on the host after the timed loops, so that no
+    # host-only work separates the warm-up from the timed steps)
     moe.forward(cfg, x, dev, ws, y=y, ids=ids, wts=wts, wst=wsts[0])
     torch.cuda.synchronize()
     g_ids = ids.cpu().numpy()
+    y_parity = y.float().cpu().numpy()
     U = int(np.unique(g_ids).size) + shape.S
-    rng = np.random.default_rng(0)
-    sample = np.arange(shape.T) if shape.T <= 16 else np.unique(
-        np.concatenate([[0, shape.T - 1], rng.choice(shape.T, 14, replace=False)]))
-    f = lambda t: None if t is None else (t.numpy() if t.dtype.itemsize == 1 else t.float().numpy())
-    ex = oracle_experts(mo, cpu, f)
-    l64 = mo.router_logits(f(cpu["x"]), f(cpu["w_router"]), f(cpu["router_bias"]))
-    w64 = mo.renormalise(mo.gate_scores(l64[sample]), g_ids[sample])
-    ref = mo.forward_tokenmajor(f(cpu["x"])[sample], ex, g_ids[sample], w64)
-    err = mo.rel_l2(y.float().cpu().numpy()[sample], ref)
-    log(f"parity on {len(sample)} tokens: rel_l2 {err:.3e}; unique experts {U}")
+
+    # The GPU's clocks follow its load: after host-only work it runs the first steps
+    # slower for a while (a 20-step prefill timing after 5 warm-up steps read 9% slow).
+    # So before the warm-up steps the layer runs back to back for SETTLE_S seconds;
+    # these runs are reported ("settle") and are neither warm-up nor timed steps.
+    t_settle, n_settle = time.time(), 0
+    while time.time() - t_settle < SETTLE_S:
+        for i in range(8):
+            moe.forward(cfg, x, None, ws, y=y, wst=wsts[i % nsets])
+        torch.cuda.synchronize()
+        n_settle += 8
+    t_settle = time.time() - t_settle
 
     for i in range(W):
         moe.forward(cfg, x, None, ws, y=y, wst=wsts[i % nsets])
     # start/stop events attached to the gate/up and down kernel dispatches of every
     # n-th timed step (each attached event costs a few microseconds of queue time)
     every = max(1, event_every)
-    timed = list(range(0, K, every))
-    ev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(moe.TIMED_EVENTS)] for i in timed}
+    timed = list(range(every - 1, K, every)) or [K - 1]     # the last of every `every` steps
+    hipt = HipTimer()
+    stream = torch.cuda.current_stream().cuda_stream
+    ev = {i: [hipt.event() for _ in range(moe.TIMED_EVENTS)] for i in timed}
     for row in ev.values():
         for e in row:
-            e.record()
+            hipt.record(e, stream)
     torch.cuda.synchronize()
-    arrays = {i: (ctypes.c_void_p * moe.TIMED_EVENTS)(*[e.cuda_event for e in row])
+    arrays = {i: (ctypes.c_void_p * moe.TIMED_EVENTS)(*[e.value for e in row])
               for i, row in ev.items()}
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -508,8 +561,8 @@ def measure(workload, nsets, K, W, event_every):
     end.record()
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / K
-    samples = {"gateup": [r[0].elapsed_time(r[1]) for r in ev.values()],
-               "down": [r[2].elapsed_time(r[3]) for r in ev.values()]}
+    samples = {"gateup": [hipt.ms(r[0], r[1]) for r in ev.values()],
+               "down": [hipt.ms(r[2], r[3]) for r in ev.values()]}
     kern_ms = {n: float(np.mean(v)) for n, v in samples.items()}
     kern_pct = {n: [round(float(np.percentile(v, q)) * 1e3, 2) for q in (10, 50, 90)]
                 for n, v in samples.items()}
@@ -522,17 +575,27 @@ def measure(workload, nsets, K, W, event_every):
     ms_plain = start.elapsed_time(end) / K
     # the spread over single steps: up to 100 more steps, each between its own event pair
     n1 = min(K, 100)
-    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for _ in range(n1)]
+    pairs = [(hipt.event(), hipt.event()) for _ in range(n1)]
     for i, (a, b) in enumerate(pairs):
-        a.record()
+        hipt.record(a, stream)
         moe.forward(cfg, x, None, ws, y=y, wst=wsts[i % nsets])
-        b.record()
+        hipt.record(b, stream)
     torch.cuda.synchronize()
-    step_us = [a.elapsed_time(b) * 1e3 for a, b in pairs]
+    step_us = [hipt.ms(a, b) * 1e3 for a, b in pairs]
+    hipt.close()
     step_pct = [round(float(np.percentile(step_us, q)), 2) for q in (10, 50, 90)]
     log(f"step {ms_per_step * 1e3:.2f} us (untimed kernels {ms_plain * 1e3:.2f} us); kernels: "
         + ", ".join(f"{n} {v * 1e3:.2f} us" for n, v in kern_ms.items()))
+    rng = np.random.default_rng(0)
+    sample = np.arange(shape.T) if shape.T <= 16 else np.unique(
+        np.concatenate([[0, shape.T - 1], rng.choice(shape.T, 14, replace=False)]))
+    f = lambda t: None if t is None else (t.numpy() if t.dtype.itemsize == 1 else t.float().numpy())
+    ex = oracle_experts(mo, cpu, f)
+    l64 = mo.router_logits(f(cpu["x"]), f(cpu["w_router"]), f(cpu["router_bias"]))
+    w64 = mo.renormalise(mo.gate_scores(l64[sample]), g_ids[sample])
+    ref = mo.forward_tokenmajor(f(cpu["x"])[sample], ex, g_ids[sample], w64)
+    err = mo.rel_l2(y_parity[sample], ref)
+    log(f"parity on {len(sample)} tokens: rel_l2 {err:.3e}; unique experts {U}")
     tokens_per_s = shape.T / (ms_per_step * 1e-3)
     which = max(kern_ms, key=kern_ms.get)
     roof = kernel_roofline(shape, which, kern_ms[which], U)
@@ -550,6 +613,7 @@ def measure(workload, nsets, K, W, event_every):
         "kernel_us": {n: round(v * 1e3, 2) for n, v in kern_ms.items()},
         "kernel_us_p10_p50_p90": kern_pct,
         "kernel_events_on_steps": f"every {every}th ({len(timed)} of {K})",
+        "settle": {"seconds": round(t_settle, 3), "runs": n_settle},
         "ms_per_step_without_kernel_events": round(ms_plain, 5),
         "step_us_p10_p50_p90": step_pct,
         "step_us_samples": f"{n1} single steps, one event pair each",
@@ -688,7 +752,7 @@ def main():
                             min(args.warmup, 10), args.event_every)
         res["prefill_leg"] = {k: leg[k] for k in (
             "value", "unit", "ms_per_step", "steps", "warmup", "config", "kernel_us",
-            "ms_per_step_without_kernel_events", "step_us_p10_p50_p90", "parity_rel_l2",
+            "ms_per_step_without_kernel_events", "step_us_p10_p50_p90", "settle", "parity_rel_l2",
             "roofline", "step_roofline")}
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(shape, cpu, args.cpu_seconds)

@@ -289,7 +289,8 @@ def forward_residual(cfg, x, norm_weight, weights: dict, ws, x_out: Optional[tor
 def forward_timed(cfg, x, wst: MoeWeights, ws, y, events_array) -> None:
     """moe_forward with start/stop events attached to the gate/up and down kernel
     dispatches.  `events_array` is a ctypes array of MOE_TIMED_EVENTS hipEvent_t
-    handles (torch.cuda.Event(enable_timing=True).cuda_event)."""
+    handles (timing events: torch.cuda.Event(enable_timing=True).cuda_event, or events
+    created with hipEventDisableSystemFence, as bench.py does)."""
     _check(load_library().moe_forward_timed(ctypes.byref(cfg), _ptr(x), ctypes.byref(wst), _ptr(y),
                                             None, None, _ptr(ws), ws.numel(), _stream(),
                                             events_array))
