@@ -30,6 +30,8 @@ SEQUENCES = [
     [("fp8", 130), ("fp8", 16)],                     # block-FP8 experts
     [("tiny", 300), ("tiny", 16)],                   # fp32 layer
     [("decode_nvfp4", 9), ("decode_nvfp4", 4)],      # NVFP4 decode kernels
+    [("decode_mxfp4", 12), ("decode_mxfp4", 3)],     # MXFP4 decode kernels
+    [("prefill_mxfp4", 300), ("prefill_mxfp4", 40)], # block-scaled matrix-core experts
 ]
 
 
