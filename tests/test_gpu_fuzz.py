@@ -1,7 +1,8 @@
 """Seeded randomized shapes through the whole layer and the decoder step: 24 valid
 configurations drawn once from a fixed seed across every expert type (fp32, bf16, block
 FP8, NVFP4), grouped and ungrouped routers, shared experts and token counts from 1 to
-300, plus 16 few-token draws, each checked against the oracle at the layer's bar.  The draw only picks sizes
+300, plus 16 few-token draws and 12 MXFP4 draws, each checked against the oracle at the
+layer's bar.  The draw only picks sizes
 within the documented limits; nothing here is meant to fail."""
 import numpy as np
 import pytest
@@ -61,7 +62,27 @@ def _draw_decode_cases(n=16, seed=2025):
     return cases
 
 
-CASES = _draw_cases() + _draw_decode_cases()
+def _draw_mx_cases(n=12, seed=2026):
+    """MXFP4 experts (H a multiple of 256, I of 128): token counts on both sides of the
+    16-token switch between the decode kernels and the block-scaled matrix-core path."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        H = int(rng.choice([256 * m for m in range(1, 9)]))
+        I = int(rng.choice([128 * m for m in range(1, 9)]))
+        E = int(rng.choice([16, 32, 64, 128, 256]))
+        G = int(rng.choice([g for g in (1, 2, 4, 8) if E // g >= 2]))
+        n_per = E // G
+        Gk = int(rng.integers(1, G + 1))
+        k = int(rng.integers(1, min(16, Gk * n_per) + 1))
+        S = int(rng.choice([0, 0, 1, 2]))
+        T = int(rng.choice([1, 3, 5, 16, 17, 40, 130, 300]))
+        cases.append((f"fzm{i}_mxfp4", T, H, I, E, G, Gk, k, S, "bf16", "mxfp4",
+                      "rms" if i % 2 else "normal", float(rng.choice([0.0, 0.3])), 5000 + i))
+    return cases
+
+
+CASES = _draw_cases() + _draw_decode_cases() + _draw_mx_cases()
 
 
 @pytest.fixture(scope="module")
