@@ -1177,6 +1177,277 @@ void k_gemm_fp8_v2(GemmFp8Args p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Block FP8 down projection, persistent.  The same tile, ring, MFMA steps and
+// epilogues as k_gemm_fp8_v2<false>, but one workgroup per CU walks a run of items, so
+// that a tile's first two slabs are loaded while the previous tile's epilogue runs.
+// Phase stamps of the one-tile-per-workgroup kernels put 23% of a gate/up tile's time
+// in its prologue (the set-up loads, then the first slabs' latency) and 19% in its
+// epilogue, with one workgroup per CU and nothing else to overlap them; with K = I
+// (four 128-deep slabs per tile) the down tile is dominated by them (47.5 -> 43 us on
+// the 2048-token layer), while the gate/up tile's twelve slabs leave the persistent
+// form no gain (67.9 against 66.2 us), so gate/up keeps k_gemm_fp8_v2.
+// Items: the n = tiles x column blocks of the launch (tile-major) are split into 8
+// contiguous runs, one per XCD (workgroup b runs on XCD b % 8), and the P workgroups
+// of an XCD take items q, q + P, q + 2P, ... of their run, so the items in flight on
+// an XCD at any time are neighbours, as the hardware's in-order dispatch would have
+// them.  The scales ride in the ring: with each slab, waves 0-1 load the 128 rows'
+// activation scales and the other waves the slab's weight block scales (4-byte
+// direct-to-LDS loads), so every wait counts the same L + 1 loads per slab.
+__global__ __launch_bounds__(Fp8Tile::NT) __attribute__((amdgpu_waves_per_eu(2)))
+void k_gemm_fp8_down_p(GemmFp8Args p) {
+  using C = Fp8Tile;
+  constexpr int BM = C::BM, BN = C::BN, W = C::W, WM = C::WM, WN = C::WN, MI = C::MI, NI = C::NI;
+  constexpr int AJ = C::AJ, BJ = C::BJ, L = C::L + 1, NT = C::NT;
+  __shared__ uint4 smem[C::RING_U4];
+  __shared__ float sa_r[3][BM];          // activation scales of the slab in each ring slot
+  __shared__ float sw_r[3][2];           // weight block scales of the slab in each ring slot
+  const int ncol = p.N / BN;
+  const int n = p.meta[1] * ncol;
+  const int per = (n + 7) >> 3;
+  const int run0 = int(blockIdx.x & 7) * per, q0 = int(blockIdx.x >> 3), P = int(gridDim.x >> 3);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar registers)
+  const int wm = wv / WN, wn = wv % WN;
+  const int64_t K = p.K;
+  const int nk = int(K / C::KB);
+  const int64_t mst = int64_t(p.N) * K;                // bytes of one expert matrix
+  const int64_t sst = int64_t(p.N / 128) * nk;         // block scales of one expert matrix
+  // Workgroup barrier for LDS hand-offs: waits for this wave's LDS operations only, not
+  // for its global loads (the next item's slabs stay in flight across the epilogue's
+  // barriers) nor its stores.
+  auto lds_sync = [] {
+    wait_vm_lgkm0<63>();
+    block_sync_nowait();
+  };
+  auto item_of = [&](int tau, int& tile, int& ct) {
+    const int q = q0 + P * tau, j = run0 + q;
+    if (q >= per || j >= n) return false;
+    tile = j / ncol;
+    ct = j - tile * ncol;
+    return true;
+  };
+
+  // ------------------------------------------------------------- issue side
+  const uint8_t* ag[AJ];
+  const uint8_t* bbase[BJ];                             // weight matrix of each load (wave-uniform)
+  uint32_t boff[BJ];                                    // this lane's byte offset in it
+  const float* scs;                                     // this lane's scale source (+ kt)
+  int src_m0, src_base, src_cnt;                        // the item's rows
+  auto set_source = [&](int tile, int ct) {
+    const int2 te = p.tiles[tile];
+    const int e = te.x, m0 = te.y;
+    const int base = p.offsets[e];
+    const int cnt = p.offsets[e + 1] - base;
+    src_m0 = m0;
+    src_base = base;
+    src_cnt = cnt;
+    auto arow_of = [&](int r) {
+      const int m = min(m0 + r, cnt - 1);
+      return int64_t(base + m);
+    };
+#pragma unroll
+    for (int i = 0; i < AJ; ++i) {
+      const int r = 8 * (wv + W * i) + (lane >> 3);
+      ag[i] = p.a + arow_of(r) * K + dma_chunk(lane, wv + W * i) * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < BJ; ++i) {
+      const int r0 = 8 * (wv + W * i), r = r0 + (lane >> 3);   // a load's rows: r0 .. r0+7
+      const int c = dma_chunk(lane, wv + W * i) * 16;
+      bbase[i] = expert_mat(p.w0, p.sh0, e, p.E, mst);
+      boff[i] = uint32_t((ct * BN + r) * K + c);
+    }
+    if (wv < 2) {
+      scs = p.a_scale + arow_of(wv * 64 + lane) * nk;
+    } else {
+      // the two 128-row scale blocks 2ct, 2ct+1 of the tile's 256 output columns
+      scs = expert_mat(p.s0, p.shs0, e, p.E, sst) + int64_t(2 * ct + (lane & 1)) * nk;
+    }
+  };
+  auto issue = [&](int kt, int slot) {
+    const int64_t ko = int64_t(kt) * C::KB;
+    uint4* sa = smem + slot * C::STAGE_U4;
+    uint4* sb = sa + C::A_U4;
+#pragma unroll
+    for (int i = 0; i < AJ; ++i) dma16(ag[i] + ko, sa + (wv + W * i) * 64);
+#pragma unroll
+    for (int i = 0; i < BJ; ++i) dma16(bbase[i] + (boff[i] + ko), sb + (wv + W * i) * 64);
+    if (wv < 2) {
+      dma4(scs + kt, &sa_r[slot][wv * 64]);
+    } else if (lane < 2) {
+      dma4(scs + kt, &sw_r[slot][0]);
+    }
+  };
+
+  // ------------------------------------------------------------- compute side
+  auto wrow = [&](int b) { return wn * (BN / WN) + b * 32 + (lane & 31); };
+  const int swb0 = (wn * (BN / WN)) / 128;            // scale block of this wave's weight rows
+  f32x16 acc[MI][NI];
+  auto compute = [&](int slot, auto&& between) {
+    const uint4* sa = smem + slot * C::STAGE_U4;
+    const uint4* sb = sa + C::A_U4;
+    i32x8 af[2][MI], bfr[2][NI];
+    auto frags = [&](int ks, i32x8 (&xa)[MI], i32x8 (&xb)[NI]) {
+      const int c0 = ks * 4 + (lane >> 5) * 2;
+#pragma unroll
+      for (int a = 0; a < MI; ++a) {
+        const int row = wm * (BM / WM) + a * 32 + (lane & 31);
+        const uint4 lo = sa[swz16(row, c0)], hi = sa[swz16(row, c0 + 1)];
+        xa[a] = i32x8{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+      }
+#pragma unroll
+      for (int b = 0; b < NI; ++b) {
+        const int row = wrow(b);
+        const uint4 lo = sb[swz16(row, c0)], hi = sb[swz16(row, c0 + 1)];
+        xb[b] = i32x8{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+      }
+    };
+    frags(0, af[0], bfr[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    between();
+    frags(1, af[1], bfr[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    float sact[MI], swt[NI];
+#pragma unroll
+    for (int a = 0; a < MI; ++a) sact[a] = sa_r[slot][wm * (BM / WM) + a * 32 + (lane & 31)];
+#pragma unroll
+    for (int b = 0; b < NI; ++b) swt[b] = sw_r[slot][swb0];
+#pragma unroll
+    for (int a = 0; a < MI; ++a)
+#pragma unroll
+      for (int b = 0; b < NI; ++b) {
+        f32x16 sl;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sl[r] = 0.f;
+        sl = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[0][b], af[0][a], sl, 0, 0, 0, 127, 0, 127);
+        sl = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[1][b], af[1][a], sl, 0, 0, 0, 127, 0, 127);
+        const float s = sact[a] * swt[b];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[a][b][r] = fmaf(sl[r], s, acc[a][b][r]);
+      }
+  };
+
+  int tile, ct;
+  if (!item_of(0, tile, ct)) return;
+  set_source(tile, ct);
+  issue(0, 0);
+  if (nk > 1) issue(1, 1);
+  for (int tau = 0;; ++tau) {
+    const int m0 = src_m0, base = src_base, cnt = src_cnt;
+#pragma unroll
+    for (int a = 0; a < MI; ++a)
+#pragma unroll
+      for (int b = 0; b < NI; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+    // Every item runs its ring from slot 0 (slab kt in slot kt % 3, slots fixed at
+    // compile time by the unrolled steps).  After an epilogue its stores are in the
+    // count too, so an item's first step waits for everything.
+#define MOE_F8P_STEP(KT, SLOT, NSLOT)                                                      \
+    {                                                                                      \
+      if ((KT) + 1 < nk && !((KT) == 0 && tau > 0)) wait_vm_lgkm0<L>(); else wait_vm_lgkm0<0>(); \
+      block_sync_nowait();                                                                 \
+      compute(SLOT, [&] { if ((KT) + 2 < nk) issue((KT) + 2, NSLOT); });                   \
+    }
+    for (int kt = 0; kt < nk; kt += 3) {
+      MOE_F8P_STEP(kt, 0, 2)
+      if (kt + 1 < nk) MOE_F8P_STEP(kt + 1, 1, 0)
+      if (kt + 2 < nk) MOE_F8P_STEP(kt + 2, 2, 1)
+    }
+#undef MOE_F8P_STEP
+    // The next item's set-up loads are waited for here, where no slab is in flight, by
+    // each wave before the barrier; once every wave has passed it the whole ring is
+    // free: the next item's first two slabs go into slots 0 and 1 and the epilogue
+    // stages through slot 2 while they land.
+    const int cur_ct = ct;
+    // down, weighted output: this wave's row weights, loaded before the next item's
+    // slabs are issued (a load waited for in the epilogue would wait for them too)
+    float wrv[MI];
+#pragma unroll
+    for (int a = 0; a < MI; ++a) {
+      const int row = wm * (BM / WM) + a * 32 + (lane & 31);
+      wrv[a] = (p.out32 || row >= cnt - m0) ? 0.f : p.row_w[base + m0 + row];
+    }
+    const bool more = item_of(tau + 1, tile, ct);
+    if (more) set_source(tile, ct);
+    wait_vm_lgkm0<0>();   // those loads have landed before any slab load is issued behind them
+    lds_sync();
+    if (more) {
+      issue(0, 0);
+      if (nk > 1) issue(1, 1);
+    }
+    const int rows = min(BM, cnt - m0);
+    unsigned char* stage = reinterpret_cast<unsigned char*>(smem + 2 * C::STAGE_U4);
+    if (p.out32) {
+#pragma unroll
+      for (int a = 0; a < MI; ++a) {
+        const int row = wm * (BM / WM) + a * 32 + (lane & 31);
+        if (row >= rows) continue;
+#pragma unroll
+        for (int b = 0; b < NI; ++b)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int col = cur_ct * BN + wn * (BN / WN) + b * 32 + 8 * g4 + 4 * (lane >> 5);
+            *reinterpret_cast<float4*>(p.out32 + int64_t(base + m0 + row) * p.N + col) =
+                make_float4(acc[a][b][4 * g4], acc[a][b][4 * g4 + 1], acc[a][b][4 * g4 + 2],
+                            acc[a][b][4 * g4 + 3]);
+          }
+      }
+    } else {
+      // weighted bf16 rows through LDS, one 64-row half of the tile at a time (the
+      // staging slot holds 48 KB): each register group is 4 consecutive columns
+      constexpr int LS = BN + 8;
+      bf16_t* stg = reinterpret_cast<bf16_t*>(stage);
+#pragma unroll
+      for (int half = 0; half < WM; ++half) {
+        if (wm == half) {
+#pragma unroll
+          for (int a = 0; a < MI; ++a) {
+            const int lrow = a * 32 + (lane & 31);
+            const float wr = wrv[a];
+#pragma unroll
+            for (int b = 0; b < NI; ++b)
+#pragma unroll
+              for (int g4 = 0; g4 < 4; ++g4) {
+                const int col = wn * (BN / WN) + b * 32 + 8 * g4 + 4 * (lane >> 5);
+                uint2 pk;
+                pk.x = uint32_t(f32_to_bf16(acc[a][b][4 * g4] * wr)) |
+                       (uint32_t(f32_to_bf16(acc[a][b][4 * g4 + 1] * wr)) << 16);
+                pk.y = uint32_t(f32_to_bf16(acc[a][b][4 * g4 + 2] * wr)) |
+                       (uint32_t(f32_to_bf16(acc[a][b][4 * g4 + 3] * wr)) << 16);
+                *reinterpret_cast<uint2*>(stg + lrow * LS + col) = pk;
+              }
+          }
+        }
+        lds_sync();
+        const int hrows = min(BM / WM, rows - half * (BM / WM));
+        for (int i = tid; i < hrows * (BN / 8); i += NT) {
+          const int lrow = i / (BN / 8), c = i - lrow * (BN / 8);
+          *reinterpret_cast<uint4*>(p.out16 + int64_t(base + m0 + half * (BM / WM) + lrow) * p.N +
+                                    cur_ct * BN + c * 8) =
+              *reinterpret_cast<const uint4*>(stg + lrow * LS + c * 8);
+        }
+        if (half + 1 < WM) lds_sync();
+      }
+    }
+    if (!more) break;
+  }
+}
+
+// Grid of the persistent block-FP8 down kernel: one workgroup per CU, a multiple of the
+// 8 XCDs.
+static int fp8_persistent_grid(unsigned* grid) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    check_launch();
+    return MOE_ERR_HIP;
+  }
+  *grid = unsigned(std::max(8, cus / 8 * 8));
+  return MOE_OK;
+}
+
 // shapes the pipelined fp8 kernels cover
 static bool fp8_pipelined_ok(const Plan& p) {
   return p.wt == MOE_E4M3_B128 && p.I % 128 == 0 && p.H % Fp8Tile::BN == 0 &&
@@ -1294,11 +1565,13 @@ int launch_down_mfma(const Plan& p, const void* h, const int32_t* offsets, const
     a.meta = meta; a.w0 = (const uint8_t*)w->w_down; a.sh0 = (const uint8_t*)w->sh_down;
     a.s0 = w->s_down; a.shs0 = w->sh_s_down; a.row_w = row_w; a.out16 = out16; a.out32 = out32;
     a.K = p.I; a.N = p.H; a.E = p.E;
-    if (fp8_pipelined_ok(p))
-      launch_kernel(p, kTimeDown, k_gemm_fp8_v2<false>,
-                    dim3(xcd_grid(p.max_tiles * (p.H / Fp8Tile::BN))), dim3(Fp8Tile::NT), 0, st, a);
-    else
+    if (fp8_pipelined_ok(p)) {
+      unsigned pg = 0;
+      MOE_TRY(fp8_persistent_grid(&pg));
+      launch_kernel(p, kTimeDown, k_gemm_fp8_down_p, dim3(pg), dim3(Fp8Tile::NT), 0, st, a);
+    } else {
       launch_kernel(p, kTimeDown, k_gemm_fp8<false>, dim3(grid), dim3(256), 0, st, a);
+    }
   }
   return check_launch();
 }

@@ -33,6 +33,16 @@ __device__ __forceinline__ void dma16(const void* g, void* lds) {
       : "s"(m0), "v"(g)
       : "memory");
 }
+// The same for 4 bytes per lane (global_load_lds_dword): lane L writes lds + 4 L.
+__device__ __forceinline__ void dma4(const void* g, void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>((lvoid_t*)lds)));
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0), "v"(g)
+      : "memory");
+}
 // s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4]<<14)
 template <int N>
 __device__ __forceinline__ void wait_vm_lgkm0() {
