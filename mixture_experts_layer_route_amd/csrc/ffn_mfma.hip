@@ -700,9 +700,10 @@ static int persistent_grid(unsigned* grid) {
 // tiles as k_gemm_fp8_down_p does.  Each tile's ring starts at slot 0 (static slots);
 // once every wave is past the K loop the next tile's first two slabs go into slots
 // 0-1 and the epilogue stages its weighted rows through slot 2, in two 64-row halves,
-// while they land.  The tile's row weights and the next tile's set-up loads are waited
-// for before those slabs are issued, and the epilogue's barriers wait for LDS only, so
-// nothing waits for the slabs in flight.
+// while they land.  The next tile's set-up loads run during the K loop and its row
+// weights arrive in LDS with its first slab, so nothing after the K loop waits for
+// memory, and the epilogue's barriers wait for LDS only, so nothing waits for the
+// slabs in flight.
 __global__ __launch_bounds__(BfCfg::NT) __attribute__((amdgpu_waves_per_eu(BfCfg::WPE)))
 void k_gemm_bf16_down_p(GemmBf16Args p) {
   using C = BfCfg;
@@ -711,6 +712,8 @@ void k_gemm_bf16_down_p(GemmBf16Args p) {
   constexpr int L = C::L, NT = C::NT, KS = BK / 16;
   static_assert(KS % 2 == 0, "fragment double buffer");
   __shared__ uint4 smem[C::RING_U4];
+  __shared__ __align__(16) float rw_l[BM];                   // the tile's row weights
+  const bool weighted = p.out32 == nullptr;
   const int ncol = p.N / BN;
   const int n = p.meta[1] * ncol;
   const int per = (n + 7) >> 3;
@@ -738,11 +741,7 @@ void k_gemm_bf16_down_p(GemmBf16Args p) {
   const bf16_t* wbase;                                       // the tile's expert matrix
   uint32_t boff[BJ];                                         // this lane's element offsets in it
   int src_m0, src_base, src_cnt;
-  auto set_source = [&](int tile, int ct) {
-    const int2 te = p.tiles[tile];
-    const int e = te.x, m0 = te.y;
-    const int base = p.offsets[e];
-    const int cnt = p.offsets[e + 1] - base;
+  auto set_source = [&](int e, int m0, int base, int cnt, int ct) {
     src_m0 = m0;
     src_base = base;
     src_cnt = cnt;
@@ -767,6 +766,17 @@ void k_gemm_bf16_down_p(GemmBf16Args p) {
     for (int i = 0; i < AJ; ++i) dma16(ag[i] + ko, sa + (wv + W * i) * 64);
 #pragma unroll
     for (int i = 0; i < BJ; ++i) dma16(wbase + (boff[i] + ko), sb + (wv + W * i) * 64);
+  };
+  // the row weights of the tile set_source chose, into rw_l by wave 0 (rows past the
+  // expert's last read its last row; the epilogue zeroes them); issued between slab 0
+  // and slab 1, so slab 0's wait covers them
+  auto issue_roww = [&] {
+    if (weighted && wv == 0) {
+      const float* rw = p.row_w + src_base + src_m0;
+      const int last = src_cnt - src_m0 - 1;
+#pragma unroll
+      for (int h = 0; h < BM / 64; ++h) dma4(rw + min(h * 64 + lane, last), rw_l + h * 64);
+    }
   };
 
   f32x16 acc[MI][NI];
@@ -800,11 +810,24 @@ void k_gemm_bf16_down_p(GemmBf16Args p) {
 
   int tile, ct;
   if (!item_of(0, tile, ct)) return;
-  set_source(tile, ct);
+  {
+    const int2 te = p.tiles[tile];
+    const int b = p.offsets[te.x];
+    set_source(te.x, te.y, b, p.offsets[te.x + 1] - b, ct);
+  }
   issue(0, 0);
+  issue_roww();
   if (nk > 1) issue(1, 1);
   for (int tau = 0;; ++tau) {
     const int m0 = src_m0, base = src_base, cnt = src_cnt;
+    // the next tile's set-up: its table entry now (the first step's wait covers it),
+    // its expert's row range after the first step, so that none of it is waited for
+    // after the K loop
+    int tile_n = 0, ct_n = 0;
+    const bool more = item_of(tau + 1, tile_n, ct_n);
+    int2 te_n = make_int2(0, 0);
+    if (more) te_n = p.tiles[tile_n];
+    int base_n = 0, end_n = 0;
 #pragma unroll
     for (int a = 0; a < MI; ++a)
 #pragma unroll
@@ -821,28 +844,39 @@ void k_gemm_bf16_down_p(GemmBf16Args p) {
     }
     for (int kt = 0; kt < nk; kt += 3) {
       MOE_BFP_STEP(kt, 0, 2)
+      if (kt == 0 && more) {
+        base_n = p.offsets[te_n.x];
+        end_n = p.offsets[te_n.x + 1];
+      }
       if (kt + 1 < nk) MOE_BFP_STEP(kt + 1, 1, 0)
       if (kt + 2 < nk) MOE_BFP_STEP(kt + 2, 2, 1)
     }
 #undef MOE_BFP_STEP
     const int cur_ct = ct;
     const int rows = min(BM, cnt - m0);
-    // this lane's row weights (accumulator rows), then the next tile's set-up, both
-    // waited for while no slab is in flight
+    // this lane's row weights (accumulator rows: four consecutive rows per 16-byte read)
     float roww[MI][16];
 #pragma unroll
     for (int a = 0; a < MI; ++a)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wm * (BM / WM) + a * 32 + acc_row(r, lane);
-        roww[a][r] = (p.out32 || row >= rows) ? 0.f : p.row_w[base + m0 + row];
+      for (int g = 0; g < 4; ++g) {
+        const int row0 = wm * (BM / WM) + a * 32 + 8 * g + 4 * (lane >> 5);
+        const float4 v = weighted ? *reinterpret_cast<const float4*>(rw_l + row0) : make_float4(0.f, 0.f, 0.f, 0.f);
+        roww[a][4 * g + 0] = row0 + 0 < rows ? v.x : 0.f;
+        roww[a][4 * g + 1] = row0 + 1 < rows ? v.y : 0.f;
+        roww[a][4 * g + 2] = row0 + 2 < rows ? v.z : 0.f;
+        roww[a][4 * g + 3] = row0 + 3 < rows ? v.w : 0.f;
       }
-    const bool more = item_of(tau + 1, tile, ct);
-    if (more) set_source(tile, ct);
+    if (more) {
+      tile = tile_n;
+      ct = ct_n;
+      set_source(te_n.x, te_n.y, base_n, end_n - base_n, ct_n);
+    }
     wait_vm_lgkm0<0>();
-    lds_sync();                      // every wave is past the K loop: the whole ring is free
+    lds_sync();                      // every wave is past the K loop and has its row weights
     if (more) {
       issue(0, 0);
+      issue_roww();
       if (nk > 1) issue(1, 1);
     }
     if (p.out32) {
