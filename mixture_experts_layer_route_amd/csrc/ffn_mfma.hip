@@ -44,6 +44,7 @@ struct GemmBf16Args {
   bf16_t* out16;              // gate/up: h [R, I]; down: weighted y_perm [R, H]
   float* out32;               // down: unweighted y_perm [R, H]
   int K, N, E;                // K: reduction length; N: output width (I for h, H for y)
+  int ES;                     // routed + shared experts (offsets holds ES + 1 entries)
 };
 
 template <bool GATEUP>
@@ -234,6 +235,9 @@ struct BfTile {
 #define MOE_BF_WN 4
 #endif
 using BfCfg = BfTile<MOE_BF_BM, MOE_BF_BN, MOE_BF_BK, MOE_BF_WM, MOE_BF_WN>;
+// largest number of routed + shared experts a layer may have (the persistent bf16 down
+// kernel keeps the expert row offsets in LDS)
+#define MOE_MAX_ES 1024
 // the NVFP4 kernel's tile (its per-thread conversion layout is built for this shape)
 using Nv4Cfg = BfTile<128, 256, 64, 2, 4>;
 
@@ -713,6 +717,7 @@ void k_gemm_bf16_down_p(GemmBf16Args p) {
   static_assert(KS % 2 == 0, "fragment double buffer");
   __shared__ uint4 smem[C::RING_U4];
   __shared__ __align__(16) float rw_l[BM];                   // the tile's row weights
+  __shared__ int offs_l[MOE_MAX_ES + 1];  // expert row offsets
   const bool weighted = p.out32 == nullptr;
   const int ncol = p.N / BN;
   const int n = p.meta[1] * ncol;
@@ -810,24 +815,25 @@ void k_gemm_bf16_down_p(GemmBf16Args p) {
 
   int tile, ct;
   if (!item_of(0, tile, ct)) return;
+  for (int i = tid; i <= p.ES; i += NT) offs_l[i] = p.offsets[i];
+  __syncthreads();
   {
     const int2 te = p.tiles[tile];
-    const int b = p.offsets[te.x];
-    set_source(te.x, te.y, b, p.offsets[te.x + 1] - b, ct);
+    const int b = __builtin_amdgcn_readfirstlane(offs_l[te.x]);
+    set_source(te.x, te.y, b, __builtin_amdgcn_readfirstlane(offs_l[te.x + 1]) - b, ct);
   }
   issue(0, 0);
   issue_roww();
   if (nk > 1) issue(1, 1);
   for (int tau = 0;; ++tau) {
     const int m0 = src_m0, base = src_base, cnt = src_cnt;
-    // the next tile's set-up: its table entry now (the first step's wait covers it),
-    // its expert's row range after the first step, so that none of it is waited for
-    // after the K loop
+    // the next tile's table entry, loaded now (the first step's wait covers it); its
+    // expert's row range comes from LDS, so none of the set-up waits for memory after
+    // the K loop
     int tile_n = 0, ct_n = 0;
     const bool more = item_of(tau + 1, tile_n, ct_n);
     int2 te_n = make_int2(0, 0);
     if (more) te_n = p.tiles[tile_n];
-    int base_n = 0, end_n = 0;
 #pragma unroll
     for (int a = 0; a < MI; ++a)
 #pragma unroll
@@ -844,10 +850,6 @@ void k_gemm_bf16_down_p(GemmBf16Args p) {
     }
     for (int kt = 0; kt < nk; kt += 3) {
       MOE_BFP_STEP(kt, 0, 2)
-      if (kt == 0 && more) {
-        base_n = p.offsets[te_n.x];
-        end_n = p.offsets[te_n.x + 1];
-      }
       if (kt + 1 < nk) MOE_BFP_STEP(kt + 1, 1, 0)
       if (kt + 2 < nk) MOE_BFP_STEP(kt + 2, 2, 1)
     }
@@ -870,7 +872,8 @@ void k_gemm_bf16_down_p(GemmBf16Args p) {
     if (more) {
       tile = tile_n;
       ct = ct_n;
-      set_source(te_n.x, te_n.y, base_n, end_n - base_n, ct_n);
+      const int base_n = __builtin_amdgcn_readfirstlane(offs_l[te_n.x]);
+      set_source(te_n.x, te_n.y, base_n, __builtin_amdgcn_readfirstlane(offs_l[te_n.x + 1]) - base_n, ct_n);
     }
     wait_vm_lgkm0<0>();
     lds_sync();                      // every wave is past the K loop and has its row weights
@@ -1779,6 +1782,7 @@ int launch_down_mfma(const Plan& p, const void* h, const int32_t* offsets, const
     a.a = (const bf16_t*)h; a.offsets = offsets; a.tiles = tiles; a.meta = meta;
     a.w0 = (const bf16_t*)w->w_down; a.sh0 = (const bf16_t*)w->sh_down;
     a.row_w = row_w; a.out16 = out16; a.out32 = out32; a.K = p.I; a.N = p.H; a.E = p.E;
+    a.ES = p.E + p.S;
     // (k_gemm_bf16_v2<false> is the same tile one per workgroup; the persistent form
     // measured 153.3 against 160.9 us on the Inkling-shaped layer, equal on prefill)
     if (bf_pipelined_ok(p)) {
