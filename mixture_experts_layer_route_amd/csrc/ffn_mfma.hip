@@ -238,6 +238,9 @@ using BfCfg = BfTile<MOE_BF_BM, MOE_BF_BN, MOE_BF_BK, MOE_BF_WM, MOE_BF_WN>;
 // largest number of routed + shared experts a layer may have (the persistent bf16 down
 // kernel keeps the expert row offsets in LDS)
 #define MOE_MAX_ES 1024
+#ifndef MOE_BF_GU_PERSIST
+#define MOE_BF_GU_PERSIST 1
+#endif
 // the NVFP4 kernel's tile (its per-thread conversion layout is built for this shape)
 using Nv4Cfg = BfTile<128, 256, 64, 2, 4>;
 
@@ -924,6 +927,206 @@ void k_gemm_bf16_down_p(GemmBf16Args p) {
         }
         if (half + 1 < WM) lds_sync();
       }
+    }
+    if (!more) break;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 gate/up + SwiGLU, persistent: the tile, ring and MFMA steps of
+// k_gemm_bf16_v2<true> with the item walk of k_gemm_bf16_down_p (one workgroup per
+// CU over an XCD-contiguous run of items, static ring slots, the next item's first two
+// slabs loaded during the epilogue).  The activation rows are gathered through
+// row_token, so an item's set-up needs its 128 row tokens before its first slab can be
+// issued: for the next item they are fetched into LDS during the current item's
+// first step (4-byte direct-to-LDS loads by wave 0, issued ahead of slab 2, so the
+// second step's wait covers them), its table entry is loaded before the K loop and its
+// expert's row range comes from LDS, so nothing after the K loop waits for memory.
+// The h tile (128 rows x 128 columns) is staged through slot 2 in one pass.
+__global__ __launch_bounds__(BfCfg::NT) __attribute__((amdgpu_waves_per_eu(BfCfg::WPE)))
+void k_gemm_bf16_gateup_p(GemmBf16Args p) {
+  using C = BfCfg;
+  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, WM = C::WM, WN = C::WN, W = C::W;
+  constexpr int MI = C::MI, NI = C::NI, CH = C::CH, RPD = C::RPD, AJ = C::AJ, BJ = C::BJ;
+  constexpr int L = C::L, NT = C::NT, KS = BK / 16, OC = BN / 2;
+  static_assert(KS % 2 == 0, "fragment double buffer");
+  static_assert(BM * C::LSG * 2 <= C::STAGE_U4 * 16, "h tile staging fits one ring slot");
+  __shared__ uint4 smem[C::RING_U4];
+  __shared__ int rt_l[BM];                 // the next item's row tokens
+  __shared__ int offs_l[MOE_MAX_ES + 1];   // expert row offsets
+  const int ncol = p.N / OC;
+  const int n = p.meta[1] * ncol;
+  const int per = (n + 7) >> 3;
+  const int run0 = int(blockIdx.x & 7) * per, q0 = int(blockIdx.x >> 3), P = int(gridDim.x >> 3);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar registers)
+  const int wm = wv / WN, wn = wv % WN;
+  const int64_t K = p.K;
+  const int nk = int(K / BK);
+  const int64_t mst = int64_t(p.N) * K;                      // elements of one expert matrix
+  auto lds_sync = [] {
+    wait_vm_lgkm0<63>();
+    block_sync_nowait();
+  };
+  auto item_of = [&](int tau, int& tile, int& ct) {
+    const int q = q0 + P * tau, j = run0 + q;
+    if (q >= per || j >= n) return false;
+    tile = j / ncol;
+    ct = j - tile * ncol;
+    return true;
+  };
+
+  const bf16_t* ag[AJ];
+  const bf16_t* bbase[BJ];                                   // gate or up matrix (wave-uniform)
+  uint32_t boff[BJ];                                         // this lane's element offsets in it
+  int src_m0, src_base, src_cnt;
+  // rtok(r): the row token of the item's row r (rows past the expert's last repeat it)
+  auto set_source = [&](int e, int m0, int base, int cnt, int ct, auto&& rtok) {
+    src_m0 = m0;
+    src_base = base;
+    src_cnt = cnt;
+#pragma unroll
+    for (int i = 0; i < AJ; ++i) {
+      const int r = RPD * (wv + W * i) + lane / CH;
+      ag[i] = p.a + int64_t(rtok(r)) * K + C::dma_chunk(lane, wv + W * i) * 8;
+    }
+    const bf16_t* wg = expert_mat(p.w0, p.sh0, e, p.E, mst);
+    const bf16_t* wu = expert_mat(p.w1, p.sh1, e, p.E, mst);
+#pragma unroll
+    for (int i = 0; i < BJ; ++i) {
+      const int r0 = RPD * (wv + W * i), r = r0 + lane / CH;   // a load's rows: r0 .. r0+RPD-1
+      bbase[i] = r0 < OC ? wg : wu;
+      boff[i] = uint32_t((ct * OC + (r0 < OC ? r : r - OC)) * K + C::dma_chunk(lane, wv + W * i) * 8);
+    }
+  };
+  auto issue = [&](int kt, int slot) {
+    const int ko = kt * BK;
+    uint4* sa = smem + slot * C::STAGE_U4;
+    uint4* sb = sa + C::A_U4;
+#pragma unroll
+    for (int i = 0; i < AJ; ++i) dma16(ag[i] + ko, sa + (wv + W * i) * 64);
+#pragma unroll
+    for (int i = 0; i < BJ; ++i) dma16(bbase[i] + (boff[i] + ko), sb + (wv + W * i) * 64);
+  };
+
+  f32x16 acc[MI][NI];
+  auto load_frags = [&](const uint4* sa, const uint4* sb, int ks, bf16x8 (&af)[MI], bf16x8 (&bfr)[NI]) {
+    const int chunk = ks * 2 + (lane >> 5);
+#pragma unroll
+    for (int a = 0; a < MI; ++a)
+      af[a] = __builtin_bit_cast(bf16x8, sa[C::pos(wm * (BM / WM) + a * 32 + (lane & 31), chunk)]);
+#pragma unroll
+    for (int b = 0; b < NI; ++b) {
+      // blocks 0..NI/2-1 are gate columns, NI/2.. the matching up columns
+      const int row = (b < NI / 2 ? 0 : OC) + wn * (OC / WN) + (b % (NI / 2)) * 32 + (lane & 31);
+      bfr[b] = __builtin_bit_cast(bf16x8, sb[C::pos(row, chunk)]);
+    }
+  };
+  auto compute = [&](int slot, auto&& between) {
+    const uint4* sa = smem + slot * C::STAGE_U4;
+    const uint4* sb = sa + C::A_U4;
+    bf16x8 af[2][MI], bfr[2][NI];
+    load_frags(sa, sb, 0, af[0], bfr[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    between();
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) load_frags(sa, sb, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int a = 0; a < MI; ++a)
+#pragma unroll
+        for (int b = 0; b < NI; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][a], bfr[ks & 1][b], acc[a][b], 0, 0, 0);
+    }
+  };
+
+  int tile, ct;
+  if (!item_of(0, tile, ct)) return;
+  for (int i = tid; i <= p.ES; i += NT) offs_l[i] = p.offsets[i];
+  __syncthreads();
+  {
+    const int2 te = p.tiles[tile];
+    const int b = __builtin_amdgcn_readfirstlane(offs_l[te.x]);
+    const int c = __builtin_amdgcn_readfirstlane(offs_l[te.x + 1]) - b;
+    set_source(te.x, te.y, b, c, ct, [&](int r) { return p.row_token[b + min(te.y + r, c - 1)]; });
+  }
+  issue(0, 0);
+  if (nk > 1) issue(1, 1);
+  for (int tau = 0;; ++tau) {
+    const int m0 = src_m0, base = src_base, cnt = src_cnt;
+    // the next item's table entry, loaded now (the first step's wait covers it)
+    int tile_n = 0, ct_n = 0;
+    const bool more = item_of(tau + 1, tile_n, ct_n);
+    int2 te_n = make_int2(0, 0);
+    if (more) te_n = p.tiles[tile_n];
+    int base_n = 0, cnt_n = 0;
+    // the next item's row tokens into rt_l (wave 0), issued in the first step ahead of
+    // slab 2, so that the second step's wait covers them
+    auto issue_rt_next = [&] {
+      base_n = __builtin_amdgcn_readfirstlane(offs_l[te_n.x]);
+      cnt_n = __builtin_amdgcn_readfirstlane(offs_l[te_n.x + 1]) - base_n;
+      if (wv == 0) {
+        const int32_t* rt = p.row_token + base_n;
+        const int last = cnt_n - 1;
+#pragma unroll
+        for (int h = 0; h < BM / 64; ++h) dma4(rt + min(te_n.y + h * 64 + lane, last), rt_l + h * 64);
+      }
+    };
+#pragma unroll
+    for (int a = 0; a < MI; ++a)
+#pragma unroll
+      for (int b = 0; b < NI; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+    // slab kt in slot kt % 3; after an epilogue its stores are in the count too, so an
+    // item's first step waits for everything
+#define MOE_BGP_STEP(KT, SLOT, NSLOT)                                                      \
+    {                                                                                      \
+      if ((KT) + 1 < nk && !((KT) == 0 && tau > 0)) wait_vm_lgkm0<L>(); else wait_vm_lgkm0<0>(); \
+      block_sync_nowait();                                                                 \
+      compute(SLOT, [&] {                                                                  \
+        if ((KT) == 0 && more) issue_rt_next();                                            \
+        if ((KT) + 2 < nk) issue((KT) + 2, NSLOT);                                         \
+      });                                                                                  \
+    }
+    for (int kt = 0; kt < nk; kt += 3) {
+      MOE_BGP_STEP(kt, 0, 2)
+      if (kt + 1 < nk) MOE_BGP_STEP(kt + 1, 1, 0)
+      if (kt + 2 < nk) MOE_BGP_STEP(kt + 2, 2, 1)
+    }
+#undef MOE_BGP_STEP
+    const int cur_ct = ct;
+    const int rows = min(BM, cnt - m0);
+    wait_vm_lgkm0<0>();
+    lds_sync();                      // every wave is past the K loop; the row tokens have landed
+    if (more) {
+      tile = tile_n;
+      ct = ct_n;
+      set_source(te_n.x, te_n.y, base_n, cnt_n, ct_n, [&](int r) { return rt_l[r]; });
+      issue(0, 0);
+      if (nk > 1) issue(1, 1);
+    }
+    // h = silu(gate) * up through slot 2, so that each row leaves as whole 16-byte pieces
+    constexpr int LS = C::LSG;
+    bf16_t* stg = reinterpret_cast<bf16_t*>(smem + 2 * C::STAGE_U4);
+#pragma unroll
+    for (int a = 0; a < MI; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * (BM / WM) + a * 32 + acc_row(r, lane);
+#pragma unroll
+        for (int b = 0; b < NI / 2; ++b) {
+          const float g = acc[a][b][r], u = acc[a][b + NI / 2][r];
+          stg[row * LS + wn * (OC / WN) + b * 32 + (lane & 31)] = f32_to_bf16(silu_lp(g) * u);
+        }
+      }
+    lds_sync();
+    constexpr int CPR = OC / 8;                // 16-byte pieces per row
+    for (int i = tid; i < rows * CPR; i += NT) {
+      const int row = i / CPR, c = i - row * CPR;
+      *reinterpret_cast<uint4*>(p.out16 + int64_t(base + m0 + row) * p.N + cur_ct * OC + c * 8) =
+          *reinterpret_cast<const uint4*>(stg + row * LS + c * 8);
     }
     if (!more) break;
   }
@@ -1737,8 +1940,12 @@ int launch_gateup_mfma(const Plan& p, const void* x, const int32_t* row_token,
     a.a = (const bf16_t*)x; a.row_token = row_token; a.offsets = offsets; a.tiles = tiles;
     a.meta = meta; a.w0 = (const bf16_t*)w->w_gate; a.w1 = (const bf16_t*)w->w_up;
     a.sh0 = (const bf16_t*)w->sh_gate; a.sh1 = (const bf16_t*)w->sh_up;
-    a.out16 = (bf16_t*)h; a.K = p.H; a.N = p.I; a.E = p.E;
-    if (bf_pipelined_ok(p))
+    a.out16 = (bf16_t*)h; a.K = p.H; a.N = p.I; a.E = p.E; a.ES = p.E + p.S;
+    if (bf_pipelined_ok(p) && MOE_BF_GU_PERSIST) {
+      unsigned pg = 0;
+      MOE_TRY(persistent_grid(&pg));
+      launch_kernel(p, kTimeGateUp, k_gemm_bf16_gateup_p, dim3(pg), dim3(BfCfg::NT), 0, st, a);
+    } else if (bf_pipelined_ok(p))
       launch_kernel(p, kTimeGateUp, k_gemm_bf16_v2<true, BfCfg>,
                     dim3(xcd_grid(p.max_tiles * (p.I / (BfCfg::BN / 2)))), dim3(BfCfg::NT), 0, st, a);
     else
