@@ -1893,40 +1893,13 @@ static bool fp8_pipelined_ok(const Plan& p) {
          p.H / 128 <= Fp8Tile::SMAX && p.I / 128 <= Fp8Tile::SMAX;
 }
 
-// Block-FP8 activations: per row and 128-wide block, scale = amax / 448 (1 for an
-// all-zero block) and codes = e4m3(v / scale), rounded to nearest even and saturated.
+// Block-FP8 activations (x, or h in the register-staged path): quant_e4m3_wave per
+// wave, 16 blocks of 128 per workgroup of 256.
 template <typename TI>
 __global__ __launch_bounds__(256) void k_quant_e4m3(const TI* __restrict__ in, int64_t rows, int K,
                                                     uint8_t* __restrict__ codes,
                                                     float* __restrict__ scales) {
-  // one 128-wide block per DPP row of 16 lanes (8 consecutive values per lane, one
-  // 16-byte load of bf16), four blocks per wave; rows past the end load a clamped
-  // block and store nothing
-  const int lane = threadIdx.x & 63, r16 = lane & 15;
-  const int nkb = K / 128;
-  const int64_t nblk = rows * nkb;
-  const int64_t idx = (int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);
-  const bool live = idx < nblk;
-  const int64_t id = live ? idx : nblk - 1;
-  const int64_t row = id / nkb;
-  const int kb = int(id - row * nkb);
-  const int64_t off = row * K + kb * 128 + r16 * 8;
-  float v[8];
-  load8(in + off, v);
-  float m = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
-  m = fmaxf(m, dppf<0xB1>(m));    // quad_perm [1,0,3,2]
-  m = fmaxf(m, dppf<0x4E>(m));    // quad_perm [2,3,0,1]
-  m = fmaxf(m, dppf<0x141>(m));   // row_half_mirror
-  m = fmaxf(m, dppf<0x140>(m));   // row_mirror
-  const float scale = m > 0.f ? m / 448.0f : 1.0f;
-  const uint32_t c[2] = {e4m3x4(v[0] / scale, v[1] / scale, v[2] / scale, v[3] / scale),
-                         e4m3x4(v[4] / scale, v[5] / scale, v[6] / scale, v[7] / scale)};
-  if (live) {
-    *reinterpret_cast<uint2*>(codes + off) = make_uint2(c[0], c[1]);
-    if (r16 == 0) scales[row * nkb + kb] = scale;
-  }
+  quant_e4m3_wave(in, rows, K, codes, scales, int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6));
 }
 
 // ===========================================================================

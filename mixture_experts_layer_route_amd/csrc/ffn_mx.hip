@@ -307,32 +307,11 @@ void k_gemm_mx4(GemmMx4Args p) {
   }
 }
 
-// MXFP8 activations: per row and 32-wide block, X = floor(log2(amax)) - 8 (clamped to
-// the E8M0 range; -127 for an all-zero block), codes = e4m3(v * 2^-X), rounded to
-// nearest even and saturated.  Eight values per lane (one 16-byte load), a block per
-// four lanes; positions past the end load a clamped group and store nothing.
+// MXFP8 activations of x: quant_mx_lane per lane, 2,048 values per workgroup of 256.
 __global__ __launch_bounds__(256) void k_quant_mx(const bf16_t* __restrict__ in, int64_t rows, int K,
                                                   uint8_t* __restrict__ codes,
                                                   uint8_t* __restrict__ scales) {
-  const int64_t n8 = rows * (K / 8);
-  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  const bool live = idx < n8;
-  const int64_t off = (live ? idx : n8 - 1) * 8;
-  float v[8];
-  load8(in + off, v);
-  float m = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
-  m = fmaxf(m, dppf<0xB1>(m));    // quad_perm [1,0,3,2]
-  m = fmaxf(m, dppf<0x4E>(m));    // quad_perm [2,3,0,1]
-  const int X = mx_exponent(m);
-  const float inv = mx_inv_scale(X);
-  const uint32_t c0 = e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
-  const uint32_t c1 = e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
-  if (live) {
-    *reinterpret_cast<uint2*>(codes + off) = make_uint2(c0, c1);
-    if ((threadIdx.x & 3) == 0) scales[off / 32] = uint8_t(X + 127);
-  }
+  quant_mx_lane(in, rows, K, codes, scales, int64_t(blockIdx.x) * 256 + threadIdx.x);
 }
 
 bool mx4_ok(const Plan& p) {

@@ -381,6 +381,7 @@ static int forward_impl(const moe_config* cfg, const void* x, const moe_weights*
   float* row_w = at<float>(ws, p.o_roww);
 
   int32_t* blk = at<int32_t>(ws, p.o_blk);
+  bool x_quantised = false;   // x's FP8 / MX codes already written by the selection launch
   if (p.fused_down && decode_ffn_ok(p)) {
     // decode: the logits (with the norm in front for the decoder step), then gate/up
     // (routing in every block) and down + combine (+ residual)
@@ -403,7 +404,19 @@ static int forward_impl(const moe_config* cfg, const void* x, const moe_weights*
                                        row_w, p.bm, stream));
   } else {
     MOE_TRY(launch_logits(p, x, w->w_router, w->router_bias, logits, stream));
-    MOE_TRY(launch_select(p, logits, ids, wts, blk, stream));
+    // the matrix-core FP8 / MX expert kernels read x's codes: their quantisation rides
+    // in the selection launch where the row selection runs
+    XQuant xq;
+    if (!p.skinny && select_rows_ok(p) && (p.wt == MOE_E4M3_B128 || p.wt == MOE_MXFP4)) {
+      xq.x = static_cast<const bf16_t*>(x);
+      xq.rows = p.T;
+      xq.K = p.H;
+      xq.mx = p.wt == MOE_MXFP4;
+      xq.codes = at<uint8_t>(ws, p.o_xq);
+      xq.scales = at<void>(ws, p.o_sx);
+      x_quantised = true;
+    }
+    MOE_TRY(launch_select(p, logits, ids, wts, blk, stream, xq));
     const int32_t* blk2 = select_rows_ok(p) ? blk + size_t(p.nblk) * p.E : nullptr;
     MOE_TRY(launch_scan_scatter(p, ids, wts, blk, blk2, off, active, meta, tiles, rowtok, inv,
                                 row_w, p.bm, stream));
@@ -427,7 +440,7 @@ static int forward_impl(const moe_config* cfg, const void* x, const moe_weights*
     uint8_t* sx8 = at<uint8_t>(ws, p.o_sx);
     uint8_t* hq = at<uint8_t>(ws, p.o_hq);
     uint8_t* shq8 = at<uint8_t>(ws, p.o_shq);
-    MOE_TRY(launch_quant_mx(x, p.T, p.H, xq, sx8, stream));
+    if (!x_quantised) MOE_TRY(launch_quant_mx(x, p.T, p.H, xq, sx8, stream));
     MOE_TRY(launch_gateup_mx4(p, xq, sx8, rowtok, off, tiles, meta, w, hq, shq8, stream));
     MOE_TRY(launch_down_mx4(p, hq, shq8, off, tiles, meta, w, row_w, nullptr, ypw, stream));
   } else {
@@ -436,7 +449,7 @@ static int forward_impl(const moe_config* cfg, const void* x, const moe_weights*
     uint8_t* hq = at<uint8_t>(ws, p.o_hq);
     float* shq = at<float>(ws, p.o_shq);
     float* h = at<float>(ws, p.o_h);
-    MOE_TRY(launch_quant(p, x, true, p.T, p.H, xq, sx, stream));
+    if (!x_quantised) MOE_TRY(launch_quant(p, x, true, p.T, p.H, xq, sx, stream));
     MOE_TRY(launch_gateup_mfma(p, x, rowtok, off, tiles, meta, w, h, xq, sx, hq, shq, stream));
     MOE_TRY(launch_down_mfma(p, hq, off, tiles, meta, w, row_w, nullptr, ypw, shq, stream));
   }

@@ -230,6 +230,74 @@ __device__ __forceinline__ float wave_max(float v) {
   return fmaxf(fmaxf(lanef(v, 0), lanef(v, 16)), fmaxf(lanef(v, 32), lanef(v, 48)));
 }
 
+// ------------------------------------------------------- activation quantisation
+// Shared by the standalone quantisation kernels and the routing launch that carries the
+// quantisation of x in extra workgroups.
+//
+// Block-FP8: per row and 128-wide block, scale = amax / 448 (1 for an all-zero block)
+// and codes = e4m3(v / scale), rounded to nearest even and saturated.  One block per
+// DPP row of 16 lanes (8 consecutive values per lane, one 16-byte load), four blocks
+// per wave; `wave` numbers the waves over the launch.  Blocks past the end load a
+// clamped block and store nothing.
+template <typename TI>
+__device__ __forceinline__ void quant_e4m3_wave(const TI* __restrict__ in, int64_t rows, int K,
+                                                uint8_t* __restrict__ codes,
+                                                float* __restrict__ scales, int64_t wave) {
+  const int lane = threadIdx.x & 63, r16 = lane & 15;
+  const int nkb = K / 128;
+  const int64_t nblk = rows * nkb;
+  const int64_t idx = wave * 4 + (lane >> 4);
+  const bool live = idx < nblk;
+  const int64_t id = live ? idx : nblk - 1;
+  const int64_t row = id / nkb;
+  const int kb = int(id - row * nkb);
+  const int64_t off = row * K + kb * 128 + r16 * 8;
+  float v[8];
+  load8(in + off, v);
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+  m = fmaxf(m, dppf<0xB1>(m));    // quad_perm [1,0,3,2]
+  m = fmaxf(m, dppf<0x4E>(m));    // quad_perm [2,3,0,1]
+  m = fmaxf(m, dppf<0x141>(m));   // row_half_mirror
+  m = fmaxf(m, dppf<0x140>(m));   // row_mirror
+  const float scale = m > 0.f ? m / 448.0f : 1.0f;
+  const uint32_t c[2] = {e4m3x4(v[0] / scale, v[1] / scale, v[2] / scale, v[3] / scale),
+                         e4m3x4(v[4] / scale, v[5] / scale, v[6] / scale, v[7] / scale)};
+  if (live) {
+    *reinterpret_cast<uint2*>(codes + off) = make_uint2(c[0], c[1]);
+    if (r16 == 0) scales[row * nkb + kb] = scale;
+  }
+}
+
+// MXFP8: per row and 32-wide block, X = floor(log2(amax)) - 8 (clamped to the E8M0
+// range; -127 for an all-zero block), codes = e4m3(v * 2^-X), rounded to nearest even
+// and saturated.  Eight values per lane (one 16-byte load), a block per four lanes;
+// `idx` numbers the lanes over the launch (a multiple of 4 starts each block).
+// Positions past the end load a clamped group and store nothing.
+__device__ __forceinline__ void quant_mx_lane(const bf16_t* __restrict__ in, int64_t rows, int K,
+                                              uint8_t* __restrict__ codes,
+                                              uint8_t* __restrict__ scales, int64_t idx) {
+  const int64_t n8 = rows * (K / 8);
+  const bool live = idx < n8;
+  const int64_t off = (live ? idx : n8 - 1) * 8;
+  float v[8];
+  load8(in + off, v);
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+  m = fmaxf(m, dppf<0xB1>(m));    // quad_perm [1,0,3,2]
+  m = fmaxf(m, dppf<0x4E>(m));    // quad_perm [2,3,0,1]
+  const int X = mx_exponent(m);
+  const float inv = mx_inv_scale(X);
+  const uint32_t c0 = e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+  const uint32_t c1 = e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+  if (live) {
+    *reinterpret_cast<uint2*>(codes + off) = make_uint2(c0, c1);
+    if ((idx & 3) == 0) scales[off / 32] = uint8_t(X + 127);
+  }
+}
+
 // DPP move whose disabled-lane value is left undefined (every pattern used here reads
 // an enabled lane), so it compiles to one v_mov_b32_dpp without a copy of the source
 template <int CTRL>

@@ -65,8 +65,21 @@ int launch_rmsnorm(const Plan& p, const void* x, const void* gamma, float eps, v
                    hipStream_t st);
 int launch_logits_norm(const Plan& p, const void* x, const void* gamma, float eps, const void* wr,
                        const float* bias, float* logits, void* xn, hipStream_t st);
+// The quantisation of x that the selection launch can carry in workgroups of its own
+// (x's block-FP8 or MXFP8 codes are read only by the expert kernels that follow, so
+// it runs beside the selection instead of as a launch of its own).
+struct XQuant {
+  const bf16_t* x = nullptr;   // null: nothing to quantise
+  int64_t rows = 0;
+  int K = 0;
+  bool mx = false;             // MXFP8 (E8M0 scales per 32) instead of block-FP8 (fp32 per 128)
+  uint8_t* codes = nullptr;
+  void* scales = nullptr;
+  int nsel = 0;                // set by the launcher: workgroups of the selection itself
+};
+// whether launch_select can carry an XQuant for this plan (the row-selection kernel)
 int launch_select(const Plan& p, const float* logits, int32_t* ids, float* w, int32_t* blk,
-                  hipStream_t st);
+                  hipStream_t st, XQuant xq = XQuant());
 int launch_scan_scatter(const Plan& p, const int32_t* ids, const float* w, int32_t* blk,
                         const int32_t* blk2, int32_t* offsets, int32_t* active, int32_t* meta,
                         int2* tiles, int32_t* row_token, int32_t* inv, float* row_w, int BM,

@@ -385,6 +385,58 @@ __global__ __launch_bounds__(512) void k_logits_mfma(const bf16_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
+// Matrix-core router logits for bf16 batches too small to fill the chip with the 64 x 64
+// tiles above (a few thousand tokens): one workgroup per 32-token x 32-expert tile, its
+// eight waves splitting H into eighths.  An MFMA's sum over its 16 k positions does not
+// depend on which inputs a lane's k slots hold as long as both operands hold the same
+// ones, so lane (row, half) of wave w takes the contiguous inputs
+// [w H/8 + half H/16, + H/16) of its token row and of its expert row: every load of the
+// wave is issued before the first MFMA (one memory round trip per workgroup instead of
+// a slab ring), and the eight partial tiles are added in wave order through LDS.
+// grid = (E/32, ceil(T/32)), block = 512; S = H/128 MFMA steps per wave.
+template <int S>
+__global__ __launch_bounds__(512) void k_logits_mfma_small(const bf16_t* __restrict__ x,
+                                                           const bf16_t* __restrict__ wr,
+                                                           const float* __restrict__ bias,
+                                                           int64_t T, int H, int E,
+                                                           float* __restrict__ logits) {
+  __shared__ float red[8][16][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int r = lane & 31, half = lane >> 5;
+  const int64_t t0 = int64_t(blockIdx.y) * 32;
+  const int e0 = blockIdx.x * 32;
+  const int kb = wv * (16 * S) + half * (8 * S);
+  const bf16_t* xa = x + min<int64_t>(t0 + r, T - 1) * H + kb;
+  const bf16_t* wb = wr + int64_t(e0 + r) * H + kb;
+  bf16x8 a[S], b[S];
+#pragma unroll
+  for (int j = 0; j < S; ++j) {
+    a[j] = *reinterpret_cast<const bf16x8*>(xa + 8 * j);
+    b[j] = *reinterpret_cast<const bf16x8*>(wb + 8 * j);
+  }
+  __builtin_amdgcn_sched_barrier(0);   // keep every load ahead of the first MFMA
+  f32x16 acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+  for (int j = 0; j < S; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], b[j], acc, 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) red[wv][i][lane] = acc[i];
+  __syncthreads();
+  // thread (i, l) for i = wv and wv + 8: element i of lane l, summed over the waves in order
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int i = wv + 8 * q;
+    float v = red[0][i][lane];
+#pragma unroll
+    for (int w = 1; w < 8; ++w) v += red[w][i][lane];
+    const int64_t t = t0 + 8 * (i >> 2) + 4 * half + (i & 3);
+    const int e = e0 + r;
+    if (t < T) logits[t * E + e] = v + (bias ? bias[e] : 0.f);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Group-limited top-k from fp32 logits, one wave per token (wave-wide arg-max
 // rounds), 16 waves per 64-token block; each block writes its per-expert row
 // counts for the permutation.  grid = ceil(T/64), block = 1024.
@@ -414,13 +466,26 @@ __global__ __launch_bounds__(1024) void k_select_wave(const float* __restrict__ 
 // wave, 32 tokens per block of 8 waves, so that a batch of a few thousand tokens
 // covers every CU.  Block 2b + h handles half h of permutation block b (64 tokens)
 // and writes its per-expert row counts to blk[h][b] ([2][nblk][E]; the scan adds
-// the halves).  grid = 2 * nblk, block = 512.
+// the halves).  Workgroups from xq.nsel = 2 * nblk on quantise x instead (eight waves
+// of quant_e4m3_wave, or 512 lanes of quant_mx_lane, each).
+// grid = 2 * nblk (+ the quantisation's workgroups), block = 512.
 template <int V>
 __global__ __launch_bounds__(512) void k_select_rows(const float* __restrict__ logits, int64_t T,
                                                      int E, int G, int Gk, int k,
                                                      int32_t* __restrict__ ids,
                                                      float* __restrict__ w,
-                                                     int32_t* __restrict__ blk, int nblk) {
+                                                     int32_t* __restrict__ blk, int nblk,
+                                                     XQuant xq) {
+  if (int(blockIdx.x) >= xq.nsel) {      // uniform over the workgroup, before any barrier
+    const int64_t qb = int64_t(blockIdx.x) - xq.nsel;
+    if (xq.mx)
+      quant_mx_lane(xq.x, xq.rows, xq.K, xq.codes, static_cast<uint8_t*>(xq.scales),
+                    qb * 512 + threadIdx.x);
+    else
+      quant_e4m3_wave(xq.x, xq.rows, xq.K, xq.codes, static_cast<float*>(xq.scales),
+                      qb * 8 + (threadIdx.x >> 6));
+    return;
+  }
   __shared__ int cnt[256];
   for (int i = threadIdx.x; i < E; i += 512) cnt[i] = 0;
   __syncthreads();
@@ -472,6 +537,19 @@ bool logits_mfma_ok(const Plan& p) {
   return p.act == MOE_BF16 && p.E % 64 == 0 && p.H % 64 == 0 && p.T > 16;
 }
 
+// the 32 x 32 tiles where the 64 x 64 ones would leave CUs idle (fewer workgroups than
+// MOE_LOGITS_SMALL_BELOW, 256 by default: one per CU)
+#ifndef MOE_LOGITS_SMALL_BELOW
+#define MOE_LOGITS_SMALL_BELOW 256
+#endif
+static bool logits_small_ok(const Plan& p) {
+  const int S = p.H / 128;
+  if (p.act != MOE_BF16 || p.T <= 16 || p.T > int64_t(65535) * 32 || p.E % 32 || p.H % 128 ||
+      (S != 8 && S != 12 && S != 16))
+    return false;
+  return !logits_mfma_ok(p) || (p.T + 63) / 64 * (p.E / 64) < MOE_LOGITS_SMALL_BELOW;
+}
+
 int launch_logits(const Plan& p, const void* x, const void* wr, const float* bias, float* logits,
                   hipStream_t st) {
   if (p.T <= 16) {
@@ -489,6 +567,18 @@ int launch_logits(const Plan& p, const void* x, const void* wr, const float* bia
     else if (p.H <= 1024) MOE_LF(8, 2)
     else MOE_LF(4, 4)
 #undef MOE_LF
+    return check_launch();
+  }
+  if (logits_small_ok(p)) {
+    const dim3 grid(unsigned(p.E / 32), unsigned((p.T + 31) / 32));
+#define MOE_LS(SS)                                                                              \
+  hipLaunchKernelGGL(k_logits_mfma_small<SS>, grid, dim3(512), 0, st, (const bf16_t*)x,        \
+                     (const bf16_t*)wr, bias, p.T, p.H, p.E, logits)
+    const int S = p.H / 128;
+    if (S == 8) MOE_LS(8);
+    else if (S == 12) MOE_LS(12);
+    else MOE_LS(16);
+#undef MOE_LS
     return check_launch();
   }
   if (logits_mfma_ok(p)) {
@@ -513,14 +603,20 @@ int launch_logits(const Plan& p, const void* x, const void* wr, const float* bia
 
 
 int launch_select(const Plan& p, const float* logits, int32_t* ids, float* w, int32_t* blk,
-                  hipStream_t st) {
+                  hipStream_t st, XQuant xq) {
   const dim3 grid(unsigned((p.T + 63) / 64));
   if (select_rows_ok(p)) {
     const int V = p.E / 16;
-    const dim3 grid2(unsigned(2 * p.nblk));
+    xq.nsel = 2 * p.nblk;
+    int64_t nq = 0;                      // workgroups of the carried quantisation
+    if (xq.x && xq.rows > 0) {
+      if (xq.mx ? (xq.K % 32 != 0) : (xq.K % 128 != 0)) return MOE_ERR_UNSUPPORTED;
+      nq = xq.mx ? (xq.rows * (xq.K / 8) + 511) / 512 : (xq.rows * (xq.K / 128) + 31) / 32;
+    }
+    const dim3 grid2(unsigned(xq.nsel + nq));
 #define MOE_SR(VV)                                                                              \
   hipLaunchKernelGGL(k_select_rows<VV>, grid2, dim3(512), 0, st, logits, p.T, p.E, p.G, p.Gk, \
-                     p.k, ids, w, blk, p.nblk)
+                     p.k, ids, w, blk, p.nblk, xq)
     if (V == 1) MOE_SR(1);
     else if (V == 2) MOE_SR(2);
     else if (V == 4) MOE_SR(4);
@@ -538,6 +634,7 @@ int launch_select(const Plan& p, const float* logits, int32_t* ids, float* w, in
 #undef MOE_SR
     return check_launch();
   }
+  if (xq.x) return MOE_ERR_UNSUPPORTED;  // only the row selection carries the quantisation
   if (p.E <= 64)
     hipLaunchKernelGGL(k_select_wave<1>, grid, dim3(1024), 0, st, logits, p.T, p.E, p.G, p.Gk, p.k, ids, w, blk);
   else if (p.E <= 128)
