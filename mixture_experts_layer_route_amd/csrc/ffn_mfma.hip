@@ -1,9 +1,9 @@
 // Grouped SwiGLU expert GEMMs on CDNA4 matrix cores (bf16, block-FP8, NVFP4).
 //
-// The pages say the bf16 experts have no grouped kernel and that a port would
-// want a real one (TensorFold issue #1247 "Ling-3.0-tiny on a Qualcomm board",
-// jschmied's comment, list "What it does not cover"); block FP8 is one of the
-// expert formats that list names as read.  These kernels are that grouped
+// According to TensorFold issue #1247 "Ling-3.0-tiny on a Qualcomm board"
+// (jschmied's comment, list "What it does not cover"), the bf16 expert path there
+// lacks a grouped kernel, which a port should supply; the same list names block
+// FP8 among the expert formats it reads.  These kernels are that grouped
 // kernel: one launch covers every expert, each workgroup reads its (expert, row
 // offset) from the device tile table the permutation built, so the host never
 // learns the per-expert row counts.  Workgroups beyond the live tile count exit.
