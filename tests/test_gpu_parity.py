@@ -65,6 +65,33 @@ def test_route(moe, name, T):
     print(f"near-ties {int(near.sum())}/{shape.T}")
 
 
+# Router-logit tile choices: the 32 x 32 tiles (H/128 = 8, 12 or 16 MFMA steps per wave;
+# E a multiple of 32 but not of 64; ragged token tiles) and the 64 x 64 tiles once their
+# grid reaches one workgroup per CU.  Logits against float64, then the routing rule.
+@pytest.mark.parametrize("case", [
+    ("lt_h1024_e32", 40, 1024, 32, 4, 2, 4),
+    ("lt_h1536_e96", 300, 1536, 96, 6, 3, 8),
+    ("lt_h2048_e64", 17, 2048, 64, 1, 1, 6),
+    ("lt_h1536_t4095", 4095, 1536, 128, 8, 4, 8),
+    ("lt_h1536_e256_t4096", 4096, 1536, 256, 1, 1, 6),
+], ids=lambda c: c[0])
+def test_route_logit_tiles(moe, case):
+    name, T, H, E, G, Gk, k = case
+    _print_case("route tiles", name)
+    shape = synth.LayerShape(name, T=T, H=H, I=128, E=E, G=G, Gk=Gk, k=k, S=0, act="bf16",
+                             wt="bf16", x_dist="rms", bias_std=0.3, seed=31)
+    cpu = synth.make_layer(shape)
+    dev = to_device(cpu)
+    cfg = config_for(shape)
+    ws = moe.alloc_workspace(cfg)
+    logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    ids, w = moe.route(cfg, dev["x"], dev["w_router"], dev["router_bias"], ws, logits)
+    torch.cuda.synchronize()
+    l64 = mo.router_logits(np_exact(cpu["x"]), np_exact(cpu["w_router"]), np_exact(cpu["router_bias"]))
+    np.testing.assert_allclose(logits.cpu().numpy(), l64, rtol=0, atol=2e-5)
+    check_routing(ids.cpu().numpy(), w.cpu().numpy(), l64, shape)
+
+
 def test_route_e64_generic_path(moe):
     """E = 64 bf16 experts in 4 groups (vector-FMA logits + thread-per-token selection)."""
     _print_case("route e64")
