@@ -5,6 +5,10 @@
   "What #874's CUDA path now covers", holds its own path to concurrent == solo).
 * moe_combine called directly with shared experts and bf16 output: the fixed-order fp32
   sum of reading R7, rounded once to bf16.
+* Chunked == whole (the same list's equivalence tests): each token's output depends only
+  on that token, so a batch run in two pieces gives the same bits as the whole batch, as
+  long as both pieces take the same kernels (matrix-core experts, the same router-logit
+  tiles).
 * The largest expert count the ABI accepts, E + S = 1024: the permutation (whose total
   row count then lies past the last thread of the scan blocks) and whole layers on
   every path (decode kernels, small-batch route+permute, skinny and matrix-core
@@ -136,3 +140,25 @@ def test_forward_1024_experts(moe, case):
     shape = S_(*case)
     cpu = synth.make_layer(shape)
     _forward_check(moe, shape, cpu, to_device(cpu))
+
+
+# splits whose pieces stay on the whole batch's kernels: matrix-core experts (more than 8
+# rows per expert on average) and the 32 x 32 router-logit tiles
+@pytest.mark.parametrize("name,T,split", [("prefill", 3000, 1500), ("prefill", 3000, 1100),
+                                          ("fp8", 2048, 1024), ("inkling", 1200, 600)])
+def test_chunked_equals_whole(moe, name, T, split):
+    print("case: chunked == whole", name, T, split, flush=True)
+    shape = synth.WORKLOADS[name].with_tokens(T)
+    cpu = synth.make_layer(shape)
+    dev = to_device(cpu)
+    cfg = config_for(shape)
+    whole = moe.forward(cfg, dev["x"], dev, moe.alloc_workspace(cfg))
+    parts = []
+    for a, b in ((0, split), (split, T)):
+        pc = config_for(shape.with_tokens(b - a))
+        parts.append(moe.forward(pc, dev["x"][a:b].contiguous(), dev, moe.alloc_workspace(pc)))
+    torch.cuda.synchronize()
+    got = torch.cat(parts)
+    diff = int((got.view(torch.int16) != whole.view(torch.int16)).sum())
+    print(f"{name} T={T} split {split}: {diff} elements differ")
+    assert diff == 0
