@@ -145,7 +145,9 @@ def test_forward_1024_experts(moe, case):
 # splits whose pieces stay on the whole batch's kernels: matrix-core experts (more than 8
 # rows per expert on average) and the 32 x 32 router-logit tiles
 @pytest.mark.parametrize("name,T,split", [("prefill", 3000, 1500), ("prefill", 3000, 1100),
-                                          ("fp8", 2048, 1024), ("inkling", 1200, 600)])
+                                          ("fp8", 2048, 1024), ("inkling", 1200, 600),
+                                          ("prefill_nvfp4", 3000, 1300),
+                                          ("prefill_mxfp4", 3000, 1700)])
 def test_chunked_equals_whole(moe, name, T, split):
     print("case: chunked == whole", name, T, split, flush=True)
     shape = synth.WORKLOADS[name].with_tokens(T)
