@@ -136,6 +136,23 @@ E2M1_MAG = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float32)
 E2M1_MID = (E2M1_MAG[:-1] + E2M1_MAG[1:]) / 2          # rounding thresholds
 
 
+def _e2m1_pack(q: np.ndarray) -> np.ndarray:
+    """Nearest E2M1 code of each float32 value (ties to the even code, saturating at 6;
+    sign in bit 3), packed two per byte with element 2i in the low nibble.  A value on the
+    midpoint between codes i and i + 1 sits above exactly i thresholds and takes i + 1
+    when i is odd."""
+    a = np.minimum(np.abs(q), np.float32(6.0))
+    idx = np.zeros(a.shape, dtype=np.uint8)
+    tie = np.zeros(a.shape, dtype=bool)
+    for i, m in enumerate(E2M1_MID):                  # number of thresholds strictly below a
+        idx += a > m
+        if i % 2 == 1:
+            tie |= a == m
+    idx += tie
+    codes = idx | (np.signbit(q).astype(np.uint8) << 3)
+    return codes[..., 0::2] | (codes[..., 1::2] << 4)
+
+
 def _encode_nvfp4(w: np.ndarray):
     """Store expert matrices [n, rows, K] as NVFP4: packed E2M1 codes [n, rows, K/2]
     (element 2i in the low nibble), E4M3 block scales [n, rows, K/16] and one fp32 scale
@@ -157,15 +174,7 @@ def _encode_nvfp4(w: np.ndarray):
     safe = np.where(den > 0, den, np.float32(1.0))
     q = (blocks / safe[..., None]).astype(np.float32)
     q[np.broadcast_to((den <= 0)[..., None], q.shape)] = 0.0
-    q = q.reshape(n, rows, K)
-    a = np.minimum(np.abs(q), np.float32(6.0))
-    idx = np.zeros(a.shape, dtype=np.uint8)
-    for m in E2M1_MID:                                # number of thresholds strictly below a
-        idx += a > m
-    last = E2M1_MID.size - 1
-    idx += (idx <= last) & (a == E2M1_MID[np.minimum(idx, last)]) & (idx % 2 == 1)   # ties: even code
-    codes = (idx | np.where(np.signbit(q), 8, 0)).astype(np.uint8)
-    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    packed = _e2m1_pack(q.reshape(n, rows, K))
     return torch.from_numpy(packed), bcode.view(torch.uint8), torch.from_numpy(g)
 
 
@@ -182,20 +191,12 @@ def _encode_mxfp4(w: np.ndarray):
     all-zero block gets X = -127.  The stored pair is the weight for every consumer.
     """
     n, rows, K = w.shape
-    blocks = w.reshape(n, rows, K // MX_BLOCK, MX_BLOCK).astype(np.float64)
-    amax = np.abs(blocks).max(axis=3)
+    blocks = w.reshape(n, rows, K // MX_BLOCK, MX_BLOCK)
+    amax = np.abs(blocks).max(axis=3).astype(np.float64)     # exact in float32
     _, ex = np.frexp(np.where(amax > 0, amax, 1.0))
     X = np.clip(np.where(amax > 0, ex - 1 - 2, -127), -127, 127)
-    q = (blocks / np.ldexp(1.0, X)[..., None]).reshape(n, rows, K).astype(np.float32)
-    a = np.minimum(np.abs(q), np.float32(6.0))
-    idx = np.zeros(a.shape, dtype=np.uint8)
-    for m in E2M1_MID:
-        idx += a > m
-    last = E2M1_MID.size - 1
-    idx += (idx <= last) & (a == E2M1_MID[np.minimum(idx, last)]) & (idx % 2 == 1)   # ties: even code
-    codes = (idx | np.where(np.signbit(q), 8, 0)).astype(np.uint8)
-    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
-    return torch.from_numpy(packed), torch.from_numpy((X + 127).astype(np.uint8))
+    q = (blocks.astype(np.float64) / np.ldexp(1.0, X)[..., None]).reshape(n, rows, K).astype(np.float32)
+    return torch.from_numpy(_e2m1_pack(q)), torch.from_numpy((X + 127).astype(np.uint8))
 
 
 def make_norm_weight(H: int, act: str, seed: int) -> torch.Tensor:
